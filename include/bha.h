@@ -1,0 +1,163 @@
+/*
+ * bha.h -- C ABI of the block-hybrid attention library (libbha.so, gfx950).
+ *
+ * Block-hybrid attention, as described for "Retrofitting Linear Attention into
+ * Diffusion Language Models" (Kim, Roh, Kim): inside the active denoising
+ * block of B tokens every query attends to every key of the block with exact,
+ * unmasked softmax; all previously committed blocks are folded into a fixed
+ * size recurrent state that the query reads through the Hedgehog feature map
+ *     phi(x) = [ softmax(x W), softmax(-x W) ]        (dimension F = 2 FW)
+ * with  S = sum_t phi(k_t) v_t^T  (F x d)  and  Z = sum_t phi(k_t)  (F).
+ * The two branches share one normaliser and a per-head gate g >= 0:
+ *     y_i = ( sum_j e^{s_ij - m_i} v_j + g e^{-m_i} phi(q_i)^T S )
+ *         / ( sum_j e^{s_ij - m_i}     + g e^{-m_i} phi(q_i)^T Z ),
+ *     s_ij = scale * q_i . k_j,  m_i = max_j s_ij.
+ * Where the pages define each piece:
+ *   - gist.science explainer, "Technical Summary", "Methodology: Block-Hybrid
+ *     Attention", list "Architecture Design": within-block softmax, the
+ *     cross-block Hedgehog map, the S_n / Z_n states updated only at a commit,
+ *     and the merge under a shared normaliser with a learned scalar gate.
+ *   - pith.science review, "The reading", "What carries the argument": the
+ *     formulas of phi, S_n and Z_n, one map per head, O(F d) read per query.
+ *   - pith.science review, "Circularity Check": the state sizes do not grow
+ *     with the number of committed tokens.
+ * The pages do not print where the gate and m sit; the form above is this
+ * library's definition.
+ *
+ * Conventions common to every entry point
+ *   - All tensor pointers are DEVICE pointers; descriptor structs (bha_dims,
+ *     bha_strides) are HOST pointers read during the call only.
+ *   - Ownership: the caller allocates and frees every buffer. The library never
+ *     allocates, frees or synchronises; it keeps no state between calls and is
+ *     reentrant.
+ *   - Asynchrony: work is enqueued on `stream` (0 = the null stream) and the
+ *     call returns without waiting. Calls on one stream run in order; a commit
+ *     must be enqueued after the last forward that should not see its block.
+ *   - Errors: arguments are checked on the host before anything is enqueued. A
+ *     bad argument returns a negative bha_status and enqueues nothing. A
+ *     failed launch returns BHA_ERR_HIP. num_requests == 0 returns BHA_OK
+ *     without reading any pointer.
+ *   - Device-side preconditions (not checkable on the host): slot ids in
+ *     [0, num_slots) -- a request with an out-of-range slot gets NaN outputs
+ *     from the forward and is skipped by the commit; slot ids of one commit
+ *     call are distinct (duplicates race); gamma >= 0; outputs do not alias
+ *     inputs.
+ *
+ * Layouts (elements, not bytes, in every stride)
+ *   Tokens  q, k, v, out : element (r, t, h, c) at  r*req + t*tok + h*head + c
+ *                          (r < R requests, t < B tokens, h < H heads, c < d);
+ *                          the last dimension is contiguous.
+ *   Map     w            : element (h, j, c) at  h*w_head_stride + j*d + c
+ *                          holds W_h[c][j], i.e. row j is column j of the
+ *                          d x FW matrix (the usual [out][in] weight layout);
+ *                          w_head_stride == 0 shares one W across heads.
+ *   Gate    gamma        : float32 [H].
+ *   State   state        : float32, one record of (d+1)*F floats per
+ *                          (slot, head), record (s, h) at (s*H + h)*(d+1)*F.
+ *                          Inside a record, S[f][c] (f < F, c < d) is stored in
+ *                          32 x 4 tiles so that 128-bit loads are contiguous:
+ *                            offset((c/32)*(F/4) + f/4)*128 + (c%32)*4 + f%4,
+ *                          and Z[f] sits at offset d*F + f. A zero record is
+ *                          the state of a request with nothing committed.
+ *   Dtypes: tokens, w and out use dims->io_dtype (float32 or bfloat16);
+ *           state, gamma and phi are always float32.
+ *   Alignment: every token / w / out pointer, every stride times the element
+ *           size, and state must be multiples of 16 bytes; gamma, slot_ids
+ *           and phi multiples of 4 bytes.
+ *   Supported sizes: d in {64, 128}; FW in {32, 64, 128}; 1 <= B <= 64;
+ *           1 <= H; 0 <= R. scale == 0 selects 1/sqrt(d).
+ */
+#ifndef BHA_H
+#define BHA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BHA_OK = 0,
+    BHA_ERR_NULL = -1,        /* a required pointer is NULL */
+    BHA_ERR_DIMS = -2,        /* negative / zero count, bad scale, size overflow */
+    BHA_ERR_UNSUPPORTED = -3, /* d, FW or B outside the supported set */
+    BHA_ERR_ALIGN = -4,       /* pointer not aligned as stated above */
+    BHA_ERR_STRIDE = -5,      /* negative or misaligned stride, rows overlapping */
+    BHA_ERR_DTYPE = -6,       /* io_dtype not a bha_dtype value */
+    BHA_ERR_HIP = -7          /* the HIP runtime reported an error at launch */
+} bha_status;
+
+typedef enum { BHA_F32 = 0, BHA_BF16 = 1 } bha_dtype;
+
+typedef struct {
+    int32_t num_requests; /* R: requests in this call (0 => no-op)            */
+    int32_t num_heads;    /* H                                                 */
+    int32_t head_dim;     /* d  in {64, 128}                                   */
+    int32_t feat_half;    /* FW in {32, 64, 128}: columns of W; F = 2 * FW     */
+    int32_t block_size;   /* B  in [1, 64]: tokens of the active block         */
+    int32_t io_dtype;     /* bha_dtype of q, k, v, w, out and x                */
+    float scale;          /* softmax scale of the block logits; 0 => 1/sqrt(d) */
+} bha_dims;
+
+typedef struct {
+    int64_t req;  /* between requests */
+    int64_t tok;  /* between tokens of a block */
+    int64_t head; /* between heads */
+} bha_strides;
+
+/*
+ * bha_feature_map -- phi(x) = [softmax(x W_h), softmax(-x W_h)] for every
+ * token of a [R][B][H][d] batch (gist.science "Architecture Design",
+ * cross-block bullet; pith.science "What carries the argument").
+ *   x   : tokens, strides xs.
+ *   phi : float32 output, contiguous [R][B][H][F].
+ */
+int bha_feature_map(const bha_dims* dims, const void* x, const bha_strides* xs,
+                    const void* w, int64_t w_head_stride, float* phi, hipStream_t stream);
+
+/*
+ * bha_block_forward -- one denoising step of block-hybrid attention for every
+ * (request, head): the within-block softmax over q, k, v, the linear read
+ * phi(q)^T S, phi(q)^T Z of the request's state record, and the gated merge
+ * written at the top of this file (gist.science "Architecture Design", all
+ * four bullets; pith.science "What carries the argument").
+ *   q, k, v      : active block tokens, strides qkv.
+ *   gamma        : per-head gate.
+ *   state        : num_slots * H records (read only).
+ *   slot_ids     : int32 [R], the state slot of each request.
+ *   out          : tokens in io_dtype, strides outs.
+ */
+int bha_block_forward(const bha_dims* dims, const void* q, const void* k, const void* v,
+                      const bha_strides* qkv, const void* w, int64_t w_head_stride,
+                      const float* gamma, const float* state, int32_t num_slots,
+                      const int32_t* slot_ids, void* out, const bha_strides* outs,
+                      hipStream_t stream);
+
+/*
+ * bha_state_commit -- fold a finished block into the state of every
+ * (request, head): S += sum_t phi(k_t) v_t^T and Z += sum_t phi(k_t) over the
+ * B tokens (gist.science "Architecture Design", state-compression bullet: the
+ * states change only when a block is committed; pith.science "What carries
+ * the argument"). A read-modify-write of each touched record; slot ids must
+ * be distinct within one call.
+ */
+int bha_state_commit(const bha_dims* dims, const void* k, const void* v, const bha_strides* kv,
+                     const void* w, int64_t w_head_stride, float* state, int32_t num_slots,
+                     const int32_t* slot_ids, hipStream_t stream);
+
+/* Floats in one (slot, head) state record: (d + 1) * 2 * FW. Returns -1 for
+ * unsupported sizes. Host only; touches no device. */
+int64_t bha_state_record_floats(int32_t head_dim, int32_t feat_half);
+
+/* Static description of a status code; never NULL. */
+const char* bha_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int bha_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BHA_H */

@@ -1,0 +1,250 @@
+"""Block-hybrid attention on MI355X (gfx950): Python binding of libbha.so.
+
+This module only marshals arguments: it takes PyTorch tensors that live on a
+ROCm device, passes their device pointers, element strides and the current
+HIP stream to the C ABI declared in ``include/bha.h``, and turns a non-zero
+status into an exception. Every step of the computation runs in the library's
+HIP kernels; there is no other implementation behind these functions, and they
+raise if ``libbha.so`` has not been built.
+
+Tensor conventions (element strides are taken from the tensors themselves):
+
+* tokens ``q, k, v, out, x``: [R][B][H][d], last dimension contiguous,
+  bfloat16 or float32 (all of one call share the dtype).
+* ``w``: [H][FW][d] (row j of head h is column j of that head's d x FW map)
+  or [FW][d] to share one map across heads; same dtype as the tokens.
+* ``gamma``: float32 [H].
+* ``state``: float32, ``num_slots * H * (d + 1) * 2FW`` elements, any shape
+  (``new_state`` makes a zeroed [num_slots][H][record] tensor).
+* ``slot_ids``: int32 [R].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BhaError", "library_path", "load_library", "version", "status_string",
+    "state_record_floats", "new_state", "feature_map", "block_forward", "state_commit",
+    "BHA_F32", "BHA_BF16",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libbha.so")
+_lib = None
+
+BHA_F32 = 0
+BHA_BF16 = 1
+
+# Every symbol include/bha.h declares.
+EXPORTED_SYMBOLS = (
+    "bha_feature_map", "bha_block_forward", "bha_state_commit",
+    "bha_state_record_floats", "bha_status_string", "bha_version",
+)
+
+
+class BhaError(RuntimeError):
+    """A bha_* entry point returned a non-zero bha_status."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status}: {status_string(status)}")
+
+
+class bha_dims(ctypes.Structure):
+    _fields_ = [
+        ("num_requests", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("feat_half", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class bha_strides(ctypes.Structure):
+    _fields_ = [("req", ctypes.c_int64), ("tok", ctypes.c_int64), ("head", ctypes.c_int64)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libbha.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m linear_attention_block_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    PD, PS = ctypes.POINTER(bha_dims), ctypes.POINTER(bha_strides)
+    lib.bha_feature_map.argtypes = [PD, P, PS, P, I64, P, P]
+    lib.bha_block_forward.argtypes = [PD, P, P, P, PS, P, I64, P, P, I32, P, P, PS, P]
+    lib.bha_state_commit.argtypes = [PD, P, P, PS, P, I64, P, I32, P, P]
+    lib.bha_state_record_floats.argtypes = [I32, I32]
+    lib.bha_state_record_floats.restype = I64
+    lib.bha_status_string.argtypes = [ctypes.c_int]
+    lib.bha_status_string.restype = ctypes.c_char_p
+    lib.bha_version.argtypes = []
+    for f in (lib.bha_feature_map, lib.bha_block_forward, lib.bha_state_commit, lib.bha_version):
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def version() -> int:
+    return int(load_library().bha_version())
+
+
+def status_string(status: int) -> str:
+    return load_library().bha_status_string(int(status)).decode()
+
+
+def state_record_floats(head_dim: int, feat_half: int) -> int:
+    return int(load_library().bha_state_record_floats(int(head_dim), int(feat_half)))
+
+
+def new_state(num_slots: int, num_heads: int, head_dim: int, feat_half: int, device) -> torch.Tensor:
+    """A zeroed state pool: [num_slots][H][(d + 1) * 2FW] float32 (nothing committed)."""
+    rec = (head_dim + 1) * 2 * feat_half
+    return torch.zeros((num_slots, num_heads, rec), dtype=torch.float32, device=device)
+
+
+# ------------------------------------------------------------------ marshalling
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BHA_BF16
+    if t.dtype == torch.float32:
+        return BHA_F32
+    raise TypeError(f"token tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _tok_strides(t: torch.Tensor, name: str) -> bha_strides:
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [R][B][H][d], got shape {tuple(t.shape)}")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    return bha_strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _w_stride(w: torch.Tensor, H: int, d: int):
+    if w.dim() == 2:
+        fw, dd = w.shape
+        if not w.is_contiguous() or dd != d:
+            raise ValueError("w [FW][d] must be contiguous with d columns")
+        return fw, 0
+    if w.dim() == 3:
+        hh, fw, dd = w.shape
+        if hh != H or dd != d or w.stride(2) != 1 or w.stride(1) != d:
+            raise ValueError("w must be [H][FW][d] with contiguous [FW][d] rows per head")
+        return fw, w.stride(0)
+    raise ValueError("w must be [H][FW][d] or [FW][d]")
+
+
+def _stream(dev: torch.device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check_device(dev, *ts):
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a ROCm device")
+    for t in ts:
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+
+
+def feature_map(x: torch.Tensor, w: torch.Tensor, *, stream=None) -> torch.Tensor:
+    """phi(x) = [softmax(x W), softmax(-x W)] -> float32 [R][B][H][2FW]."""
+    lib = load_library()
+    xs = _tok_strides(x, "x")
+    R, B, H, d = x.shape
+    fw, wh = _w_stride(w, H, d)
+    if w.dtype != x.dtype:
+        raise TypeError("w must have the dtype of x")
+    _check_device(x.device, w)
+    phi = torch.empty((R, B, H, 2 * fw), dtype=torch.float32, device=x.device)
+    dims = bha_dims(R, H, d, fw, B, _io_dtype(x), 0.0)
+    st = lib.bha_feature_map(ctypes.byref(dims), _ptr(x), ctypes.byref(xs), _ptr(w), wh,
+                             _ptr(phi), _stream(x.device, stream))
+    if st != 0:
+        raise BhaError("bha_feature_map", st)
+    return phi
+
+
+def block_forward(q, k, v, w, gamma, state, slot_ids, *, out=None, scale: float = 0.0,
+                  stream=None) -> torch.Tensor:
+    """One block-hybrid attention step for every (request, head); returns ``out``."""
+    lib = load_library()
+    qs = _tok_strides(q, "q")
+    R, B, H, d = q.shape
+    for t, n in ((k, "k"), (v, "v")):
+        if t.shape != q.shape:
+            raise ValueError(f"{n} must match q in shape")
+        if (t.stride(0), t.stride(1), t.stride(2)) != (qs.req, qs.tok, qs.head):
+            raise ValueError(f"{n} must have the strides of q")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{n} must have the dtype of q")
+    fw, wh = _w_stride(w, H, d)
+    if w.dtype != q.dtype:
+        raise TypeError("w must have the dtype of q")
+    if gamma.dtype != torch.float32 or gamma.numel() != H or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous float32 [H] tensor")
+    if state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError("state must be a contiguous float32 tensor")
+    rec = (d + 1) * 2 * fw
+    if state.numel() % (H * rec) != 0:
+        raise ValueError("state size is not a whole number of [H][record] slots")
+    num_slots = state.numel() // (H * rec)
+    if slot_ids.dtype != torch.int32 or slot_ids.numel() != R or not slot_ids.is_contiguous():
+        raise ValueError("slot_ids must be a contiguous int32 [R] tensor")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    os_ = _tok_strides(out, "out")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    _check_device(q.device, k, v, w, gamma, state, slot_ids, out)
+    dims = bha_dims(R, H, d, fw, B, _io_dtype(q), float(scale))
+    st = lib.bha_block_forward(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(qs),
+                               _ptr(w), wh, _ptr(gamma), _ptr(state), num_slots, _ptr(slot_ids),
+                               _ptr(out), ctypes.byref(os_), _stream(q.device, stream))
+    if st != 0:
+        raise BhaError("bha_block_forward", st)
+    return out
+
+
+def state_commit(k, v, w, state, slot_ids, *, stream=None) -> None:
+    """Fold the block (k, v) into the state records of ``slot_ids`` (in place)."""
+    lib = load_library()
+    ks = _tok_strides(k, "k")
+    R, B, H, d = k.shape
+    if v.shape != k.shape or (v.stride(0), v.stride(1), v.stride(2)) != (ks.req, ks.tok, ks.head):
+        raise ValueError("v must match k in shape and strides")
+    if v.dtype != k.dtype or w.dtype != k.dtype:
+        raise TypeError("k, v and w must share one dtype")
+    fw, wh = _w_stride(w, H, d)
+    if state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError("state must be a contiguous float32 tensor")
+    rec = (d + 1) * 2 * fw
+    if state.numel() % (H * rec) != 0:
+        raise ValueError("state size is not a whole number of [H][record] slots")
+    num_slots = state.numel() // (H * rec)
+    if slot_ids.dtype != torch.int32 or slot_ids.numel() != R or not slot_ids.is_contiguous():
+        raise ValueError("slot_ids must be a contiguous int32 [R] tensor")
+    _check_device(k.device, v, w, state, slot_ids)
+    dims = bha_dims(R, H, d, fw, B, _io_dtype(k), 0.0)
+    st = lib.bha_state_commit(ctypes.byref(dims), _ptr(k), _ptr(v), ctypes.byref(ks), _ptr(w), wh,
+                              _ptr(state), num_slots, _ptr(slot_ids), _stream(k.device, stream))
+    if st != 0:
+        raise BhaError("bha_state_commit", st)

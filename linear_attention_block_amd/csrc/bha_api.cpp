@@ -1,0 +1,107 @@
+// C-ABI entry points of libbha.so: validate on the host, then enqueue the
+// kernels on the caller's stream. The interface contract is in include/bha.h.
+#include <math.h>
+
+#include "bha_internal.hpp"
+
+#define BHA_VERSION_NUMBER 10000 /* 1.0.0 */
+
+using namespace bha;
+
+static int launch_status(hipError_t e)
+{
+    if (e != hipSuccess) return BHA_ERR_HIP;
+    return (hipGetLastError() == hipSuccess) ? BHA_OK : BHA_ERR_HIP;
+}
+
+extern "C" int bha_feature_map(const bha_dims* dims, const void* x, const bha_strides* xs,
+                               const void* w, int64_t w_head_stride, float* phi,
+                               hipStream_t stream)
+{
+    int st = validate_dims(dims);
+    if (st != BHA_OK) return st;
+    if (dims->num_requests == 0) return BHA_OK;
+    if ((st = validate_tokens(x, xs, dims, false)) != BHA_OK) return st;
+    if ((st = validate_w(w, w_head_stride, dims)) != BHA_OK) return st;
+    if (!phi) return BHA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(phi) % 4 != 0) return BHA_ERR_ALIGN;
+    PhiArgs a;
+    a.R = dims->num_requests; a.H = dims->num_heads; a.d = dims->head_dim;
+    a.FW = dims->feat_half; a.B = dims->block_size; a.io = dims->io_dtype;
+    a.x = x; a.xs = *xs; a.w = w; a.wh = w_head_stride; a.phi = phi;
+    return launch_status(launch_feature_map_generic(a, stream));
+}
+
+extern "C" int bha_block_forward(const bha_dims* dims, const void* q, const void* k, const void* v,
+                                 const bha_strides* qkv, const void* w, int64_t w_head_stride,
+                                 const float* gamma, const float* state, int32_t num_slots,
+                                 const int32_t* slot_ids, void* out, const bha_strides* outs,
+                                 hipStream_t stream)
+{
+    int st = validate_dims(dims);
+    if (st != BHA_OK) return st;
+    if (dims->num_requests == 0) return BHA_OK;
+    if ((st = validate_tokens(q, qkv, dims, false)) != BHA_OK) return st;
+    if ((st = validate_tokens(k, qkv, dims, false)) != BHA_OK) return st;
+    if ((st = validate_tokens(v, qkv, dims, false)) != BHA_OK) return st;
+    if ((st = validate_w(w, w_head_stride, dims)) != BHA_OK) return st;
+    if (!gamma) return BHA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(gamma) % 4 != 0) return BHA_ERR_ALIGN;
+    if ((st = validate_state(state, num_slots, slot_ids, dims)) != BHA_OK) return st;
+    if ((st = validate_tokens(out, outs, dims, true)) != BHA_OK) return st;
+    ForwardArgs a;
+    a.R = dims->num_requests; a.H = dims->num_heads; a.d = dims->head_dim;
+    a.FW = dims->feat_half; a.B = dims->block_size; a.io = dims->io_dtype;
+    a.scale = dims->scale > 0.0f ? dims->scale : 1.0f / sqrtf((float)dims->head_dim);
+    a.q = q; a.k = k; a.v = v; a.qs = *qkv; a.w = w; a.wh = w_head_stride; a.gamma = gamma;
+    a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids; a.out = out; a.os = *outs;
+    hipError_t e = launch_forward_mfma(a, stream);
+    if (e == hipErrorNotSupported) e = launch_forward_generic(a, stream);
+    return launch_status(e);
+}
+
+extern "C" int bha_state_commit(const bha_dims* dims, const void* k, const void* v,
+                                const bha_strides* kv, const void* w, int64_t w_head_stride,
+                                float* state, int32_t num_slots, const int32_t* slot_ids,
+                                hipStream_t stream)
+{
+    int st = validate_dims(dims);
+    if (st != BHA_OK) return st;
+    if (dims->num_requests == 0) return BHA_OK;
+    if ((st = validate_tokens(k, kv, dims, false)) != BHA_OK) return st;
+    if ((st = validate_tokens(v, kv, dims, false)) != BHA_OK) return st;
+    if ((st = validate_w(w, w_head_stride, dims)) != BHA_OK) return st;
+    if ((st = validate_state(state, num_slots, slot_ids, dims)) != BHA_OK) return st;
+    CommitArgs a;
+    a.R = dims->num_requests; a.H = dims->num_heads; a.d = dims->head_dim;
+    a.FW = dims->feat_half; a.B = dims->block_size; a.io = dims->io_dtype;
+    a.k = k; a.v = v; a.ks = *kv; a.w = w; a.wh = w_head_stride;
+    a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids;
+    hipError_t e = launch_commit_mfma(a, stream);
+    if (e == hipErrorNotSupported) e = launch_commit_generic(a, stream);
+    return launch_status(e);
+}
+
+extern "C" int64_t bha_state_record_floats(int32_t head_dim, int32_t feat_half)
+{
+    if (head_dim != 64 && head_dim != 128) return -1;
+    if (feat_half != 32 && feat_half != 64 && feat_half != 128) return -1;
+    return (int64_t)(head_dim + 1) * 2 * feat_half;
+}
+
+extern "C" const char* bha_status_string(int status)
+{
+    switch (status) {
+        case BHA_OK: return "BHA_OK: success";
+        case BHA_ERR_NULL: return "BHA_ERR_NULL: a required pointer is NULL";
+        case BHA_ERR_DIMS: return "BHA_ERR_DIMS: bad count, scale or size overflow";
+        case BHA_ERR_UNSUPPORTED: return "BHA_ERR_UNSUPPORTED: head_dim, feat_half or block_size not supported";
+        case BHA_ERR_ALIGN: return "BHA_ERR_ALIGN: pointer not aligned";
+        case BHA_ERR_STRIDE: return "BHA_ERR_STRIDE: negative, misaligned or overlapping stride";
+        case BHA_ERR_DTYPE: return "BHA_ERR_DTYPE: io_dtype is not a bha_dtype value";
+        case BHA_ERR_HIP: return "BHA_ERR_HIP: the HIP runtime reported an error";
+        default: return "unknown bha_status";
+    }
+}
+
+extern "C" int bha_version(void) { return BHA_VERSION_NUMBER; }

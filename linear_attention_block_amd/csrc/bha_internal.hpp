@@ -1,0 +1,65 @@
+// Internal declarations shared by the C-ABI layer and the HIP kernels of
+// libbha.so. Not part of the public interface (include/bha.h is).
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#include "../../include/bha.h"
+
+namespace bha {
+
+// Everything a launch needs, already validated on the host.
+struct ForwardArgs {
+    int R, H, d, FW, B, io;
+    float scale;  // resolved: never 0
+    const void *q, *k, *v;
+    bha_strides qs;
+    const void* w;
+    int64_t wh;
+    const float* gamma;
+    const float* state;
+    int num_slots;
+    const int32_t* slot_ids;
+    void* out;
+    bha_strides os;
+};
+
+struct CommitArgs {
+    int R, H, d, FW, B, io;
+    const void *k, *v;
+    bha_strides ks;
+    const void* w;
+    int64_t wh;
+    float* state;
+    int num_slots;
+    const int32_t* slot_ids;
+};
+
+struct PhiArgs {
+    int R, H, d, FW, B, io;
+    const void* x;
+    bha_strides xs;
+    const void* w;
+    int64_t wh;
+    float* phi;
+};
+
+// Plain fp32-arithmetic kernels: every supported size and both I/O dtypes.
+hipError_t launch_forward_generic(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_commit_generic(const CommitArgs& a, hipStream_t s);
+hipError_t launch_feature_map_generic(const PhiArgs& a, hipStream_t s);
+
+// bf16 MFMA kernels for bf16 I/O and B <= 32. Return hipErrorNotSupported
+// (without launching) for sizes they do not cover.
+hipError_t launch_forward_mfma(const ForwardArgs& a, hipStream_t s);
+hipError_t launch_commit_mfma(const CommitArgs& a, hipStream_t s);
+
+// Host-side argument checks (no HIP calls); see bha_validate.cpp.
+int validate_dims(const bha_dims* d);
+int validate_tokens(const void* p, const bha_strides* st, const bha_dims* d, bool is_output);
+int validate_w(const void* w, int64_t w_head_stride, const bha_dims* d);
+int validate_state(const void* state, int32_t num_slots, const int32_t* slot_ids,
+                   const bha_dims* d);
+
+}  // namespace bha

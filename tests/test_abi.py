@@ -1,0 +1,193 @@
+"""C-ABI tests that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host (before any HIP call)
+with the documented status codes. Only calls that are rejected, or that are
+no-ops (zero requests), are made here: nothing is launched.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import linear_attention_block_amd as bha
+from linear_attention_block_amd import bha_dims, bha_strides
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bha.h")
+
+OK, NULL, DIMS, UNSUP, ALIGN, STRIDE, DTYPE, HIP = 0, -1, -2, -3, -4, -5, -6, -7
+FAKE = 0x10000000  # 16-byte aligned, never dereferenced: every call below is rejected first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bha.library_path()):
+        pytest.skip("libbha.so not built")
+    return bha.load_library()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(bha_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_three_path_calls():
+    fns = header_functions()
+    for name in ("bha_feature_map", "bha_block_forward", "bha_state_commit"):
+        assert name in fns
+
+
+def test_library_exports_every_header_symbol(lib):
+    fns = header_functions()
+    assert set(fns) == set(bha.EXPORTED_SYMBOLS)
+    for name in fns:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert bha.version() == 10000
+    for st in (OK, NULL, DIMS, UNSUP, ALIGN, STRIDE, DTYPE, HIP):
+        assert bha.status_string(st).startswith(("BHA_OK", "BHA_ERR"))
+    assert bha.status_string(12345) == "unknown bha_status"
+
+
+def test_state_record_floats(lib):
+    assert bha.state_record_floats(128, 64) == 129 * 128
+    assert bha.state_record_floats(64, 32) == 65 * 64
+    assert bha.state_record_floats(128, 128) == 129 * 256
+    assert bha.state_record_floats(96, 64) == -1
+    assert bha.state_record_floats(128, 48) == -1
+
+
+def _dims(**kw):
+    base = dict(num_requests=4, num_heads=2, head_dim=128, feat_half=64, block_size=32,
+                io_dtype=1, scale=0.0)
+    base.update(kw)
+    return bha_dims(**base)
+
+
+def _st(req=32 * 2 * 128, tok=2 * 128, head=128):
+    return bha_strides(req, tok, head)
+
+
+def fwd(lib, dims, q=FAKE, k=FAKE, v=FAKE, qs=None, w=FAKE, wh=64 * 128, gamma=FAKE,
+        state=FAKE, num_slots=8, slots=FAKE, out=FAKE + (1 << 24), outs=None):
+    qs = qs or _st()
+    outs = outs or _st()
+    P = ctypes.c_void_p
+    return lib.bha_block_forward(ctypes.byref(dims) if dims is not None else None, P(q), P(k), P(v),
+                                 ctypes.byref(qs), P(w), wh, P(gamma), P(state), num_slots, P(slots),
+                                 P(out), ctypes.byref(outs), P(0))
+
+
+def commit(lib, dims, k=FAKE, v=FAKE, ks=None, w=FAKE, wh=64 * 128, state=FAKE, num_slots=8,
+           slots=FAKE):
+    ks = ks or _st()
+    P = ctypes.c_void_p
+    return lib.bha_state_commit(ctypes.byref(dims) if dims is not None else None, P(k), P(v),
+                                ctypes.byref(ks), P(w), wh, P(state), num_slots, P(slots), P(0))
+
+
+def fmap(lib, dims, x=FAKE, xs=None, w=FAKE, wh=64 * 128, phi=FAKE):
+    xs = xs or _st()
+    P = ctypes.c_void_p
+    return lib.bha_feature_map(ctypes.byref(dims) if dims is not None else None, P(x),
+                               ctypes.byref(xs), P(w), wh, P(phi), P(0))
+
+
+@pytest.mark.parametrize("call", [fwd, commit, fmap])
+def test_zero_requests_is_a_noop(lib, call):
+    # nothing is read, not even the (null) pointers
+    if call is fwd:
+        assert fwd(lib, _dims(num_requests=0), q=0, k=0, v=0, w=0, gamma=0, state=0, slots=0, out=0) == OK
+    elif call is commit:
+        assert commit(lib, _dims(num_requests=0), k=0, v=0, w=0, state=0, slots=0) == OK
+    else:
+        assert fmap(lib, _dims(num_requests=0), x=0, w=0, phi=0) == OK
+
+
+@pytest.mark.parametrize("call", [fwd, commit, fmap])
+def test_null_dims(lib, call):
+    assert call(lib, None) == NULL
+
+
+@pytest.mark.parametrize("call", [fwd, commit, fmap])
+@pytest.mark.parametrize("kw,expect", [
+    (dict(io_dtype=7), DTYPE),
+    (dict(num_requests=-1), DIMS),
+    (dict(num_heads=0), DIMS),
+    (dict(scale=-1.0), DIMS),
+    (dict(scale=float("nan")), DIMS),
+    (dict(scale=float("inf")), DIMS),
+    (dict(head_dim=96), UNSUP),
+    (dict(head_dim=256), UNSUP),
+    (dict(feat_half=48), UNSUP),
+    (dict(feat_half=256), UNSUP),
+    (dict(block_size=0), UNSUP),
+    (dict(block_size=65), UNSUP),
+])
+def test_bad_dims(lib, call, kw, expect):
+    assert call(lib, _dims(**kw)) == expect
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "w", "gamma", "state", "slots", "out"])
+def test_forward_null_pointers(lib, name):
+    assert fwd(lib, _dims(), **{name: 0}) == NULL
+
+
+@pytest.mark.parametrize("name", ["k", "v", "w", "state", "slots"])
+def test_commit_null_pointers(lib, name):
+    assert commit(lib, _dims(), **{name: 0}) == NULL
+
+
+@pytest.mark.parametrize("name", ["x", "w", "phi"])
+def test_feature_map_null_pointers(lib, name):
+    assert fmap(lib, _dims(), **{name: 0}) == NULL
+
+
+@pytest.mark.parametrize("name,off", [("q", 8), ("k", 2), ("v", 4), ("w", 8), ("state", 4),
+                                      ("out", 8), ("gamma", 2), ("slots", 1)])
+def test_forward_misaligned(lib, name, off):
+    assert fwd(lib, _dims(), **{name: FAKE + off}) == ALIGN
+
+
+def test_commit_misaligned(lib):
+    assert commit(lib, _dims(), state=FAKE + 8) == ALIGN
+    assert commit(lib, _dims(), k=FAKE + 2) == ALIGN
+
+
+@pytest.mark.parametrize("qs", [_st(req=-256), _st(tok=2 * 128 + 4), _st(head=129)])
+def test_forward_bad_input_strides(lib, qs):
+    assert fwd(lib, _dims(), qs=qs) == STRIDE
+
+
+def test_forward_overlapping_output_rows(lib):
+    # heads 128 apart but tokens only 64 apart: rows of different tokens overlap
+    assert fwd(lib, _dims(), outs=bha_strides(32 * 2 * 128, 64, 128)) == STRIDE
+    # broadcast (zero) stride is fine for an input but not for the output
+    assert fwd(lib, _dims(), outs=bha_strides(0, 256, 128)) == STRIDE
+
+
+def test_bad_w_head_stride(lib):
+    assert fwd(lib, _dims(), wh=-8) == STRIDE
+    assert fwd(lib, _dims(), wh=12) == STRIDE
+    assert commit(lib, _dims(), wh=4) == STRIDE
+
+
+def test_bad_slot_count(lib):
+    assert fwd(lib, _dims(), num_slots=0) == DIMS
+    assert commit(lib, _dims(), num_slots=-3) == DIMS
+
+
+def test_fp32_stride_alignment(lib):
+    # float32 tokens: strides must be multiples of 4 elements
+    assert fwd(lib, _dims(io_dtype=0), qs=_st(tok=2 * 128 + 2)) == STRIDE
+    assert fwd(lib, _dims(io_dtype=0), qs=_st(tok=2 * 128 + 4), outs=_st(tok=2 * 128 + 4),
+               out=FAKE + (1 << 26), q=FAKE, k=FAKE, v=FAKE, num_slots=0) == DIMS
+
+
+def test_size_overflow(lib):
+    huge = bha_strides(1 << 61, 256, 128)
+    assert fwd(lib, _dims(), qs=huge) == DIMS

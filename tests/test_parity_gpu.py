@@ -1,0 +1,249 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Inputs come from ``synth`` (seeded); the same exact values go to the device and
+to the oracle. Errors use the normwise metric max over (request, head) of
+max|got - ref| / max|ref|. Bars: 1e-4 with float32 I/O, 2e-2 with bf16 I/O
+(bf16 matrix-core inputs, fp32 accumulation).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_block_amd as bha
+import oracle
+import synth
+from helpers import normwise_err, pairs, record_to_plain, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = min(16, os.cpu_count() or 1)
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU visible")
+    bha.load_library()  # raises if libbha.so is missing: no fallback
+    return torch.device("cuda:0")
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+class Run:
+    """One case on the GPU: state built by chained commits, then one forward
+    and one commit of the active block; plus the oracle's view of each step."""
+
+    def __init__(self, case: synth.Case, dev):
+        self.c = case
+        self.dev = dev
+        c = case
+        self.w = to_device(c.w, c.io, dev)
+        self.gamma = torch.from_numpy(c.gamma).to(dev)
+        self.slots = torch.from_numpy(c.slot_ids).to(dev)
+        self.state = bha.new_state(c.num_slots, c.H, c.d, c.FW, dev)
+
+    def build_state(self):
+        c = self.c
+        for i in range(int(c.n_blocks.max(initial=0))):
+            act = np.nonzero(c.n_blocks > i)[0]
+            kb = np.stack([c.prefix_k[r][i * c.B:(i + 1) * c.B] for r in act])
+            vb = np.stack([c.prefix_v[r][i * c.B:(i + 1) * c.B] for r in act])
+            bha.state_commit(to_device(kb, c.io, self.dev), to_device(vb, c.io, self.dev), self.w,
+                             self.state, torch.from_numpy(c.slot_ids[act]).to(self.dev))
+        torch.cuda.synchronize()
+
+    def plain_state(self):
+        """(S [R][H][F][d], Z [R][H][F]) float64 of the batch's slots."""
+        rec = self.state.cpu().numpy()[self.c.slot_ids]
+        return record_to_plain(rec, self.c.d, self.c.F)
+
+    def oracle_state(self):
+        c = self.c
+        S = np.zeros((c.R, c.H, c.F, c.d))
+        Z = np.zeros((c.R, c.H, c.F))
+        w64 = c.w.astype(np.float64)
+        for r in range(c.R):
+            if c.n_blocks[r] == 0:
+                continue
+            k = np.ascontiguousarray(np.transpose(c.prefix_k[r], (1, 0, 2)))[None]
+            v = np.ascontiguousarray(np.transpose(c.prefix_v[r], (1, 0, 2)))[None]
+            s1, z1 = S[r:r + 1].copy(), Z[r:r + 1].copy()
+            oracle.state_commit_batch(s1, z1, k, v, w64, nthreads=NTHREADS)
+            S[r], Z[r] = s1[0], z1[0]
+        return S, Z
+
+    def forward(self, out=None):
+        c = self.c
+        q, k, v = (to_device(x, c.io, self.dev) for x in (c.q, c.k, c.v))
+        y = bha.block_forward(q, k, v, self.w, self.gamma, self.state, self.slots, out=out)
+        torch.cuda.synchronize()
+        return y
+
+    def oracle_forward(self, S, Z):
+        c = self.c
+        return oracle.block_forward_batch(pairs(c.q), pairs(c.k), pairs(c.v), c.w, c.gamma, S, Z,
+                                          nthreads=NTHREADS)
+
+    def commit_active(self):
+        c = self.c
+        bha.state_commit(to_device(c.k, c.io, self.dev), to_device(c.v, c.io, self.dev), self.w,
+                         self.state, self.slots)
+        torch.cuda.synchronize()
+
+
+def _full_check(case, dev):
+    tol = TOL[case.io]
+    run = Run(case, dev)
+    run.build_state()
+    S_gpu, Z_gpu = run.plain_state()
+    S_ora, Z_ora = run.oracle_state()
+    e_s = normwise_err(S_gpu, S_ora, (2, 3))
+    e_z = normwise_err(Z_gpu, Z_ora, (2,))
+    _log(f"[{case.name}] state build  S err {e_s:.2e}  Z err {e_z:.2e}")
+    assert e_s <= tol and e_z <= tol
+
+    y = to_host(run.forward())
+    ref_same = run.oracle_forward(S_gpu, Z_gpu)  # the same fp32 state bytes
+    ref_ora = run.oracle_forward(S_ora, Z_ora)   # the oracle's own state
+    e1 = normwise_err(pairs(y), ref_same, (2, 3))
+    e2 = normwise_err(pairs(y), ref_ora, (2, 3))
+    _log(f"[{case.name}] forward  err(same state) {e1:.2e}  err(oracle state) {e2:.2e}")
+    assert np.all(np.isfinite(y))
+    assert e1 <= tol and e2 <= tol
+
+    run.commit_active()
+    S2, Z2 = run.plain_state()
+    S_ref, Z_ref = S_gpu.copy(), Z_gpu.copy()
+    oracle.state_commit_batch(S_ref, Z_ref, pairs(case.k), pairs(case.v), case.w.astype(np.float64),
+                              nthreads=NTHREADS)
+    e_s = normwise_err(S2, S_ref, (2, 3))
+    e_z = normwise_err(Z2, Z_ref, (2,))
+    _log(f"[{case.name}] commit  S err {e_s:.2e}  Z err {e_z:.2e}")
+    assert e_s <= tol and e_z <= tol
+    return run
+
+
+def test_tiny_fp32_end_to_end(dev):
+    # 1 request, 1 head, d=64, FW=32, B=8, 4 committed blocks, gate 0.5, fp32 I/O
+    _full_check(synth.make_case("tiny"), dev)
+
+
+def test_b16_bf16_end_to_end(dev):
+    # 16 requests x 16 heads, d=128, FW=64, B=32, 2,048-token prefixes, bf16 I/O
+    _full_check(synth.make_case("b16"), dev)
+
+
+SWEEP = [
+    # (io, d, FW, B): B <= 32 with bf16 takes the matrix-core kernels, the rest the fp32 kernels
+    ("bf16", 128, 64, 32), ("bf16", 128, 64, 1), ("bf16", 128, 64, 17), ("bf16", 128, 32, 32),
+    ("bf16", 128, 128, 32), ("bf16", 64, 32, 8), ("bf16", 64, 64, 31), ("bf16", 64, 128, 32),
+    ("bf16", 128, 64, 33), ("bf16", 64, 32, 64), ("f32", 128, 64, 32), ("f32", 64, 128, 5),
+    ("f32", 128, 32, 64), ("f32", 64, 64, 1),
+]
+
+
+@pytest.mark.parametrize("io,d,fw,b", SWEEP)
+def test_shape_sweep(dev, io, d, fw, b):
+    # ragged prefixes of 0..3 blocks (0 = empty state), 5 requests, 3 heads
+    case = synth.make_case("tiny", R=5, H=3, d=d, FW=fw, B=b, io=io, blocks=(0, 3), gamma="uniform")
+    _log(f"[sweep] io={io} d={d} FW={fw} B={b} n_blocks={case.n_blocks.tolist()}")
+    _full_check(case, dev)
+
+
+def test_feature_map(dev):
+    for io, d, fw in (("bf16", 128, 64), ("f32", 64, 32), ("bf16", 64, 128)):
+        case = synth.make_case("tiny", R=3, H=2, d=d, FW=fw, B=7, io=io, with_prefix=False)
+        x = to_device(case.q, io, dev)
+        phi = to_host(bha.feature_map(x, to_device(case.w, io, dev)))
+        ref = np.empty_like(phi)
+        for h in range(case.H):
+            ref[:, :, h] = oracle.phi(case.q[:, :, h].reshape(-1, d), case.w[h]).reshape(3, 7, 2 * fw)
+        err = normwise_err(phi, ref, (3,))
+        _log(f"[feature_map] io={io} d={d} FW={fw} err {err:.2e}")
+        assert err <= 1e-5
+
+
+def test_strided_views_and_shared_map(dev):
+    # q, k, v as views of one fused [R][B][3][H][d] tensor; out as a [R][H][B][d]
+    # tensor seen through a permute; one W shared by every head
+    case = synth.make_case("tiny", R=4, H=3, d=128, FW=64, B=32, io="bf16", blocks=(1, 2),
+                           gamma="uniform")
+    case.w[:] = case.w[0]
+    run = Run(case, dev)
+    run.w = to_device(case.w[0], case.io, dev)  # [FW][d]: head stride 0
+    run.build_state()
+    fused = to_device(np.stack([case.q, case.k, case.v], axis=2), case.io, dev)
+    q, k, v = fused[:, :, 0], fused[:, :, 1], fused[:, :, 2]
+    out = torch.empty((case.R, case.H, case.B, case.d), dtype=torch.bfloat16, device=dev)
+    out_v = out.permute(0, 2, 1, 3)
+    bha.block_forward(q, k, v, run.w, run.gamma, run.state, run.slots, out=out_v)
+    torch.cuda.synchronize()
+    S, Z = run.plain_state()
+    err = normwise_err(pairs(to_host(out_v)), run.oracle_forward(S, Z), (2, 3))
+    _log(f"[strided] err {err:.2e}")
+    assert err <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("io,b", [("bf16", 32), ("f32", 8)])
+def test_out_of_range_slot_is_isolated(dev, io, b):
+    case = synth.make_case("tiny", R=4, H=2, d=64, FW=32, B=b, io=io, blocks=(1, 2), gamma="uniform")
+    run = Run(case, dev)
+    run.build_state()
+    before = run.state.clone()
+    bad = case.slot_ids.copy()
+    bad[2] = case.num_slots  # out of range
+    run.slots = torch.from_numpy(bad).to(dev)
+    y = to_host(run.forward())
+    assert np.all(np.isnan(y[2]))
+    good = [0, 1, 3]
+    S, Z = record_to_plain(before.cpu().numpy()[case.slot_ids], case.d, case.F)
+    ref = run.oracle_forward(S, Z)
+    assert normwise_err(pairs(y)[good], ref[good], (2, 3)) <= TOL[io]
+    run.commit_active()  # the bad request is skipped, the others commit
+    after = run.state.cpu().numpy()
+    untouched = np.setdiff1d(np.arange(case.num_slots), case.slot_ids[good])
+    assert np.array_equal(after[untouched], before.cpu().numpy()[untouched])
+
+
+def test_gate_zero_is_block_softmax(dev):
+    case = synth.make_case("tiny", R=3, H=2, d=128, FW=64, B=32, io="bf16", blocks=(2, 3),
+                           gamma="uniform")
+    case.gamma[:] = 0.0
+    run = Run(case, dev)
+    run.build_state()
+    y = pairs(to_host(run.forward()))
+    ref = oracle.block_forward_batch(pairs(case.q), pairs(case.k), pairs(case.v), case.w, case.gamma,
+                                     np.zeros((3, 2, 128, 128)), np.zeros((3, 2, 128)))
+    assert normwise_err(y, ref, (2, 3)) <= TOL["bf16"]
+
+
+def test_large_gate(dev):
+    case = synth.make_case("tiny", R=2, H=2, d=128, FW=64, B=32, io="bf16", blocks=(2, 3),
+                           gamma="uniform")
+    case.gamma[:] = 1e6
+    run = Run(case, dev)
+    run.build_state()
+    y = pairs(to_host(run.forward()))
+    S, Z = run.plain_state()
+    assert normwise_err(y, run.oracle_forward(S, Z), (2, 3)) <= TOL["bf16"]
+
+
+def test_bitwise_deterministic(dev):
+    case = synth.make_case("tiny", R=6, H=4, d=128, FW=64, B=32, io="bf16", blocks=(1, 3),
+                           gamma="uniform")
+    run = Run(case, dev)
+    run.build_state()
+    y1 = run.forward().clone()
+    y2 = run.forward()
+    assert torch.equal(y1, y2)
+    s0 = run.state.clone()
+    run.commit_active()
+    s1 = run.state.clone()
+    run.state.copy_(s0)
+    run.commit_active()
+    assert torch.equal(run.state, s1)
