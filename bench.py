@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the block-hybrid attention hot path on one MI355X.
+
+One step is one block cycle of the model's block-hybrid layers on a
+continuous-batching decode batch: for each of the 32 denoising steps of the
+active block every layer runs ``bha_block_forward`` over all requests and heads,
+and then every layer folds the finished block into its state with
+``bha_state_commit``. Each layer instance has its own state pool, W and gate,
+as the model's six block-hybrid layers do, so consecutive forwards of one layer
+do not find its 270 MB state in the 256 MB Infinity Cache.
+
+Default workload (decode256): 256 requests x 16 heads, d = 128, FW = 64
+(F = 128), B = 32, ragged prefixes of UniformInt{8..256} blocks (256..8,192
+tokens) committed into the states before timing, bf16 Q/K/V/W/O, fp32 states.
+
+Prints ONE JSON line: value = active-block tokens per second through
+block-hybrid attention (each forward moves R * B tokens through one layer),
+the roofline of the dominant kernel (the forward; algorithmic bytes per launch
+divided by its HIP-event-timed average launch duration, against 8 TB/s), and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "active-block tokens/s through block-hybrid attn; achieved HBM GB/s vs peak"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+KERNEL_SOURCES = ("linear_attention_block_amd/csrc/mfma.hip", "linear_attention_block_amd/csrc/bha_device.hpp")
+
+
+def forward_bytes(R, H, d, FW, B, es=2):
+    """Algorithmic HBM bytes of one bha_block_forward launch: per (request, head)
+    the fp32 S tiles and Z (read), Q, K, V (read) and O (written); W once per head."""
+    F = 2 * FW
+    return R * H * (d * F * 4 + F * 4 + 4 * B * d * es) + H * FW * d * es
+
+
+def commit_bytes(R, H, d, FW, B, es=2):
+    """Algorithmic HBM bytes of one bha_state_commit launch: per (request, head)
+    the state record read and written back, K and V read; W once per head."""
+    F = 2 * FW
+    return R * H * (2 * (d * F * 4 + F * 4) + 2 * B * d * es) + H * FW * d * es
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(config: str):
+    """HBM bytes per forward launch measured with rocprofv3 counters, if the
+    summary in profiles/ was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"forward_{config}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def record_to_plain(rec, d, F):
+    """State records [..., (d+1)F] -> (S [..., F, d], Z [..., F]) in float64,
+    following the record layout of include/bha.h (S in 32 x 4 tiles, then Z)."""
+    import numpy as np
+
+    f = np.arange(F)[:, None]
+    c = np.arange(d)[None, :]
+    idx = ((c // 32) * (F // 4) + f // 4) * 128 + (c % 32) * 4 + (f % 4)
+    rec = np.asarray(rec, dtype=np.float64)
+    return np.ascontiguousarray(rec[..., idx]), np.ascontiguousarray(rec[..., d * F:(d + 1) * F])
+
+
+def cpu_baseline(layer, case, denoise, n_req, log):
+    """Time the fp64 oracle on one block cycle of the first n_req requests."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B
+    n_req = min(n_req, R)
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+
+    def host(t):
+        return np.ascontiguousarray(
+            t[:n_req].float().cpu().numpy().astype(np.float64).transpose(0, 2, 1, 3))
+
+    q, k, v = host(layer["q"]), host(layer["k"]), host(layer["v"])
+    w = layer["w"].float().cpu().numpy().astype(np.float64)
+    g = layer["gamma"].cpu().numpy().astype(np.float64)
+    rec = layer["state"].cpu().numpy()[case.slot_ids[:n_req]]
+    S, Z = record_to_plain(rec, d, 2 * FW)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(denoise):
+        oracle.block_forward_batch(q, k, v, w, g, S, Z, nthreads=nthreads)
+    oracle.state_commit_batch(S, Z, k, v, w, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    tokens = denoise * n_req * B
+    log(f"cpu oracle: {n_req} requests x {H} heads, {denoise} forwards + 1 commit in {dt:.2f} s "
+        f"on {nthreads} threads")
+    return {
+        "value": tokens / dt,
+        "unit": "tokens/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": (f"one block cycle ({denoise} forwards + 1 commit, one layer) of the first {n_req} "
+                   f"of {R} requests, all {H} heads, same workload and state; fp64 C oracle, "
+                   f"{dt:.2f} s wall"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="decode256",
+                    choices=["decode256", "b16", "longctx2k", "longctx16k", "longctx32k", "wide2048"])
+    ap.add_argument("--layers", type=int, default=6, help="block-hybrid layer instances (default 6)")
+    ap.add_argument("--denoise", type=int, default=32, help="denoising forwards per block")
+    ap.add_argument("--cpu-sample-requests", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (counter scaling)")
+    args = ap.parse_args()
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this library's hot path runs on one GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported. Every (request, head) pair is independent, "
+              "so requests or heads shard across GPUs with no exchange; run one process per GPU.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import linear_attention_block_amd as bha
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bha.load_library()
+    case = synth.make_case(args.config, with_prefix=False, with_qkv=False)
+    R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B
+    nl, nd = args.layers, args.denoise
+    slots = torch.from_numpy(case.slot_ids).to(dev)
+    max_blocks = int(case.n_blocks.max())
+    act = [torch.from_numpy(case.slot_ids[case.n_blocks > i]).to(dev) for i in range(max_blocks)]
+
+    t_setup = time.perf_counter()
+    layers = []
+    for L in range(nl):
+        w, gamma = synth.device_layer_params(args.config, L, dev)
+        state = bha.new_state(case.num_slots, H, d, FW, dev)
+        for i in range(max_blocks):
+            kb, vb = synth.device_blocks(args.config, i, act[i].numel(), dev, layer=L)
+            bha.state_commit(kb, vb, w, state, act[i])
+        q, k, v = synth.device_step_qkv(args.config, 0, R, dev, layer=L)
+        out = torch.empty_like(q)
+        layers.append(dict(w=w, gamma=gamma, state=state, q=q, k=k, v=v, out=out,
+                           fwd=bha.prepare_forward(q, k, v, w, gamma, state, slots, out),
+                           com=bha.prepare_commit(k, v, w, state, slots)))
+    torch.cuda.synchronize()
+    log(f"setup: {nl} layers x {R} requests, prefixes {int(case.n_blocks.min()) * B}.."
+        f"{max_blocks * B} tokens ({int(case.n_blocks.sum()) * B} total), "
+        f"{time.perf_counter() - t_setup:.1f} s")
+
+    n_fwd, n_com = nd * nl, nl
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps * (n_fwd + n_com))]
+
+    def step(evs):
+        it = iter(evs) if evs is not None else None
+        for _ in range(nd):
+            for lay in layers:
+                if it is not None:
+                    e0, e1 = next(it)
+                    e0.record()
+                    lay["fwd"]()
+                    e1.record()
+                else:
+                    lay["fwd"]()
+        for lay in layers:
+            if it is not None:
+                e0, e1 = next(it)
+                e0.record()
+                lay["com"]()
+                e1.record()
+            else:
+                lay["com"]()
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    per = n_fwd + n_com
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s * per:(s + 1) * per])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    fwd_ms, com_ms = [], []
+    for s in range(args.steps):
+        blk = ev[s * per:(s + 1) * per]
+        fwd_ms += [a.elapsed_time(b) for a, b in blk[:n_fwd]]
+        com_ms += [a.elapsed_time(b) for a, b in blk[n_fwd:]]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms) * 1e-3
+    com_avg = sum(com_ms) / len(com_ms) * 1e-3
+    fb, cb = forward_bytes(R, H, d, FW, B), commit_bytes(R, H, d, FW, B)
+    tokens = args.steps * nd * nl * R * B
+    value = tokens / elapsed
+    log(f"forward: avg {fwd_avg * 1e6:.1f} us/launch, {fb / fwd_avg / 1e9:.0f} GB/s algorithmic "
+        f"({fb / 1e6:.1f} MB/launch); commit: avg {com_avg * 1e6:.1f} us/launch, "
+        f"{cb / com_avg / 1e9:.0f} GB/s ({cb / 1e6:.1f} MB/launch)")
+    log(f"step: {elapsed / args.steps * 1e3:.2f} ms ({nd} x {nl} forwards + {nl} commits); "
+        f"{value / 1e6:.1f} M tokens/s")
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x {args.copy_calibration_mib} MiB device copies")
+
+    achieved = fb / fwd_avg / 1e9
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{args.config}: continuous-batching decode, {R} requests x {H} heads, d={d}, "
+                         f"FW={FW} (F={2 * FW}), B={B}, ragged prefixes {int(case.n_blocks.min()) * B}-"
+                         f"{max_blocks * B} tokens; per step {nd} denoising forwards then 1 commit "
+                         f"in each of {nl} block-hybrid layers"),
+            "requests": R, "heads": H, "head_dim": d, "feat_half": FW, "block": B,
+            "denoise_steps": nd, "layers": nl, "state_dtype": "f32", "io_dtype": "bf16",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": read_traffic(args.config),
+            "kernel": "bha_block_forward (forward_mfma_kernel<128,64>)" if (d, FW) == (128, 64)
+            else "bha_block_forward",
+            "bytes_per_launch": fb,
+            "avg_launch_us": fwd_avg * 1e6,
+        },
+        "commit": {
+            "avg_launch_us": com_avg * 1e6,
+            "bytes_per_launch": cb,
+            "achieved_GBps": cb / com_avg / 1e9,
+            "frac": cb / com_avg / 1e9 / PEAK_HBM_GBS,
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(layers[0], case, nd,
+                                                                          args.cpu_sample_requests, log),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

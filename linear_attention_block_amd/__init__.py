@@ -28,6 +28,7 @@ import torch
 __all__ = [
     "BhaError", "library_path", "load_library", "version", "status_string",
     "state_record_floats", "new_state", "feature_map", "block_forward", "state_commit",
+    "prepare_forward", "prepare_commit",
     "BHA_F32", "BHA_BF16",
 ]
 
@@ -183,16 +184,13 @@ def feature_map(x: torch.Tensor, w: torch.Tensor, *, stream=None) -> torch.Tenso
     return phi
 
 
-def block_forward(q, k, v, w, gamma, state, slot_ids, *, out=None, scale: float = 0.0,
-                  stream=None) -> torch.Tensor:
-    """One block-hybrid attention step for every (request, head); returns ``out``."""
-    lib = load_library()
+def _forward_args(q, k, v, w, gamma, state, slot_ids, out, scale, stream):
     qs = _tok_strides(q, "q")
     R, B, H, d = q.shape
     for t, n in ((k, "k"), (v, "v")):
         if t.shape != q.shape:
             raise ValueError(f"{n} must match q in shape")
-        if (t.stride(0), t.stride(1), t.stride(2)) != (qs.req, qs.tok, qs.head):
+        if (t.stride(0), t.stride(1), t.stride(2)) != (qs.req, qs.tok, qs.head) or t.stride(3) != 1:
             raise ValueError(f"{n} must have the strides of q")
         if t.dtype != q.dtype:
             raise TypeError(f"{n} must have the dtype of q")
@@ -201,24 +199,53 @@ def block_forward(q, k, v, w, gamma, state, slot_ids, *, out=None, scale: float 
         raise TypeError("w must have the dtype of q")
     if gamma.dtype != torch.float32 or gamma.numel() != H or not gamma.is_contiguous():
         raise ValueError("gamma must be a contiguous float32 [H] tensor")
+    num_slots = _num_slots(state, H, d, fw)
+    if slot_ids.dtype != torch.int32 or slot_ids.numel() != R or not slot_ids.is_contiguous():
+        raise ValueError("slot_ids must be a contiguous int32 [R] tensor")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    os_ = _tok_strides(out, "out")
+    _check_device(q.device, k, v, w, gamma, state, slot_ids, out)
+    dims = bha_dims(R, H, d, fw, B, _io_dtype(q), float(scale))
+    return (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(qs), _ptr(w), wh,
+            _ptr(gamma), _ptr(state), num_slots, _ptr(slot_ids), _ptr(out), ctypes.byref(os_),
+            _stream(q.device, stream)), (dims, qs, os_)
+
+
+def _commit_args(k, v, w, state, slot_ids, stream):
+    ks = _tok_strides(k, "k")
+    R, B, H, d = k.shape
+    if v.shape != k.shape or (v.stride(0), v.stride(1), v.stride(2)) != (ks.req, ks.tok, ks.head):
+        raise ValueError("v must match k in shape and strides")
+    if v.dtype != k.dtype or w.dtype != k.dtype:
+        raise TypeError("k, v and w must share one dtype")
+    fw, wh = _w_stride(w, H, d)
+    num_slots = _num_slots(state, H, d, fw)
+    if slot_ids.dtype != torch.int32 or slot_ids.numel() != R or not slot_ids.is_contiguous():
+        raise ValueError("slot_ids must be a contiguous int32 [R] tensor")
+    _check_device(k.device, v, w, state, slot_ids)
+    dims = bha_dims(R, H, d, fw, B, _io_dtype(k), 0.0)
+    return (ctypes.byref(dims), _ptr(k), _ptr(v), ctypes.byref(ks), _ptr(w), wh, _ptr(state),
+            num_slots, _ptr(slot_ids), _stream(k.device, stream)), (dims, ks)
+
+
+def _num_slots(state, H, d, fw):
     if state.dtype != torch.float32 or not state.is_contiguous():
         raise ValueError("state must be a contiguous float32 tensor")
     rec = (d + 1) * 2 * fw
-    if state.numel() % (H * rec) != 0:
+    if state.numel() % (H * rec) != 0 or state.numel() == 0:
         raise ValueError("state size is not a whole number of [H][record] slots")
-    num_slots = state.numel() // (H * rec)
-    if slot_ids.dtype != torch.int32 or slot_ids.numel() != R or not slot_ids.is_contiguous():
-        raise ValueError("slot_ids must be a contiguous int32 [R] tensor")
+    return state.numel() // (H * rec)
+
+
+def block_forward(q, k, v, w, gamma, state, slot_ids, *, out=None, scale: float = 0.0,
+                  stream=None) -> torch.Tensor:
+    """One block-hybrid attention step for every (request, head); returns ``out``."""
+    lib = load_library()
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
-    os_ = _tok_strides(out, "out")
-    if out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("out must match q in shape and dtype")
-    _check_device(q.device, k, v, w, gamma, state, slot_ids, out)
-    dims = bha_dims(R, H, d, fw, B, _io_dtype(q), float(scale))
-    st = lib.bha_block_forward(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(qs),
-                               _ptr(w), wh, _ptr(gamma), _ptr(state), num_slots, _ptr(slot_ids),
-                               _ptr(out), ctypes.byref(os_), _stream(q.device, stream))
+    args, _keep = _forward_args(q, k, v, w, gamma, state, slot_ids, out, scale, stream)
+    st = lib.bha_block_forward(*args)
     if st != 0:
         raise BhaError("bha_block_forward", st)
     return out
@@ -227,24 +254,35 @@ def block_forward(q, k, v, w, gamma, state, slot_ids, *, out=None, scale: float 
 def state_commit(k, v, w, state, slot_ids, *, stream=None) -> None:
     """Fold the block (k, v) into the state records of ``slot_ids`` (in place)."""
     lib = load_library()
-    ks = _tok_strides(k, "k")
-    R, B, H, d = k.shape
-    if v.shape != k.shape or (v.stride(0), v.stride(1), v.stride(2)) != (ks.req, ks.tok, ks.head):
-        raise ValueError("v must match k in shape and strides")
-    if v.dtype != k.dtype or w.dtype != k.dtype:
-        raise TypeError("k, v and w must share one dtype")
-    fw, wh = _w_stride(w, H, d)
-    if state.dtype != torch.float32 or not state.is_contiguous():
-        raise ValueError("state must be a contiguous float32 tensor")
-    rec = (d + 1) * 2 * fw
-    if state.numel() % (H * rec) != 0:
-        raise ValueError("state size is not a whole number of [H][record] slots")
-    num_slots = state.numel() // (H * rec)
-    if slot_ids.dtype != torch.int32 or slot_ids.numel() != R or not slot_ids.is_contiguous():
-        raise ValueError("slot_ids must be a contiguous int32 [R] tensor")
-    _check_device(k.device, v, w, state, slot_ids)
-    dims = bha_dims(R, H, d, fw, B, _io_dtype(k), 0.0)
-    st = lib.bha_state_commit(ctypes.byref(dims), _ptr(k), _ptr(v), ctypes.byref(ks), _ptr(w), wh,
-                              _ptr(state), num_slots, _ptr(slot_ids), _stream(k.device, stream))
+    args, _keep = _commit_args(k, v, w, state, slot_ids, stream)
+    st = lib.bha_state_commit(*args)
     if st != 0:
         raise BhaError("bha_state_commit", st)
+
+
+class _Prepared:
+    """A C-ABI call whose arguments were checked and marshalled once; calling it
+    enqueues the same call again (on the stream captured at preparation). The
+    tensors must stay alive and keep their storage while it is used."""
+
+    def __init__(self, fn, name, args, keep):
+        self._fn, self._name, self._args, self._keep = fn, name, args, keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != 0:
+            raise BhaError(self._name, st)
+
+
+def prepare_forward(q, k, v, w, gamma, state, slot_ids, out, *, scale: float = 0.0, stream=None):
+    """Marshal a bha_block_forward call once, for launch-rate-bound loops."""
+    args, keep = _forward_args(q, k, v, w, gamma, state, slot_ids, out, scale, stream)
+    keep = keep + (q, k, v, w, gamma, state, slot_ids, out)
+    return _Prepared(load_library().bha_block_forward, "bha_block_forward", args, keep)
+
+
+def prepare_commit(k, v, w, state, slot_ids, *, stream=None):
+    """Marshal a bha_state_commit call once, for launch-rate-bound loops."""
+    args, keep = _commit_args(k, v, w, state, slot_ids, stream)
+    keep = keep + (k, v, w, state, slot_ids)
+    return _Prepared(load_library().bha_state_commit, "bha_state_commit", args, keep)

@@ -112,7 +112,7 @@ def _cast(x: np.ndarray, io: str) -> np.ndarray:
     return round_bf16(x) if io == "bf16" else x
 
 
-def make_case(name: str, *, R=None, with_prefix=True, step=0, **over) -> Case:
+def make_case(name: str, *, R=None, with_prefix=True, with_qkv=True, step=0, **over) -> Case:
     """Draw a whole case on the host. ``R`` (and any shape key) may be overridden,
     e.g. to take the first requests of a large config; ``step`` selects which
     denoising step's Q/K/V is drawn (each step draws fresh values)."""
@@ -139,40 +139,71 @@ def make_case(name: str, *, R=None, with_prefix=True, step=0, **over) -> Case:
             prefix_k.append(_cast(st["prefix"].standard_normal((n, H, d), dtype=np.float32), io))
             prefix_v.append(_cast(st["prefix"].standard_normal((n, H, d), dtype=np.float32), io))
     g = st["step"]
-    for _ in range(step):
-        g.standard_normal((3, R, B, H, d), dtype=np.float32)
-    qkv = _cast(g.standard_normal((3, R, B, H, d), dtype=np.float32), io)
+    if with_qkv:
+        for _ in range(step):
+            g.standard_normal((3, R, B, H, d), dtype=np.float32)
+        qkv = _cast(g.standard_normal((3, R, B, H, d), dtype=np.float32), io)
+    else:
+        qkv = np.zeros((3, 0, B, H, d), dtype=np.float32)
     return Case(name=name, R=R, H=H, d=d, FW=FW, B=B, io=io, num_slots=num_slots,
                 q=qkv[0], k=qkv[1], v=qkv[2], w=w, gamma=gamma, slot_ids=slot_ids,
                 n_blocks=n_blocks, prefix_k=prefix_k, prefix_v=prefix_v)
 
 
-def device_blocks(name: str, block_index: int, rows: int, device, *, R=None, **over):
+def _device_gen(device, *keys):
+    import torch
+
+    gen = torch.Generator(device=device)
+    seed = 0
+    for k in keys:
+        seed = (seed * 1_000_003 + int(k)) % (1 << 62)
+    gen.manual_seed(seed)
+    return gen
+
+
+def _io_torch(io):
+    import torch
+
+    return torch.bfloat16 if io == "bf16" else torch.float32
+
+
+def device_layer_params(name: str, layer: int, device, **over):
+    """W ([H][FW][d], N(0, 1/d)) and gate ([H], U(0, 1)) of one layer instance,
+    drawn on ``device``."""
+    import torch
+
+    cfg = dict(CONFIGS[name])
+    cfg.update(over)
+    H, d, FW = cfg["H"], cfg["d"], cfg["FW"]
+    gen = _device_gen(device, 1000 + cfg["cid"], 11, layer)
+    w = torch.randn((H, FW, d), generator=gen, device=device, dtype=torch.float32) / float(np.sqrt(d))
+    gamma = torch.rand((H,), generator=gen, device=device, dtype=torch.float32)
+    return w.to(_io_torch(cfg["io"])), gamma
+
+
+def device_blocks(name: str, block_index: int, rows: int, device, *, layer: int = 0, **over):
     """Prefix K and V of one block index for ``rows`` requests, drawn on ``device``
-    with a torch generator seeded from the config id and the block index.
-    Returns two [rows][B][H][d] tensors in the config's I/O dtype."""
+    with a torch generator seeded from the config id, the layer and the block
+    index. Returns two [rows][B][H][d] tensors in the config's I/O dtype."""
     import torch
 
     cfg = dict(CONFIGS[name])
     cfg.update(over)
     B, H, d = cfg["B"], cfg["H"], cfg["d"]
-    gen = torch.Generator(device=device)
-    gen.manual_seed((1000 + cfg["cid"]) * 1_000_003 + block_index)
-    dt = torch.bfloat16 if cfg["io"] == "bf16" else torch.float32
+    gen = _device_gen(device, 1000 + cfg["cid"], 22, layer, block_index)
     kv = torch.randn((2, rows, B, H, d), generator=gen, device=device, dtype=torch.float32)
-    kv = kv.to(dt)
+    kv = kv.to(_io_torch(cfg["io"]))
     return kv[0], kv[1]
 
 
-def device_step_qkv(name: str, step: int, R: int, device, **over):
+def device_step_qkv(name: str, step: int, R: int, device, *, layer: int = 0, **over):
     """Fresh Q, K, V ([R][B][H][d] each) of one denoising step, drawn on ``device``."""
     import torch
 
     cfg = dict(CONFIGS[name])
     cfg.update(over)
     B, H, d = cfg["B"], cfg["H"], cfg["d"]
-    gen = torch.Generator(device=device)
-    gen.manual_seed((1000 + cfg["cid"]) * 7_000_003 + step)
-    dt = torch.bfloat16 if cfg["io"] == "bf16" else torch.float32
-    qkv = torch.randn((3, R, B, H, d), generator=gen, device=device, dtype=torch.float32).to(dt)
+    gen = _device_gen(device, 1000 + cfg["cid"], 33, layer, step)
+    qkv = torch.randn((3, R, B, H, d), generator=gen, device=device, dtype=torch.float32)
+    qkv = qkv.to(_io_torch(cfg["io"]))
     return qkv[0], qkv[1], qkv[2]
