@@ -61,48 +61,77 @@ __device__ __forceinline__ void load_state_slice(const float* rec_slice, int lan
     for (int t = 0; t < NSL; ++t) sv[t] = __builtin_nontemporal_load(p + t * 64);
 }
 
-// Stage rows [0, 32) x d of a bf16 token tensor into LDS (row stride RS),
-// zero-filling rows >= nrows.
-template <int D, int NT, int RS>
-__device__ __forceinline__ void stage_rows(uint16_t* dst, const uint16_t* src, int64_t tok, int nrows, int tid)
-{
-    constexpr int CH = D / 8;
-    for (int idx = tid; idx < 32 * CH; idx += NT) {
-        const int t = idx / CH, ch = idx % CH;
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (t < nrows) x = *reinterpret_cast<const uint4*>(src + t * tok + ch * 8);
-        *reinterpret_cast<uint4*>(dst + t * RS + ch * 8) = x;
-    }
-}
+// A thread's share of the 16-byte chunks of a 32-row x D bf16 token block,
+// held in registers between the global loads and the LDS writes so that all
+// global loads of a work-group can be issued back to back. Rows >= nrows are
+// zero.
+template <int D, int NT>
+struct RowChunks {
+    static constexpr int CH = D / 8;
+    static constexpr int N = 32 * CH / NT;
+    uint4 v[N];
 
-// Stage V transposed: Vt[c][t] (row stride VS), zero for t >= nrows.
-template <int D, int NT, int VS>
-__device__ __forceinline__ void stage_vt(uint16_t* dst, const uint16_t* src, int64_t tok, int nrows, int tid)
-{
-    constexpr int CH = D / 8;
-    for (int idx = tid; idx < 32 * CH; idx += NT) {
-        const int t = idx / CH, ch = idx % CH;
-        uint4 x = make_uint4(0u, 0u, 0u, 0u);
-        if (t < nrows) x = *reinterpret_cast<const uint4*>(src + t * tok + ch * 8);
-        const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+    __device__ __forceinline__ void load(const uint16_t* src, int64_t tok, int nrows, int tid)
+    {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            dst[(ch * 8 + 2 * e) * VS + t] = static_cast<uint16_t>(w4[e] & 0xFFFFu);
-            dst[(ch * 8 + 2 * e + 1) * VS + t] = static_cast<uint16_t>(w4[e] >> 16);
+        for (int i = 0; i < N; ++i) {
+            const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
+            v[i] = make_uint4(0u, 0u, 0u, 0u);
+            if (t < nrows) v[i] = *reinterpret_cast<const uint4*>(src + t * tok + ch * 8);
         }
     }
-}
-
-// Stage W (FW rows of d bf16) into LDS.
-template <int D, int FW, int NT, int RS>
-__device__ __forceinline__ void stage_w(uint16_t* dst, const uint16_t* src, int tid)
-{
-    constexpr int CH = D / 8;
-    for (int idx = tid; idx < FW * CH; idx += NT) {
-        const int j = idx / CH, ch = idx % CH;
-        *reinterpret_cast<uint4*>(dst + j * RS + ch * 8) = *reinterpret_cast<const uint4*>(src + j * D + ch * 8);
+    // row-major copy, row stride RS
+    template <int RS>
+    __device__ __forceinline__ void store_rows(uint16_t* dst, int tid) const
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
+            *reinterpret_cast<uint4*>(dst + t * RS + ch * 8) = v[i];
+        }
     }
-}
+    // transposed copy dst[c][t], row stride VS
+    template <int VS>
+    __device__ __forceinline__ void store_transposed(uint16_t* dst, int tid) const
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
+            const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dst[(ch * 8 + 2 * e) * VS + t] = static_cast<uint16_t>(w4[e] & 0xFFFFu);
+                dst[(ch * 8 + 2 * e + 1) * VS + t] = static_cast<uint16_t>(w4[e] >> 16);
+            }
+        }
+    }
+};
+
+// A thread's share of one head's W (FW rows of D bf16).
+template <int D, int FW, int NT>
+struct WChunks {
+    static constexpr int CH = D / 8;
+    static constexpr int N = FW * CH / NT;
+    uint4 v[N];
+
+    __device__ __forceinline__ void load(const uint16_t* src, int tid)
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = tid + i * NT, j = idx / CH, ch = idx % CH;
+            v[i] = *reinterpret_cast<const uint4*>(src + j * D + ch * 8);
+        }
+    }
+    template <int RS>
+    __device__ __forceinline__ void store_rows(uint16_t* dst, int tid) const
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = tid + i * NT, j = idx / CH, ch = idx % CH;
+            *reinterpret_cast<uint4*>(dst + j * RS + ch * 8) = v[i];
+        }
+    }
+};
 
 // u^T = W^T X^T for the 32 staged token rows X (lane = token).
 template <int D, int FW, int RS>
@@ -119,52 +148,29 @@ __device__ __forceinline__ void feature_logits(const uint16_t* Ws, const uint16_
     }
 }
 
-// In place: u -> exp(u - max u) * (1/sum) for the first half, and returns in
-// en the second half exp(-u - max(-u)) * (1/sum). The FW values of one token
-// are split between lanes n and n + 32.
+// Maximum and minimum of one token's FW feature logits, split between lanes
+// n and n + 32.
 template <int FW>
-__device__ __forceinline__ void hedgehog_softmax(f32x16 (&ep)[FW / 32], f32x16 (&en)[FW / 32])
+__device__ __forceinline__ void logit_range(const f32x16 (&u)[FW / 32], float& mx, float& mn)
 {
-    float mx = -INFINITY, mn = INFINITY;
+    mx = -INFINITY;
+    mn = INFINITY;
 #pragma unroll
     for (int T = 0; T < FW / 32; ++T)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            mx = fmaxf(mx, ep[T][v]);
-            mn = fminf(mn, ep[T][v]);
+            mx = fmaxf(mx, u[T][v]);
+            mn = fminf(mn, u[T][v]);
         }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     mn = fminf(mn, __shfl_xor(mn, 32, 64));
-    float sp = 0.0f, sn = 0.0f;
-#pragma unroll
-    for (int T = 0; T < FW / 32; ++T)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float x = ep[T][v];
-            const float a = __expf(x - mx);
-            const float b = __expf(mn - x);
-            ep[T][v] = a;
-            en[T][v] = b;
-            sp += a;
-            sn += b;
-        }
-    sp += __shfl_xor(sp, 32, 64);
-    sn += __shfl_xor(sn, 32, 64);
-    const float ip = 1.0f / sp, in = 1.0f / sn;
-#pragma unroll
-    for (int T = 0; T < FW / 32; ++T)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            ep[T][v] *= ip;
-            en[T][v] *= in;
-        }
 }
 
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
 template <int D, int FW>
-__global__ __launch_bounds__(64 * (D / 32)) void forward_mfma_kernel(ForwardArgs a)
+__global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(3, 3))) void forward_mfma_kernel(ForwardArgs a)
 {
     using C = Cfg<D, FW>;
     constexpr int F = C::F;
@@ -190,85 +196,84 @@ __global__ __launch_bounds__(64 * (D / 32)) void forward_mfma_kernel(ForwardArgs
     }
     const float* rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * F;
 
+    // All global loads first, small operands before the state stream, so that
+    // waiting for the operands (the vector-memory counter retires in order)
+    // does not wait for the state.
+    const int64_t base = static_cast<int64_t>(r) * a.qs.req + static_cast<int64_t>(h) * a.qs.head;
+    RowChunks<D, C::NT> qc, kc, vc;
+    WChunks<D, FW, C::NT> wc;
+    qc.load(static_cast<const uint16_t*>(a.q) + base, a.qs.tok, B, tid);
+    kc.load(static_cast<const uint16_t*>(a.k) + base, a.qs.tok, B, tid);
+    vc.load(static_cast<const uint16_t*>(a.v) + base, a.qs.tok, B, tid);
+    wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
+    f32x4 zc = f32x4{};
+    if (tid < F / 4) zc = reinterpret_cast<const f32x4*>(rec + D * F)[tid];
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 sv[C::NSL];
     load_state_slice(rec + wv * F * 32, lane, sv);
-
-    const int64_t base = static_cast<int64_t>(r) * a.qs.req + static_cast<int64_t>(h) * a.qs.head;
-    stage_rows<D, C::NT, C::RS>(Qs, static_cast<const uint16_t*>(a.q) + base, a.qs.tok, B, tid);
-    stage_rows<D, C::NT, C::RS>(Ks, static_cast<const uint16_t*>(a.k) + base, a.qs.tok, B, tid);
-    stage_vt<D, C::NT, C::VS>(Vt, static_cast<const uint16_t*>(a.v) + base, a.qs.tok, B, tid);
-    stage_w<D, FW, C::NT, C::RS>(Ws, static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
-    for (int f4 = tid; f4 < F / 4; f4 += C::NT)
-        reinterpret_cast<f32x4*>(Zs)[f4] = reinterpret_cast<const f32x4*>(rec + D * F)[f4];
+    __builtin_amdgcn_sched_barrier(0);
+    qc.template store_rows<C::RS>(Qs, tid);
+    kc.template store_rows<C::RS>(Ks, tid);
+    vc.template store_transposed<C::VS>(Vt, tid);
+    wc.template store_rows<C::RS>(Ws, tid);
+    if (tid < F / 4) reinterpret_cast<f32x4*>(Zs)[tid] = zc;
     __syncthreads();
 
-    // phi(q) for token ln: both halves, fp32, in accumulator layout
-    f32x16 ep[FW / 32], en[FW / 32];
-    feature_logits<D, FW, C::RS>(Ws, Qs, ln, g, ep);
-    hedgehog_softmax<FW>(ep, en);
-
-    // den = phi(q) . Z
-    float den = 0.0f;
-#pragma unroll
-    for (int T = 0; T < FW / 32; ++T)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int fw = 32 * T + 8 * (v >> 2) + 4 * g + (v & 3);
-            den = fmaf(ep[T][v], Zs[fw], den);
-            den = fmaf(en[T][v], Zs[FW + fw], den);
-        }
-    den += __shfl_xor(den, 32, 64);
-
-    // phi(q) as bf16 B operands, one per 16 features
+    // phi(q) for token ln as bf16 B operands of unnormalised exponentials,
+    // e+ = exp(u - max u) and e- = exp(min u - u); the two softmax
+    // normalisers sp, sn are applied after the contraction.
+    float sp = 0.0f, sn = 0.0f, den = 0.0f;
     bf16x8 pb[F / 16];
+    {
+        f32x16 u[FW / 32];
+        feature_logits<D, FW, C::RS>(Ws, Qs, ln, g, u);
+        float mx, mn;
+        logit_range<FW>(u, mx, mn);
+        float dp = 0.0f, dn = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < F / 16; ++kb) {
-        const bool neg = 16 * kb >= FW;
-        const int fw0 = 16 * kb - (neg ? FW : 0);
-        const int T = fw0 / 32, rb = (fw0 % 32) / 16 * 8;
+        for (int T = 0; T < FW / 32; ++T)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[kb][e] = static_cast<__bf16>(neg ? en[T][rb + e] : ep[T][rb + e]);
+            for (int v = 0; v < 16; ++v) {
+                const int fw = 32 * T + 8 * (v >> 2) + 4 * g + (v & 3);
+                const float ea = __expf(u[T][v] - mx);
+                const float eb = __expf(mn - u[T][v]);
+                sp += ea;
+                sn += eb;
+                dp = fmaf(ea, Zs[fw], dp);
+                dn = fmaf(eb, Zs[FW + fw], dn);
+                pb[2 * T + (v >> 3)][v & 7] = static_cast<__bf16>(ea);
+                pb[FW / 16 + 2 * T + (v >> 3)][v & 7] = static_cast<__bf16>(eb);
+            }
+        sp += __shfl_xor(sp, 32, 64);
+        sn += __shfl_xor(sn, 32, 64);
+        dp += __shfl_xor(dp, 32, 64);
+        dn += __shfl_xor(dn, 32, 64);
+        den = dp / sp + dn / sn;
     }
 
     // block logits s^T = K Q^T, masked beyond B, exponentials and row sums
-    f32x16 sacc = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb)
-        sacc = mfma32(lds_frag(Ks + ln * C::RS + 16 * kb + 8 * g), lds_frag(Qs + ln * C::RS + 16 * kb + 8 * g), sacc);
-    float m = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int j = 8 * (v >> 2) + 4 * g + (v & 3);
-        const float s = j < B ? sacc[v] * a.scale : -INFINITY;
-        sacc[v] = s;
-        m = fmaxf(m, s);
-    }
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    float l = 0.0f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const float p = __expf(sacc[v] - m);
-        sacc[v] = p;
-        l += p;
-    }
-    l += __shfl_xor(l, 32, 64);
+    float m = -INFINITY, l = 0.0f;
     bf16x8 pp[2];
+    {
+        f32x16 sacc = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < C::NKB; ++kb)
+            sacc = mfma32(lds_frag(Ks + ln * C::RS + 16 * kb + 8 * g), lds_frag(Qs + ln * C::RS + 16 * kb + 8 * g), sacc);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pp[kb][e] = static_cast<__bf16>(sacc[8 * kb + e]);
-
-    // linear read: lin^T = S^T phi(q)^T over this wave's 32 columns
-    f32x16 lacc = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < F / 16; ++kb) {
-        bf16x8 as;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            as[e] = static_cast<__bf16>(sv[2 * kb][e]);
-            as[4 + e] = static_cast<__bf16>(sv[2 * kb + 1][e]);
+        for (int v = 0; v < 16; ++v) {
+            const int j = 8 * (v >> 2) + 4 * g + (v & 3);
+            const float s = j < B ? sacc[v] * a.scale : -INFINITY;
+            sacc[v] = s;
+            m = fmaxf(m, s);
         }
-        lacc = mfma32(as, pb[kb], lacc);
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float p = __expf(sacc[v] - m);
+            l += p;
+            pp[v >> 3][v & 7] = static_cast<__bf16>(p);
+        }
+        l += __shfl_xor(l, 32, 64);
     }
 
     // within-block numerator: sm^T = V^T P^T over this wave's 32 columns
@@ -278,8 +283,26 @@ __global__ __launch_bounds__(64 * (D / 32)) void forward_mfma_kernel(ForwardArgs
         const uint16_t* vr = Vt + (32 * wv + ln) * C::VS + 16 * kb + 4 * g;
         const uint2 lo = *reinterpret_cast<const uint2*>(vr);
         const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-        const uint4 q4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        vacc = mfma32(__builtin_bit_cast(bf16x8, q4), pp[kb], vacc);
+        vacc = mfma32(__builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), pp[kb], vacc);
+    }
+
+    // linear read over this wave's 32 columns: lacc = sum_f e_f S_f with the
+    // + half rescaled by sn/sp, so that phi(q)^T S = lacc / sn
+    f32x16 lacc = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < F / 16; ++kb) {
+        if (kb == FW / 16) {
+            const float rs = sn / sp;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) lacc[v] *= rs;
+        }
+        bf16x8 as;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            as[e] = static_cast<__bf16>(sv[2 * kb][e]);
+            as[4 + e] = static_cast<__bf16>(sv[2 * kb + 1][e]);
+        }
+        lacc = mfma32(as, pb[kb], lacc);
     }
 
     // merge and store this wave's 32 columns of token ln
@@ -287,6 +310,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void forward_mfma_kernel(ForwardArgs
         float al, be;
         merge_weights(a.gamma[h], m, al, be);
         const float inv = 1.0f / (al * l + be * den);
+        const float bl = be / sn;
         uint16_t* orow = out + static_cast<int64_t>(ln) * a.os.tok + 32 * wv + 4 * g;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
@@ -294,8 +318,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void forward_mfma_kernel(ForwardArgs
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int v0 = 4 * q4 + 2 * e;
-                const float y0 = (al * vacc[v0] + be * lacc[v0]) * inv;
-                const float y1 = (al * vacc[v0 + 1] + be * lacc[v0 + 1]) * inv;
+                const float y0 = (al * vacc[v0] + bl * lacc[v0]) * inv;
+                const float y1 = (al * vacc[v0 + 1] + bl * lacc[v0 + 1]) * inv;
                 pk[e] = static_cast<uint32_t>(bf16_bits(y0)) | (static_cast<uint32_t>(bf16_bits(y1)) << 16);
             }
             *reinterpret_cast<uint2*>(orow + 8 * q4) = make_uint2(pk[0], pk[1]);
@@ -330,29 +354,49 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
     if (slot < 0 || slot >= a.num_slots) return;
     float* rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * F;
 
+    const int64_t base = static_cast<int64_t>(r) * a.ks.req + static_cast<int64_t>(h) * a.ks.head;
+    RowChunks<D, C::NT> kc, vc;
+    WChunks<D, FW, C::NT> wc;
+    kc.load(static_cast<const uint16_t*>(a.k) + base, a.ks.tok, B, tid);
+    vc.load(static_cast<const uint16_t*>(a.v) + base, a.ks.tok, B, tid);
+    wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 sv[C::NSL];
     load_state_slice(rec + wv * F * 32, lane, sv);
-
-    const int64_t base = static_cast<int64_t>(r) * a.ks.req + static_cast<int64_t>(h) * a.ks.head;
-    stage_rows<D, C::NT, C::RS>(Ks, static_cast<const uint16_t*>(a.k) + base, a.ks.tok, B, tid);
-    stage_vt<D, C::NT, C::VS>(Vt, static_cast<const uint16_t*>(a.v) + base, a.ks.tok, B, tid);
-    stage_w<D, FW, C::NT, C::RS>(Ws, static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
+    __builtin_amdgcn_sched_barrier(0);
+    kc.template store_rows<C::RS>(Ks, tid);
+    vc.template store_transposed<C::VS>(Vt, tid);
+    wc.template store_rows<C::RS>(Ws, tid);
     __syncthreads();
 
-    f32x16 ep[FW / 32], en[FW / 32];
-    feature_logits<D, FW, C::RS>(Ws, Ks, ln, g, ep);
-    hedgehog_softmax<FW>(ep, en);
+    // phi(k_t) for token ln, normalised, fp32
+    f32x16 u[FW / 32];
+    feature_logits<D, FW, C::RS>(Ws, Ks, ln, g, u);
+    float mx, mn;
+    logit_range<FW>(u, mx, mn);
+    float sp = 0.0f, sn = 0.0f;
+#pragma unroll
+    for (int T = 0; T < FW / 32; ++T)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            sp += __expf(u[T][v] - mx);
+            sn += __expf(mn - u[T][v]);
+        }
+    sp += __shfl_xor(sp, 32, 64);
+    sn += __shfl_xor(sn, 32, 64);
+    // padded tokens contribute zero
+    const float ip = ln < B ? 1.0f / sp : 0.0f;
+    const float in = ln < B ? 1.0f / sn : 0.0f;
     __syncthreads();  // every wave is done reading W before phi(K)^T overwrites it
 
-    // phi(k_t)^T into LDS as fp32 [f][t]; padded tokens contribute zero
-    const bool live = ln < B;
+    // phi(k_t)^T into LDS as fp32 [f][t]
 #pragma unroll
     for (int T = 0; T < FW / 32; ++T)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int fw = 32 * T + 8 * (v >> 2) + 4 * g + (v & 3);
-            Pt[fw * C::PS + ln] = live ? ep[T][v] : 0.0f;
-            Pt[(FW + fw) * C::PS + ln] = live ? en[T][v] : 0.0f;
+            Pt[fw * C::PS + ln] = __expf(u[T][v] - mx) * ip;
+            Pt[(FW + fw) * C::PS + ln] = __expf(mn - u[T][v]) * in;
         }
     __syncthreads();
 
