@@ -30,6 +30,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
 {
@@ -37,6 +38,33 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
 }
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane k supplies the 8-byte address of row k/4, columns 4(k%4) .. +3 of
+// a 4 x 16 block, and receives column k of that block's 4 rows.
+__device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p)
+{
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// A-operand fragment of V^T for the 32x32x16 product over tokens: lane
+// (n, g) = (lane % 32, lane / 32) gets V[j][c0 + n] for
+// j = 16 kb + 4 g + {0..3} and 16 kb + 8 + 4 g + {0..3}, from V stored
+// row-major (row stride RS elements) in LDS.
+template <int RS>
+__device__ __forceinline__ bf16x8 vt_frag(const uint16_t* Vs, int c0, int kb, int lane)
+{
+    const int m = lane & 15, q = lane >> 4, g = lane >> 5;
+    const int col = c0 + 16 * (q & 1) + 4 * (m & 3);
+    const int row = 16 * kb + 4 * g + (m >> 2);
+    const i16x4 lo = lds_read_tr(Vs + row * RS + col);
+    const i16x4 hi = lds_read_tr(Vs + (row + 8) * RS + col);
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
 
 template <int D, int FW>
 struct Cfg {
@@ -48,6 +76,10 @@ struct Cfg {
     static constexpr int PS = 32 + 4;       // padded LDS row (fp32) of phi(K)^T
     static constexpr int NSL = F / 8;       // 128-bit state loads per lane
     static constexpr int NKB = D / 16;      // k-steps over d
+    // resident work-groups per CU the persistent forward is built for: its
+    // register budget (state slice + one pair's working set) allows two,
+    // except with F = 256 whose state slice alone takes 128 registers
+    static constexpr int WPE = FW >= 128 ? 1 : 2;
 };
 
 // Issue the 128-bit loads of wave w's slice of the S tiles: load t gives lane
@@ -71,13 +103,18 @@ struct RowChunks {
     static constexpr int N = 32 * CH / NT;
     uint4 v[N];
 
-    __device__ __forceinline__ void load(const uint16_t* src, int64_t tok, int nrows, int tid)
+    // tok: token stride in elements; the launcher guarantees 32 * tok fits in
+    // 31 bits. Rows >= nrows read row nrows - 1 (always present) and are
+    // zeroed, so the loads need no divergent branches.
+    __device__ __forceinline__ void load(const uint16_t* src, int tok, int nrows, int tid)
     {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
-            v[i] = make_uint4(0u, 0u, 0u, 0u);
-            if (t < nrows) v[i] = *reinterpret_cast<const uint4*>(src + t * tok + ch * 8);
+            const int tr = t < nrows ? t : nrows - 1;
+            const uint4 x = *reinterpret_cast<const uint4*>(src + (tr * tok + ch * 8));
+            const bool keep = t < nrows;
+            v[i] = make_uint4(keep ? x.x : 0u, keep ? x.y : 0u, keep ? x.z : 0u, keep ? x.w : 0u);
         }
     }
     // row-major copy, row stride RS
@@ -170,127 +207,107 @@ __device__ __forceinline__ void logit_range(const f32x16 (&u)[FW / 32], float& m
 // Forward
 // ---------------------------------------------------------------------------
 template <int D, int FW>
-__global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(3, 3))) void forward_mfma_kernel(ForwardArgs a)
+struct alignas(16) FwdLds {
+    using C = Cfg<D, FW>;
+    uint16_t Qs[32 * C::RS];
+    uint16_t Ks[32 * C::RS];
+    uint16_t Ws[FW * C::RS];
+    uint16_t Vs[32 * C::RS];  // V rows, read transposed by ds_read_b64_tr_b16
+    float Zs[C::F];
+};
+
+// The per-pair operands a thread stages through LDS, held in registers from
+// their global loads to the LDS writes.
+template <int D, int FW>
+struct PairOperands {
+    using C = Cfg<D, FW>;
+    RowChunks<D, C::NT> q, k, v;
+    f32x4 z;
+    const float* rec;  // the pair's state record; nullptr for an out-of-range slot
+
+    __device__ __forceinline__ void load(const ForwardArgs& a, int p, int tid)
+    {
+        const int r = p / a.H, h = p % a.H;
+        const int slot = a.slot_ids[r];
+        rec = nullptr;
+        if (slot < 0 || slot >= a.num_slots) return;
+        rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * C::F;
+        const int64_t base = static_cast<int64_t>(r) * a.qs.req + static_cast<int64_t>(h) * a.qs.head;
+        const int tok = static_cast<int>(a.qs.tok);
+        q.load(static_cast<const uint16_t*>(a.q) + base, tok, a.B, tid);
+        k.load(static_cast<const uint16_t*>(a.k) + base, tok, a.B, tid);
+        v.load(static_cast<const uint16_t*>(a.v) + base, tok, a.B, tid);
+        z = reinterpret_cast<const f32x4*>(rec + D * C::F)[tid % (C::F / 4)];
+    }
+
+    __device__ __forceinline__ void store(FwdLds<D, FW>& sm, int tid) const
+    {
+        q.template store_rows<C::RS>(sm.Qs, tid);
+        k.template store_rows<C::RS>(sm.Ks, tid);
+        v.template store_rows<C::RS>(sm.Vs, tid);
+        if (tid < C::F / 4) reinterpret_cast<f32x4*>(sm.Zs)[tid] = z;
+    }
+};
+
+// One (request, head) pair once its operands are in LDS and this wave's slice
+// of the state is in sv: phi(q), the block softmax, P V, phi(q)^T S and the
+// merge, then the store of this wave's 32 output columns.
+// phi(q) for token ln as bf16 B operands of unnormalised exponentials
+// e+ = exp(u - max u) and e- = exp(min u - u); returns the two normalisers
+// sp, sn and den = phi(q)^T Z.
+template <int D, int FW>
+__device__ __forceinline__ void phi_operands(const FwdLds<D, FW>& sm, int ln, int g, bf16x8 (&pb)[Cfg<D, FW>::F / 16],
+                                             float& sp, float& sn, float& den)
 {
     using C = Cfg<D, FW>;
-    constexpr int F = C::F;
-    const int pair = blockIdx.x;
-    const int r = pair / a.H, h = pair % a.H;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int ln = lane & 31, g = lane >> 5;
-
-    __shared__ __attribute__((aligned(16))) uint16_t Qs[32 * C::RS];
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[32 * C::RS];
-    __shared__ __attribute__((aligned(16))) uint16_t Ws[FW * C::RS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * C::VS];
-    __shared__ __attribute__((aligned(16))) float Zs[F];
-
-    const int B = a.B;
-    uint16_t* out = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
-                    static_cast<int64_t>(h) * a.os.head;
-    const int slot = a.slot_ids[r];
-    if (slot < 0 || slot >= a.num_slots) {
-        for (int idx = tid; idx < B * D; idx += C::NT)
-            out[static_cast<int64_t>(idx / D) * a.os.tok + idx % D] = 0x7FC0u;  // NaN
-        return;
-    }
-    const float* rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * F;
-
-    // All global loads first, small operands before the state stream, so that
-    // waiting for the operands (the vector-memory counter retires in order)
-    // does not wait for the state.
-    const int64_t base = static_cast<int64_t>(r) * a.qs.req + static_cast<int64_t>(h) * a.qs.head;
-    RowChunks<D, C::NT> qc, kc, vc;
-    WChunks<D, FW, C::NT> wc;
-    qc.load(static_cast<const uint16_t*>(a.q) + base, a.qs.tok, B, tid);
-    kc.load(static_cast<const uint16_t*>(a.k) + base, a.qs.tok, B, tid);
-    vc.load(static_cast<const uint16_t*>(a.v) + base, a.qs.tok, B, tid);
-    wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
-    f32x4 zc = f32x4{};
-    if (tid < F / 4) zc = reinterpret_cast<const f32x4*>(rec + D * F)[tid];
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 sv[C::NSL];
-    load_state_slice(rec + wv * F * 32, lane, sv);
-    __builtin_amdgcn_sched_barrier(0);
-    qc.template store_rows<C::RS>(Qs, tid);
-    kc.template store_rows<C::RS>(Ks, tid);
-    vc.template store_transposed<C::VS>(Vt, tid);
-    wc.template store_rows<C::RS>(Ws, tid);
-    if (tid < F / 4) reinterpret_cast<f32x4*>(Zs)[tid] = zc;
-    __syncthreads();
-
-    // phi(q) for token ln as bf16 B operands of unnormalised exponentials,
-    // e+ = exp(u - max u) and e- = exp(min u - u); the two softmax
-    // normalisers sp, sn are applied after the contraction.
-    float sp = 0.0f, sn = 0.0f, den = 0.0f;
-    bf16x8 pb[F / 16];
-    {
-        f32x16 u[FW / 32];
-        feature_logits<D, FW, C::RS>(Ws, Qs, ln, g, u);
-        float mx, mn;
-        logit_range<FW>(u, mx, mn);
-        float dp = 0.0f, dn = 0.0f;
+    f32x16 u[FW / 32];
+    feature_logits<D, FW, C::RS>(sm.Ws, sm.Qs, ln, g, u);
+    constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
-        for (int T = 0; T < FW / 32; ++T)
+    for (int T = 0; T < FW / 32; ++T)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int fw = 32 * T + 8 * (v >> 2) + 4 * g + (v & 3);
-                const float ea = __expf(u[T][v] - mx);
-                const float eb = __expf(mn - u[T][v]);
+        for (int v = 0; v < 16; ++v) u[T][v] *= kLog2e;  // base-2 logits
+    float mx, mn;
+    logit_range<FW>(u, mx, mn);
+    float dp = 0.0f, dn = 0.0f;
+    sp = 0.0f;
+    sn = 0.0f;
+#pragma unroll
+    for (int T = 0; T < FW / 32; ++T)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int fw0 = 32 * T + 8 * q4 + 4 * g;
+            const f32x4 zp = *reinterpret_cast<const f32x4*>(sm.Zs + fw0);
+            const f32x4 zn = *reinterpret_cast<const f32x4*>(sm.Zs + FW + fw0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int v = 4 * q4 + e;
+                const float ea = __builtin_amdgcn_exp2f(u[T][v] - mx);
+                const float eb = __builtin_amdgcn_exp2f(mn - u[T][v]);
                 sp += ea;
                 sn += eb;
-                dp = fmaf(ea, Zs[fw], dp);
-                dn = fmaf(eb, Zs[FW + fw], dn);
+                dp = fmaf(ea, zp[e], dp);
+                dn = fmaf(eb, zn[e], dn);
                 pb[2 * T + (v >> 3)][v & 7] = static_cast<__bf16>(ea);
                 pb[FW / 16 + 2 * T + (v >> 3)][v & 7] = static_cast<__bf16>(eb);
             }
-        sp += __shfl_xor(sp, 32, 64);
-        sn += __shfl_xor(sn, 32, 64);
-        dp += __shfl_xor(dp, 32, 64);
-        dn += __shfl_xor(dn, 32, 64);
-        den = dp / sp + dn / sn;
-    }
-
-    // block logits s^T = K Q^T, masked beyond B, exponentials and row sums
-    float m = -INFINITY, l = 0.0f;
-    bf16x8 pp[2];
-    {
-        f32x16 sacc = f32x16{};
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-            sacc = mfma32(lds_frag(Ks + ln * C::RS + 16 * kb + 8 * g), lds_frag(Qs + ln * C::RS + 16 * kb + 8 * g), sacc);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int j = 8 * (v >> 2) + 4 * g + (v & 3);
-            const float s = j < B ? sacc[v] * a.scale : -INFINITY;
-            sacc[v] = s;
-            m = fmaxf(m, s);
         }
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float p = __expf(sacc[v] - m);
-            l += p;
-            pp[v >> 3][v & 7] = static_cast<__bf16>(p);
-        }
-        l += __shfl_xor(l, 32, 64);
-    }
+    sp += __shfl_xor(sp, 32, 64);
+    sn += __shfl_xor(sn, 32, 64);
+    dp += __shfl_xor(dp, 32, 64);
+    dn += __shfl_xor(dn, 32, 64);
+    den = dp / sp + dn / sn;
+}
 
-    // within-block numerator: sm^T = V^T P^T over this wave's 32 columns
-    f32x16 vacc = f32x16{};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const uint16_t* vr = Vt + (32 * wv + ln) * C::VS + 16 * kb + 4 * g;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
-        vacc = mfma32(__builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y)), pp[kb], vacc);
-    }
-
-    // linear read over this wave's 32 columns: lacc = sum_f e_f S_f with the
-    // + half rescaled by sn/sp, so that phi(q)^T S = lacc / sn
+// Linear read of this wave's 32 columns: sum_f e_f S_f with the + half
+// rescaled by sn/sp, so that phi(q)^T S = result / sn. Consumes the state slice.
+template <int D, int FW>
+__device__ __forceinline__ f32x16 linear_read(const f32x4 (&sv)[Cfg<D, FW>::NSL], const bf16x8 (&pb)[Cfg<D, FW>::F / 16],
+                                              float sp, float sn)
+{
     f32x16 lacc = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < F / 16; ++kb) {
+    for (int kb = 0; kb < Cfg<D, FW>::F / 16; ++kb) {
         if (kb == FW / 16) {
             const float rs = sn / sp;
 #pragma unroll
@@ -304,26 +321,137 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(3
         }
         lacc = mfma32(as, pb[kb], lacc);
     }
+    return lacc;
+}
 
-    // merge and store this wave's 32 columns of token ln
-    if (ln < B) {
-        float al, be;
-        merge_weights(a.gamma[h], m, al, be);
-        const float inv = 1.0f / (al * l + be * den);
-        const float bl = be / sn;
-        uint16_t* orow = out + static_cast<int64_t>(ln) * a.os.tok + 32 * wv + 4 * g;
+// Block logits s^T = K Q^T (masked beyond B), row maximum m, exponentials P
+// and row sum l for token ln, then this wave's 32 columns of P V.
+template <int D, int FW>
+__device__ __forceinline__ f32x16 block_softmax_pv(const ForwardArgs& a, const FwdLds<D, FW>& sm, int wv, int ln,
+                                                   int g, float& m, float& l)
+{
+    using C = Cfg<D, FW>;
+    bf16x8 pp[2];
+    {
+        f32x16 sacc = f32x16{};
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            uint32_t pk[2];
+        for (int kb = 0; kb < C::NKB; ++kb)
+            sacc = mfma32(lds_frag(sm.Ks + ln * C::RS + 16 * kb + 8 * g),
+                          lds_frag(sm.Qs + ln * C::RS + 16 * kb + 8 * g), sacc);
+        m = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int v0 = 4 * q4 + 2 * e;
-                const float y0 = (al * vacc[v0] + bl * lacc[v0]) * inv;
-                const float y1 = (al * vacc[v0 + 1] + bl * lacc[v0 + 1]) * inv;
-                pk[e] = static_cast<uint32_t>(bf16_bits(y0)) | (static_cast<uint32_t>(bf16_bits(y1)) << 16);
-            }
-            *reinterpret_cast<uint2*>(orow + 8 * q4) = make_uint2(pk[0], pk[1]);
+        for (int v = 0; v < 16; ++v) {
+            const int j = 8 * (v >> 2) + 4 * g + (v & 3);
+            const float s = j < a.B ? sacc[v] * a.scale : -INFINITY;
+            sacc[v] = s;
+            m = fmaxf(m, s);
         }
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        l = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float p = __expf(sacc[v] - m);
+            l += p;
+            pp[v >> 3][v & 7] = static_cast<__bf16>(p);
+        }
+        l += __shfl_xor(l, 32, 64);
+    }
+    f32x16 vacc = f32x16{};
+    const int lane = 32 * g + ln;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) vacc = mfma32(vt_frag<C::RS>(sm.Vs, 32 * wv, kb, lane), pp[kb], vacc);
+    return vacc;
+}
+
+// Merge of the two branches for token ln and store of this wave's 32 columns.
+__device__ __forceinline__ void merge_store(const ForwardArgs& a, const f32x16& vacc, const f32x16& lacc, float gamma,
+                                            float m, float l, float den, float sn, int r, int h, int wv, int ln, int g)
+{
+    if (ln >= a.B) return;
+    float al, be;
+    merge_weights(gamma, m, al, be);
+    const float inv = __builtin_amdgcn_rcpf(al * l + be * den);
+    const float bl = be * __builtin_amdgcn_rcpf(sn);
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
+                     static_cast<int64_t>(h) * a.os.head + (ln * static_cast<int>(a.os.tok) + 32 * wv + 4 * g);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        uint32_t pk[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int v0 = 4 * q4 + 2 * e;
+            const float y0 = (al * vacc[v0] + bl * lacc[v0]) * inv;
+            const float y1 = (al * vacc[v0 + 1] + bl * lacc[v0 + 1]) * inv;
+            pk[e] = static_cast<uint32_t>(bf16_bits(y0)) | (static_cast<uint32_t>(bf16_bits(y1)) << 16);
+        }
+        *reinterpret_cast<uint2*>(orow + 8 * q4) = make_uint2(pk[0], pk[1]);
+    }
+}
+
+// Persistent forward: WPE work-groups per compute unit, and work-group b
+// takes pairs b, b + G, b + 2G, ... (G = gridDim.x, a multiple of H, so every
+// pair of a work-group has the same head: W_h and the gate are loaded once).
+// Per pair: the operands arrive in LDS, then phi(q), the block softmax and P V
+// run while this wave's state slice streams in; the linear read consumes the
+// slice, the next pair's slice is issued at once, and the merge and stores
+// follow. The next pair's Q, K, V, Z loads are issued right after the current
+// ones reach LDS. The vector memory counter retires in issue order, so every
+// wait only covers loads issued before the ones still streaming.
+template <int D, int FW>
+__global__ __launch_bounds__(64 * (D / 32))
+__attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forward_mfma_kernel(ForwardArgs a, int npairs)
+{
+    using C = Cfg<D, FW>;
+    constexpr int F = C::F;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int ln = lane & 31, g = lane >> 5;
+    const int G = gridDim.x;
+    int p = blockIdx.x;
+    if (p >= npairs) return;
+    const int h = p % a.H;
+    const float gamma = a.gamma[h];
+
+    __shared__ FwdLds<D, FW> sm;
+    {
+        WChunks<D, FW, C::NT> wc;
+        wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
+        wc.template store_rows<C::RS>(sm.Ws, tid);
+    }
+
+    PairOperands<D, FW> op;
+    f32x4 sv[C::NSL];
+    op.load(a, p, tid);
+    if (op.rec) load_state_slice(op.rec + wv * F * 32, lane, sv);
+    for (;;) {
+        const int pn = p + G;
+        const bool more = pn < npairs;
+        const bool valid = op.rec != nullptr;
+        const int r = p / a.H;
+        __syncthreads();  // every wave is done with the previous pair's LDS operands
+        if (valid) op.store(sm, tid);
+        __syncthreads();
+        if (more) op.load(a, pn, tid);
+        f32x16 lacc, vacc;
+        float sp, sn, den, m, l;
+        if (valid) {
+            bf16x8 pb[F / 16];
+            phi_operands<D, FW>(sm, ln, g, pb, sp, sn, den);
+            vacc = block_softmax_pv<D, FW>(a, sm, wv, ln, g, m, l);
+            lacc = linear_read<D, FW>(sv, pb, sp, sn);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (more && op.rec) load_state_slice(op.rec + wv * F * 32, lane, sv);
+        __builtin_amdgcn_sched_barrier(0);
+        if (valid) {
+            merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, ln, g);
+        } else {
+            uint16_t* out = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
+                            static_cast<int64_t>(h) * a.os.head;
+            for (int idx = tid; idx < a.B * D; idx += C::NT)
+                out[static_cast<int64_t>(idx / D) * a.os.tok + idx % D] = 0x7FC0u;  // NaN
+        }
+        if (!more) break;
+        p = pn;
     }
 }
 
@@ -357,8 +485,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
     const int64_t base = static_cast<int64_t>(r) * a.ks.req + static_cast<int64_t>(h) * a.ks.head;
     RowChunks<D, C::NT> kc, vc;
     WChunks<D, FW, C::NT> wc;
-    kc.load(static_cast<const uint16_t*>(a.k) + base, a.ks.tok, B, tid);
-    vc.load(static_cast<const uint16_t*>(a.v) + base, a.ks.tok, B, tid);
+    kc.load(static_cast<const uint16_t*>(a.k) + base, static_cast<int>(a.ks.tok), B, tid);
+    vc.load(static_cast<const uint16_t*>(a.v) + base, static_cast<int>(a.ks.tok), B, tid);
     wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
     __builtin_amdgcn_sched_barrier(0);
     f32x4 sv[C::NSL];
@@ -433,17 +561,45 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
     }
 }
 
+// Compute units of the current device (cached per device ordinal).
+static int compute_units()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Persistent grid: as many work-groups as can be resident (WPE per CU),
+// rounded down to a multiple of H so that each keeps one head, and no more
+// than there are pairs.
+template <int D, int FW>
+static hipError_t launch_forward(const ForwardArgs& a, hipStream_t s)
+{
+    const int npairs = a.R * a.H;
+    int64_t G = static_cast<int64_t>(compute_units()) * Cfg<D, FW>::WPE;
+    G = (G / a.H) * a.H;
+    if (G < a.H) G = a.H;
+    if (G > npairs) G = npairs;
+    hipLaunchKernelGGL((forward_mfma_kernel<D, FW>), dim3(static_cast<uint32_t>(G)), dim3(64 * (D / 32)), 0, s, a,
+                       npairs);
+    return hipGetLastError();
+}
+
 template <int D>
 static hipError_t forward_by_fw(const ForwardArgs& a, hipStream_t s)
 {
-    const dim3 grid(static_cast<uint32_t>(a.R * a.H)), block(64 * (D / 32));
     switch (a.FW) {
-        case 32: hipLaunchKernelGGL((forward_mfma_kernel<D, 32>), grid, block, 0, s, a); break;
-        case 64: hipLaunchKernelGGL((forward_mfma_kernel<D, 64>), grid, block, 0, s, a); break;
-        case 128: hipLaunchKernelGGL((forward_mfma_kernel<D, 128>), grid, block, 0, s, a); break;
+        case 32: return launch_forward<D, 32>(a, s);
+        case 64: return launch_forward<D, 64>(a, s);
+        case 128: return launch_forward<D, 128>(a, s);
         default: return hipErrorNotSupported;
     }
-    return hipGetLastError();
 }
 
 template <int D>
@@ -461,9 +617,13 @@ static hipError_t commit_by_fw(const CommitArgs& a, hipStream_t s)
 
 }  // namespace
 
+// The matrix-core kernels address a block's rows with 32-bit offsets.
+static bool small_token_stride(int64_t tok) { return tok >= 0 && tok < (int64_t(1) << 25); }
+
 hipError_t launch_forward_mfma(const ForwardArgs& a, hipStream_t s)
 {
     if (a.io != BHA_BF16 || a.B > 32) return hipErrorNotSupported;
+    if (!small_token_stride(a.qs.tok) || !small_token_stride(a.os.tok)) return hipErrorNotSupported;
     if (a.d == 128) return forward_by_fw<128>(a, s);
     if (a.d == 64) return forward_by_fw<64>(a, s);
     return hipErrorNotSupported;
@@ -472,6 +632,7 @@ hipError_t launch_forward_mfma(const ForwardArgs& a, hipStream_t s)
 hipError_t launch_commit_mfma(const CommitArgs& a, hipStream_t s)
 {
     if (a.io != BHA_BF16 || a.B > 32) return hipErrorNotSupported;
+    if (!small_token_stride(a.ks.tok)) return hipErrorNotSupported;
     if (a.d == 128) return commit_by_fw<128>(a, s);
     if (a.d == 64) return commit_by_fw<64>(a, s);
     return hipErrorNotSupported;
