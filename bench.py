@@ -249,6 +249,20 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"copy calibration: 3 x {args.copy_calibration_mib} MiB device copies")
 
+    # context: a plain device-to-device copy of the forward's byte count (read + write)
+    ctx_src = torch.empty(fb // 4, dtype=torch.float32, device=dev)
+    ctx_dst = torch.empty_like(ctx_src)
+    ctx_dst.copy_(ctx_src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        ctx_dst.copy_(ctx_src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * ctx_src.numel() * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del ctx_src, ctx_dst
+    log(f"context: torch device copy of {fb / 1e6:.0f} MB runs at {copy_gbps:.0f} GB/s (read + write)")
+
     achieved = fb / fwd_avg / 1e9
     result = {
         "metric": METRIC,
@@ -278,11 +292,11 @@ def main() -> int:
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": read_traffic(args.config),
-            "kernel": "bha_block_forward (forward_mfma_kernel<128,64>)" if (d, FW) == (128, 64)
-            else "bha_block_forward",
+            "kernel": f"bha_block_forward: forward_mfma_kernel<{d},{FW}> (persistent, bf16 MFMA)",
             "bytes_per_launch": fb,
             "avg_launch_us": fwd_avg * 1e6,
         },
+        "context": {"torch_copy_GBps": copy_gbps},
         "commit": {
             "avg_launch_us": com_avg * 1e6,
             "bytes_per_launch": cb,
