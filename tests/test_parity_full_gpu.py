@@ -1,0 +1,111 @@
+"""GPU parity at full workload sizes, on sampled (request, head) pairs.
+
+The batch is the one bench.py times: every request's state is built on the GPU
+by chained commits of its whole prefix (drawn on the device), then one forward
+of the whole batch and one commit run in the same launch configuration. The
+oracle then checks, one pair at a time:
+  * sampled forward outputs, from the same fp32 state bytes the kernel read;
+  * the commit on sampled pairs, from the same pre-commit state;
+  * the chained GPU state of the shortest and longest requests against the
+    oracle's state built from scratch over their whole prefix.
+Bars: normwise 2e-2 (bf16 I/O, fp32 accumulation and state).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_block_amd as bha
+import oracle
+import synth
+from helpers import normwise_err, record_to_plain, to_host
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = min(16, os.cpu_count() or 1)
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU visible")
+    bha.load_library()
+    return torch.device("cuda:0")
+
+
+def _run_full(name, dev, n_pairs=24, seed=0):
+    case = synth.make_case(name, with_prefix=False, with_qkv=False)
+    R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B
+    F = 2 * FW
+    print(f"[{name}] R={R} H={H} d={d} FW={FW} B={B} prefix blocks {case.n_blocks.min()}..{case.n_blocks.max()}",
+          flush=True)
+    slots = torch.from_numpy(case.slot_ids).to(dev)
+    w, gamma = synth.device_layer_params(name, 0, dev)
+    state = bha.new_state(case.num_slots, H, d, FW, dev)
+    track = sorted({int(np.argmin(case.n_blocks)), int(np.argmax(case.n_blocks))})
+    kept = {r: ([], []) for r in track}
+    for i in range(int(case.n_blocks.max())):
+        act = np.nonzero(case.n_blocks > i)[0]
+        kb, vb = synth.device_blocks(name, i, len(act), dev, layer=0)
+        bha.state_commit(kb, vb, w, state, torch.from_numpy(case.slot_ids[act]).to(dev))
+        for r in track:
+            if case.n_blocks[r] > i:
+                j = int(np.searchsorted(act, r))
+                kept[r][0].append(kb[j].float().cpu().numpy())
+                kept[r][1].append(vb[j].float().cpu().numpy())
+    q, k, v = synth.device_step_qkv(name, 0, R, dev, layer=0)
+    out = bha.block_forward(q, k, v, w, gamma, state, slots)
+    torch.cuda.synchronize()
+    pre = state[torch.from_numpy(case.slot_ids.astype(np.int64)).to(dev)].cpu().numpy()  # [R][H][rec]
+    bha.state_commit(k, v, w, state, slots)
+    torch.cuda.synchronize()
+    post = state[torch.from_numpy(case.slot_ids.astype(np.int64)).to(dev)].cpu().numpy()
+
+    w64 = w.float().cpu().numpy().astype(np.float64)
+    g64 = gamma.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(seed)
+    rs = rng.integers(0, R, size=n_pairs)
+    hs = rng.integers(0, H, size=n_pairs)
+    qh, kh, vh, oh = (to_host(t) for t in (q, k, v, out))
+    err_f = err_c = 0.0
+    for r, h in zip(rs, hs):
+        S, Z = record_to_plain(pre[r, h], d, F)
+        ref = oracle.block_forward(qh[r, :, h], kh[r, :, h], vh[r, :, h], w64[h], g64[h], S, Z)
+        err_f = max(err_f, normwise_err(oh[r, :, h], ref, None))
+        S2, Z2 = S.copy(), Z.copy()
+        oracle.state_commit(S2, Z2, kh[r, :, h], vh[r, :, h], w64[h])
+        Sg, Zg = record_to_plain(post[r, h], d, F)
+        err_c = max(err_c, normwise_err(Sg, S2, None), normwise_err(Zg, Z2, None))
+    print(f"[{name}] forward err {err_f:.2e}, commit err {err_c:.2e} over {n_pairs} sampled pairs", flush=True)
+    assert err_f <= TOL and err_c <= TOL
+
+    for r in track:
+        kp = np.concatenate(kept[r][0]).astype(np.float64)  # [N][H][d]
+        vp = np.concatenate(kept[r][1]).astype(np.float64)
+        S_ref = np.zeros((1, H, F, d))
+        Z_ref = np.zeros((1, H, F))
+        oracle.state_commit_batch(S_ref, Z_ref, np.ascontiguousarray(kp.transpose(1, 0, 2))[None],
+                                  np.ascontiguousarray(vp.transpose(1, 0, 2))[None], w64, nthreads=NTHREADS)
+        Sg, Zg = record_to_plain(pre[r], d, F)
+        e_s = normwise_err(Sg, S_ref[0], (1, 2))
+        e_z = normwise_err(Zg, Z_ref[0], (1,))
+        print(f"[{name}] chained state of request {r} ({kp.shape[0]} prefix tokens): S err {e_s:.2e}, "
+              f"Z err {e_z:.2e}", flush=True)
+        assert e_s <= TOL and e_z <= TOL
+
+
+def test_decode256_full_size(dev):
+    # 256 requests x 16 heads, d=128, FW=64, B=32, ragged prefixes 256..8,192 tokens
+    _run_full("decode256", dev)
+
+
+def test_long_context_32k_full_size(dev):
+    # 64 requests x 16 heads with 32,768-token prefixes
+    _run_full("longctx32k", dev, n_pairs=16)
+
+
+def test_wide2048_full_size(dev):
+    # 2,048 requests x 16 heads, FW=128 (F=256), prefixes 512..4,096 tokens
+    _run_full("wide2048", dev, n_pairs=16)
