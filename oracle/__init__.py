@@ -14,6 +14,9 @@ passes numpy arrays. Layouts (all C-contiguous float64):
 * ``state_build(k, v, w)`` -> (S [2FW][d], Z [2FW]).
 * ``state_commit(S, Z, k, v, w)`` updates S, Z in place.
 * ``block_forward(q, k, v, w, gamma, S, Z, scale)`` -> out [B][d].
+* ``prefix_attention(q, k, v, kp, vp, scale)``: softmax attention of the
+  block's queries over the whole prefix plus the block (the path the method
+  replaces) -> out [B][d].
 * batched variants over (request, head) pairs with plain pair-major layouts
   q/k/v/out [R][H][B][d], w [H][FW][d], gamma [H], S [R][H][2FW][d], Z [R][H][2FW].
 """
@@ -56,6 +59,8 @@ def _load():
         lib.bha_ref_block_forward.argtypes = [I, I, I, P, P, P, P, D, D, P, P, P]
         lib.bha_ref_block_forward_batch.argtypes = [I, I, I, I, I, P, P, P, P, P, D, P, P, P, I]
         lib.bha_ref_state_commit_batch.argtypes = [I, I, I, I, I, P, P, P, P, P, I]
+        lib.bha_ref_prefix_attention.argtypes = [I, I, I, P, P, P, P, P, D, P]
+        lib.bha_ref_prefix_attention.restype = None
         for f in (lib.bha_ref_feature_map, lib.bha_ref_state_commit, lib.bha_ref_state_build,
                   lib.bha_ref_block_forward, lib.bha_ref_block_forward_batch,
                   lib.bha_ref_state_commit_batch):
@@ -124,6 +129,21 @@ def block_forward(q, k, v, w, gamma, S, Z, scale=0.0):
     out = np.empty((B, d), dtype=np.float64)
     _load().bha_ref_block_forward(B, d, fw, _p(q), _p(k), _p(v), _p(w), float(gamma),
                                   float(scale), _p(S), _p(Z), _p(out))
+    return out
+
+
+def prefix_attention(q, k, v, kp, vp, scale=0.0):
+    """Softmax attention of the block's queries over prefix + block keys:
+    q, k, v [B][d], kp, vp [N][d] -> out [B][d]."""
+    q = _f64(q, name="q")
+    B, d = q.shape
+    k = _f64(k, (B, d), "k")
+    v = _f64(v, (B, d), "v")
+    kp = _f64(kp, name="kp").reshape(-1, d)
+    vp = _f64(vp, (kp.shape[0], d), "vp")
+    out = np.empty((B, d), dtype=np.float64)
+    _load().bha_ref_prefix_attention(B, kp.shape[0], d, _p(q), _p(k), _p(v), _p(kp), _p(vp),
+                                     float(scale), _p(out))
     return out
 
 

@@ -12,6 +12,8 @@
  *         section "Methodology: Block-Hybrid Attention", list "Architecture
  *         Design" (within-block softmax, cross-block Hedgehog linear
  *         attention, the S_n / Z_n states, the shared-normaliser merge).
+ *   [ML]  mlsanity.com index of the paper, "Abstract (arXiv)" (the cost the
+ *         method removes: every denoising step attends to all previous blocks).
  *   [PR]  pith.science review of the paper, "The reading", paragraph "What
  *         carries the argument" (the formulas for phi, S_n and Z_n; the per
  *         query O(F d) read), and "Circularity Check" (state sizes).
@@ -160,6 +162,46 @@ void bha_ref_block_forward(int B, int d, int fw, const double* q, const double* 
     }
     free(lin);
     free(ph);
+    free(s);
+}
+
+/* ---------------------------------------------------------------------------
+ * Softmax attention over the whole prefix, the path block-hybrid attention
+ * replaces ([ML] abstract and [GS] Problem Statement: with KV caching, every
+ * denoising step of the active block still attends to all previous blocks).
+ * Each query of the block attends with one softmax to the np prefix tokens
+ * (kp, vp: [np][d]) and to the B keys of the block itself (no mask):
+ *   y_i = sum_t e^{c q_i.k_t} v_t / sum_t e^{c q_i.k_t}  over t in prefix + block.
+ * The row maximum is subtracted before exponentiating (the value is the same).
+ * q, k, v, out: [B][d].
+ * ------------------------------------------------------------------------- */
+void bha_ref_prefix_attention(int B, int np, int d, const double* q, const double* k, const double* v,
+                              const double* kp, const double* vp, double scale, double* out)
+{
+    const double c = (scale > 0.0) ? scale : 1.0 / sqrt((double)d);
+    const int nk = np + B;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(nk > 0 ? nk : 1));
+    for (int i = 0; i < B; ++i) {
+        const double* qi = q + (size_t)i * d;
+        for (int t = 0; t < nk; ++t) {
+            const double* kt = t < np ? kp + (size_t)t * d : k + (size_t)(t - np) * d;
+            double acc = 0.0;
+            for (int e = 0; e < d; ++e) acc += qi[e] * kt[e];
+            s[t] = c * acc;
+        }
+        double m = s[0];
+        for (int t = 1; t < nk; ++t) if (s[t] > m) m = s[t];
+        double den = 0.0;
+        for (int t = 0; t < nk; ++t) den += exp(s[t] - m);
+        for (int e = 0; e < d; ++e) {
+            double num = 0.0;
+            for (int t = 0; t < nk; ++t) {
+                const double* vt = t < np ? vp + (size_t)t * d : v + (size_t)(t - np) * d;
+                num += exp(s[t] - m) * vt[e];
+            }
+            out[(size_t)i * d + e] = num / den;
+        }
+    }
     free(s);
 }
 

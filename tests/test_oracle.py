@@ -331,3 +331,39 @@ def test_batched_commit_matches_pairs():
             oracle.state_commit(s1, z1, k[r, h], v[r, h], w[h])
             np.testing.assert_array_equal(S[r, h], s1)
             np.testing.assert_array_equal(Z[r, h], z1)
+
+
+# ---------------------------------------------------------------- softmax prefix attention
+@pytest.mark.parametrize("d,b,n", [(8, 4, 0), (8, 4, 13), (16, 1, 5), (6, 7, 40)])
+def test_prefix_attention_is_softmax_attention_over_prefix_and_block(d, b, n):
+    # one softmax over the prefix keys followed by the block's keys, no mask:
+    # PyTorch's CPU attention on the concatenated keys and values
+    rng = _rng(30)
+    q, k, v = (rng.standard_normal((b, d)) for _ in range(3))
+    kp, vp = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    y = oracle.prefix_attention(q, k, v, kp, vp)
+    ref = _sdpa(q, np.concatenate([kp, k]), np.concatenate([vp, v]))
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_prefix_attention_is_order_invariant_over_prefix():
+    rng = _rng(31)
+    q, k, v = (rng.standard_normal((3, 8)) for _ in range(3))
+    kp, vp = rng.standard_normal((9, 8)), rng.standard_normal((9, 8))
+    p = rng.permutation(9)
+    np.testing.assert_allclose(oracle.prefix_attention(q, k, v, kp[p], vp[p]),
+                               oracle.prefix_attention(q, k, v, kp, vp), rtol=1e-12, atol=1e-14)
+
+
+def test_prefix_attention_explicit_scale_and_constant_values():
+    rng = _rng(32)
+    q, k = rng.standard_normal((4, 8)), rng.standard_normal((4, 8))
+    kp = rng.standard_normal((6, 8))
+    cval = rng.standard_normal(8)
+    y = oracle.prefix_attention(q, k, np.tile(cval, (4, 1)), kp, np.tile(cval, (6, 1)), scale=0.25)
+    np.testing.assert_allclose(y, np.tile(cval, (4, 1)), rtol=1e-12, atol=1e-13)
+    kp2, vp2 = rng.standard_normal((6, 8)), rng.standard_normal((6, 8))
+    v = rng.standard_normal((4, 8))
+    y2 = oracle.prefix_attention(q, k, v, kp2, vp2, scale=0.25)
+    np.testing.assert_allclose(y2, _sdpa(q, np.concatenate([kp2, k]), np.concatenate([vp2, v]), scale=0.25),
+                               rtol=1e-12, atol=1e-13)
