@@ -146,6 +146,26 @@ int bha_state_commit(const bha_dims* dims, const void* k, const void* v, const b
                      const void* w, int64_t w_head_stride, float* state, int32_t num_slots,
                      const int32_t* slot_ids, hipStream_t stream);
 
+/*
+ * bha_state_prefill -- fold a whole run of tokens per request into its state
+ * in one launch: a prompt of any length, or several finished blocks at once.
+ * For request r the tokens are rows seq_offsets[r] .. seq_offsets[r+1]-1 of
+ * packed k and v, and S += sum_t phi(k_t) v_t^T, Z += sum_t phi(k_t) over
+ * them -- the same sums a commit takes per block (gist.science "Architecture
+ * Design", state-compression bullet; pith.science "What carries the
+ * argument"), taken over all of them at once.
+ *   k, v        : element (t, h, c) at t*kv->tok + h*kv->head + c for
+ *                 t < total_tokens (kv->req is not used).
+ *   seq_offsets : int32 [R + 1] device; clamped on the device to
+ *                 0 <= seq_offsets[r] <= seq_offsets[r+1] <= total_tokens.
+ *   dims->block_size must be a supported value but is not used.
+ * Slot ids must be distinct (duplicates race). total_tokens == 0 is a no-op.
+ */
+int bha_state_prefill(const bha_dims* dims, const void* k, const void* v, const bha_strides* kv,
+                      const int32_t* seq_offsets, int64_t total_tokens, const void* w,
+                      int64_t w_head_stride, float* state, int32_t num_slots,
+                      const int32_t* slot_ids, hipStream_t stream);
+
 /* Floats in one (slot, head) state record: (d + 1) * 2 * FW. Returns -1 for
  * unsupported sizes. Host only; touches no device. */
 int64_t bha_state_record_floats(int32_t head_dim, int32_t feat_half);

@@ -28,7 +28,7 @@ import torch
 __all__ = [
     "BhaError", "library_path", "load_library", "version", "status_string",
     "state_record_floats", "new_state", "feature_map", "block_forward", "state_commit",
-    "prepare_forward", "prepare_commit",
+    "prepare_forward", "prepare_commit", "state_prefill",
     "BHA_F32", "BHA_BF16",
 ]
 
@@ -41,7 +41,7 @@ BHA_BF16 = 1
 
 # Every symbol include/bha.h declares.
 EXPORTED_SYMBOLS = (
-    "bha_feature_map", "bha_block_forward", "bha_state_commit",
+    "bha_feature_map", "bha_block_forward", "bha_state_commit", "bha_state_prefill",
     "bha_state_record_floats", "bha_status_string", "bha_version",
 )
 
@@ -89,6 +89,8 @@ def load_library():
     lib.bha_feature_map.argtypes = [PD, P, PS, P, I64, P, P]
     lib.bha_block_forward.argtypes = [PD, P, P, P, PS, P, I64, P, P, I32, P, P, PS, P]
     lib.bha_state_commit.argtypes = [PD, P, P, PS, P, I64, P, I32, P, P]
+    lib.bha_state_prefill.argtypes = [PD, P, P, PS, P, I64, P, I64, P, I32, P, P]
+    lib.bha_state_prefill.restype = ctypes.c_int
     lib.bha_state_record_floats.argtypes = [I32, I32]
     lib.bha_state_record_floats.restype = I64
     lib.bha_status_string.argtypes = [ctypes.c_int]
@@ -258,6 +260,36 @@ def state_commit(k, v, w, state, slot_ids, *, stream=None) -> None:
     st = lib.bha_state_commit(*args)
     if st != 0:
         raise BhaError("bha_state_commit", st)
+
+
+def state_prefill(k, v, seq_offsets, w, state, slot_ids, *, stream=None) -> None:
+    """Fold each request's packed token range into its state records (in place).
+
+    k, v: [T][H][d] packed tokens (last dimension contiguous); seq_offsets:
+    int32 [R + 1] on the device, request r owning rows seq_offsets[r] ..
+    seq_offsets[r+1]-1; slot_ids: int32 [R], distinct."""
+    lib = load_library()
+    if k.dim() != 3 or v.shape != k.shape or k.stride(2) != 1 or v.stride(2) != 1:
+        raise ValueError("k and v must be [T][H][d] with a contiguous last dimension")
+    if (v.stride(0), v.stride(1)) != (k.stride(0), k.stride(1)):
+        raise ValueError("v must have the strides of k")
+    if v.dtype != k.dtype or w.dtype != k.dtype:
+        raise TypeError("k, v and w must share one dtype")
+    T, H, d = k.shape
+    fw, wh = _w_stride(w, H, d)
+    num_slots = _num_slots(state, H, d, fw)
+    R = slot_ids.numel()
+    if slot_ids.dtype != torch.int32 or not slot_ids.is_contiguous():
+        raise ValueError("slot_ids must be a contiguous int32 tensor")
+    if seq_offsets.dtype != torch.int32 or seq_offsets.numel() != R + 1 or not seq_offsets.is_contiguous():
+        raise ValueError("seq_offsets must be a contiguous int32 [R + 1] tensor")
+    _check_device(k.device, v, w, state, slot_ids, seq_offsets)
+    dims = bha_dims(R, H, d, fw, 1, _io_dtype(k), 0.0)
+    ks = bha_strides(0, k.stride(0), k.stride(1))
+    st = lib.bha_state_prefill(ctypes.byref(dims), _ptr(k), _ptr(v), ctypes.byref(ks), _ptr(seq_offsets), T,
+                               _ptr(w), wh, _ptr(state), num_slots, _ptr(slot_ids), _stream(k.device, stream))
+    if st != 0:
+        raise BhaError("bha_state_prefill", st)
 
 
 class _Prepared:

@@ -1,6 +1,7 @@
 // C-ABI entry points of libbha.so: validate on the host, then enqueue the
 // kernels on the caller's stream. The interface contract is in include/bha.h.
 #include <math.h>
+#include <stdint.h>
 
 #include "bha_internal.hpp"
 
@@ -77,7 +78,42 @@ extern "C" int bha_state_commit(const bha_dims* dims, const void* k, const void*
     a.FW = dims->feat_half; a.B = dims->block_size; a.io = dims->io_dtype;
     a.k = k; a.v = v; a.ks = *kv; a.w = w; a.wh = w_head_stride;
     a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids;
+    a.seq_offsets = nullptr; a.total_tokens = 0;
     hipError_t e = launch_commit_mfma(a, stream);
+    if (e == hipErrorNotSupported) e = launch_commit_generic(a, stream);
+    return launch_status(e);
+}
+
+extern "C" int bha_state_prefill(const bha_dims* dims, const void* k, const void* v, const bha_strides* kv,
+                                 const int32_t* seq_offsets, int64_t total_tokens, const void* w,
+                                 int64_t w_head_stride, float* state, int32_t num_slots,
+                                 const int32_t* slot_ids, hipStream_t stream)
+{
+    int st = validate_dims(dims);
+    if (st != BHA_OK) return st;
+    if (dims->num_requests == 0) return BHA_OK;
+    if (total_tokens < 0) return BHA_ERR_DIMS;
+    if (!seq_offsets || !kv) return BHA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(seq_offsets) % 4 != 0) return BHA_ERR_ALIGN;
+    if (total_tokens == 0) return BHA_OK;
+    // the packed tokens, checked as one "request" of total_tokens rows
+    bha_dims packed = *dims;
+    packed.num_requests = 1;
+    if (total_tokens > INT32_MAX) return BHA_ERR_DIMS;
+    packed.block_size = static_cast<int32_t>(total_tokens);
+    bha_strides ps = *kv;
+    ps.req = 0;
+    if ((st = validate_tokens(k, &ps, &packed, false)) != BHA_OK) return st;
+    if ((st = validate_tokens(v, &ps, &packed, false)) != BHA_OK) return st;
+    if ((st = validate_w(w, w_head_stride, dims)) != BHA_OK) return st;
+    if ((st = validate_state(state, num_slots, slot_ids, dims)) != BHA_OK) return st;
+    CommitArgs a;
+    a.R = dims->num_requests; a.H = dims->num_heads; a.d = dims->head_dim;
+    a.FW = dims->feat_half; a.B = dims->block_size; a.io = dims->io_dtype;
+    a.k = k; a.v = v; a.ks = ps; a.w = w; a.wh = w_head_stride;
+    a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids;
+    a.seq_offsets = seq_offsets; a.total_tokens = total_tokens;
+    hipError_t e = launch_prefill_mfma(a, stream);
     if (e == hipErrorNotSupported) e = launch_commit_generic(a, stream);
     return launch_status(e);
 }

@@ -34,7 +34,27 @@ struct CommitArgs {
     float* state;
     int num_slots;
     const int32_t* slot_ids;
+    // prefill: request r's tokens are packed rows seq_offsets[r] .. seq_offsets[r+1]-1
+    // (of total_tokens); nullptr for a commit of B tokens per request
+    const int32_t* seq_offsets;
+    int64_t total_tokens;
 };
+
+// Token range of request r in a commit or prefill, clamped as documented.
+__device__ __forceinline__ void commit_rows(const CommitArgs& a, int r, int64_t& first_row, int& n)
+{
+    if (a.seq_offsets == nullptr) {
+        first_row = -1;  // rows r*req + t*tok
+        n = a.B;
+        return;
+    }
+    int64_t s0 = a.seq_offsets[r], s1 = a.seq_offsets[r + 1];
+    s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);
+    s1 = s1 < s0 ? s0 : (s1 > a.total_tokens ? a.total_tokens : s1);
+    first_row = s0;
+    const int64_t len = s1 - s0;
+    n = len > 0x7fffffff ? 0x7fffffff : static_cast<int>(len);
+}
 
 struct PhiArgs {
     int R, H, d, FW, B, io;
@@ -54,6 +74,7 @@ hipError_t launch_feature_map_generic(const PhiArgs& a, hipStream_t s);
 // (without launching) for sizes they do not cover.
 hipError_t launch_forward_mfma(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_commit_mfma(const CommitArgs& a, hipStream_t s);
+hipError_t launch_prefill_mfma(const CommitArgs& a, hipStream_t s);
 
 // Host-side argument checks (no HIP calls); see bha_validate.cpp.
 int validate_dims(const bha_dims* d);

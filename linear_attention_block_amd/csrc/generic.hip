@@ -114,8 +114,9 @@ __global__ __launch_bounds__(kThreads) void forward_generic_kernel(ForwardArgs a
 }
 
 // ---------------------------------------------------------------------------
-// Commit: one work-group per (request, head, 32-column slice cs of S). Tokens
-// are taken 16 at a time: phi(k_t) for the chunk into LDS, then each thread
+// Commit and prefill: one work-group per (request, head, 32-column slice cs of
+// S), over the request's B block tokens (commit) or its packed token range
+// (prefill). Tokens are taken 16 at a time: phi(k_t) for the chunk into LDS, then each thread
 // accumulates its (f, c) entries of sum_t phi(k_t) v_t^T. The slice cs == 0
 // work-group also folds sum_t phi(k_t) into Z. Finally a read-modify-write.
 // ---------------------------------------------------------------------------
@@ -142,7 +143,11 @@ __global__ __launch_bounds__(kThreads) void commit_generic_kernel(CommitArgs a)
     const int slot = a.slot_ids[r];
     if (slot < 0 || slot >= a.num_slots) return;
     float* rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(a.d + 1) * F;
-    const int64_t base = r * a.ks.req + static_cast<int64_t>(h) * a.ks.head;
+    int64_t first_row;
+    int n;
+    commit_rows(a, static_cast<int>(r), first_row, n);
+    if (n == 0) return;
+    const int64_t base = (first_row < 0 ? r * a.ks.req : first_row * a.ks.tok) + static_cast<int64_t>(h) * a.ks.head;
     const T* kb = static_cast<const T*>(a.k) + base;
     const T* vb = static_cast<const T*>(a.v) + base;
     const T* W = static_cast<const T*>(a.w) + static_cast<int64_t>(h) * a.wh;
@@ -152,8 +157,8 @@ __global__ __launch_bounds__(kThreads) void commit_generic_kernel(CommitArgs a)
     for (int k = 0; k < KPT; ++k) acc[k] = 0.0f;
     float zacc = 0.0f;
 
-    for (int t0 = 0; t0 < a.B; t0 += TC) {
-        const int nt = min(TC, a.B - t0);
+    for (int t0 = 0; t0 < n; t0 += TC) {
+        const int nt = min(TC, n - t0);
         for (int idx = tid; idx < nt * a.d; idx += kThreads) {
             const int tt = idx / a.d, cc = idx % a.d;
             xk[tt][cc] = ld_elem(kb, static_cast<int64_t>(t0 + tt) * a.ks.tok + cc);

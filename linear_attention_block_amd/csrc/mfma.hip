@@ -561,6 +561,142 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
     }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill: one work-group per (request, head) folds the request's whole packed
+// token range into the state, 32 tokens per step, with the state slice held in
+// registers throughout (one read and one write of the record). Per step: the
+// chunk's K and V rows go to LDS (the next chunk's loads are issued before the
+// arithmetic), every wave computes phi(k_t) for the 32 tokens (lane = token),
+// the waves write disjoint row ranges of phi(K)^T into LDS (fp32), and each
+// wave adds phi(K)^T V for its 32 value columns into its slice by MFMA, V being
+// read transposed with ds_read_b64_tr_b16; Z accumulates in fp32.
+// ---------------------------------------------------------------------------
+template <int D, int FW>
+__global__ __launch_bounds__(64 * (D / 32)) void prefill_mfma_kernel(CommitArgs a)
+{
+    using C = Cfg<D, FW>;
+    constexpr int F = C::F;
+    const int pair = blockIdx.x;
+    const int r = pair / a.H, h = pair % a.H;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int ln = lane & 31, g = lane >> 5;
+
+    __shared__ __attribute__((aligned(16))) uint16_t Ks[32 * C::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[32 * C::RS];
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[FW * C::RS];
+    __shared__ __attribute__((aligned(16))) float Pt[F * C::PS];
+
+    const int slot = a.slot_ids[r];
+    if (slot < 0 || slot >= a.num_slots) return;
+    int64_t first_row;
+    int n;
+    commit_rows(a, r, first_row, n);
+    if (n == 0) return;
+    float* rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * F;
+    const int64_t base = first_row * a.ks.tok + static_cast<int64_t>(h) * a.ks.head;
+    const uint16_t* kb = static_cast<const uint16_t*>(a.k) + base;
+    const uint16_t* vb = static_cast<const uint16_t*>(a.v) + base;
+    const int tok = static_cast<int>(a.ks.tok);
+
+    RowChunks<D, C::NT> kc, vc;
+    {
+        WChunks<D, FW, C::NT> wc;
+        wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
+        kc.load(kb, tok, n < 32 ? n : 32, tid);
+        vc.load(vb, tok, n < 32 ? n : 32, tid);
+        wc.template store_rows<C::RS>(Ws, tid);
+    }
+    f32x4 sv[C::NSL];
+    load_state_slice(rec + wv * F * 32, lane, sv);
+    float zacc[(F + C::NT - 1) / C::NT];
+#pragma unroll
+    for (int i = 0; i < (F + C::NT - 1) / C::NT; ++i) zacc[i] = 0.0f;
+
+    const int nchunks = (n + 31) / 32;
+    for (int c = 0; c < nchunks; ++c) {
+        const int nc = n - 32 * c < 32 ? n - 32 * c : 32;
+        __syncthreads();  // every wave is done with the previous chunk's LDS data
+        kc.template store_rows<C::RS>(Ks, tid);
+        vc.template store_rows<C::RS>(Vs, tid);
+        __syncthreads();
+        if (c + 1 < nchunks) {
+            const int rem = n - 32 * (c + 1);
+            kc.load(kb + static_cast<int64_t>(32 * (c + 1)) * a.ks.tok, tok, rem < 32 ? rem : 32, tid);
+            vc.load(vb + static_cast<int64_t>(32 * (c + 1)) * a.ks.tok, tok, rem < 32 ? rem : 32, tid);
+        }
+
+        // phi(k_t) for token ln, normalised; tokens beyond the chunk give zero
+        f32x16 u[FW / 32];
+        feature_logits<D, FW, C::RS>(Ws, Ks, ln, g, u);
+        float mx, mn;
+        logit_range<FW>(u, mx, mn);
+        float sp = 0.0f, sn = 0.0f;
+#pragma unroll
+        for (int T = 0; T < FW / 32; ++T)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                sp += __expf(u[T][v] - mx);
+                sn += __expf(mn - u[T][v]);
+            }
+        sp += __shfl_xor(sp, 32, 64);
+        sn += __shfl_xor(sn, 32, 64);
+        const float ip = ln < nc ? 1.0f / sp : 0.0f;
+        const float in = ln < nc ? 1.0f / sn : 0.0f;
+        // phi(K)^T rows of the feature tiles T = wv, wv + NW, ... (disjoint across waves)
+#pragma unroll
+        for (int T = 0; T < FW / 32; ++T) {
+            if (T % C::NW != wv) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int fw = 32 * T + 8 * (v >> 2) + 4 * g + (v & 3);
+                Pt[fw * C::PS + ln] = __expf(u[T][v] - mx) * ip;
+                Pt[(FW + fw) * C::PS + ln] = __expf(mn - u[T][v]) * in;
+            }
+        }
+        __syncthreads();
+
+        // dS = phi(K)^T V over this wave's 32 columns, added into the slice
+#pragma unroll
+        for (int ft = 0; ft < F / 32; ++ft) {
+            f32x16 acc = f32x16{};
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                const float* pr = Pt + (32 * ft + ln) * C::PS + 16 * kb2 + 4 * g;
+                const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr);
+                const f32x4 p1 = *reinterpret_cast<const f32x4*>(pr + 8);
+                bf16x8 ap;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ap[e] = static_cast<__bf16>(p0[e]);
+                    ap[4 + e] = static_cast<__bf16>(p1[e]);
+                }
+                acc = mfma32(ap, vt_frag<C::RS>(Vs, 32 * wv, kb2, lane), acc);
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) sv[4 * ft + (v >> 2)][v & 3] += acc[v];
+        }
+        // dZ in fp32, fixed summation order
+#pragma unroll
+        for (int i = 0; i < (F + C::NT - 1) / C::NT; ++i) {
+            const int f = tid + i * C::NT;
+            if (f < F) {
+                float z = 0.0f;
+#pragma unroll
+                for (int t = 0; t < 32; ++t) z += Pt[f * C::PS + t];
+                zacc[i] += z;
+            }
+        }
+    }
+    f32x4* dst = reinterpret_cast<f32x4*>(rec + wv * F * 32) + lane;
+#pragma unroll
+    for (int t = 0; t < C::NSL; ++t) __builtin_nontemporal_store(sv[t], dst + t * 64);
+#pragma unroll
+    for (int i = 0; i < (F + C::NT - 1) / C::NT; ++i) {
+        const int f = tid + i * C::NT;
+        if (f < F) rec[D * F + f] += zacc[i];
+    }
+}
+
 // Compute units of the current device (cached per device ordinal).
 static int compute_units()
 {
@@ -603,6 +739,19 @@ static hipError_t forward_by_fw(const ForwardArgs& a, hipStream_t s)
 }
 
 template <int D>
+static hipError_t prefill_by_fw(const CommitArgs& a, hipStream_t s)
+{
+    const dim3 grid(static_cast<uint32_t>(a.R * a.H)), block(64 * (D / 32));
+    switch (a.FW) {
+        case 32: hipLaunchKernelGGL((prefill_mfma_kernel<D, 32>), grid, block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((prefill_mfma_kernel<D, 64>), grid, block, 0, s, a); break;
+        case 128: hipLaunchKernelGGL((prefill_mfma_kernel<D, 128>), grid, block, 0, s, a); break;
+        default: return hipErrorNotSupported;
+    }
+    return hipGetLastError();
+}
+
+template <int D>
 static hipError_t commit_by_fw(const CommitArgs& a, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>(a.R * a.H)), block(64 * (D / 32));
@@ -626,6 +775,15 @@ hipError_t launch_forward_mfma(const ForwardArgs& a, hipStream_t s)
     if (!small_token_stride(a.qs.tok) || !small_token_stride(a.os.tok)) return hipErrorNotSupported;
     if (a.d == 128) return forward_by_fw<128>(a, s);
     if (a.d == 64) return forward_by_fw<64>(a, s);
+    return hipErrorNotSupported;
+}
+
+hipError_t launch_prefill_mfma(const CommitArgs& a, hipStream_t s)
+{
+    if (a.io != BHA_BF16 || a.seq_offsets == nullptr) return hipErrorNotSupported;
+    if (!small_token_stride(a.ks.tok)) return hipErrorNotSupported;
+    if (a.d == 128) return prefill_by_fw<128>(a, s);
+    if (a.d == 64) return prefill_by_fw<64>(a, s);
     return hipErrorNotSupported;
 }
 

@@ -191,3 +191,28 @@ def test_fp32_stride_alignment(lib):
 def test_size_overflow(lib):
     huge = bha_strides(1 << 61, 256, 128)
     assert fwd(lib, _dims(), qs=huge) == DIMS
+
+
+def prefill(lib, dims, k=FAKE, v=FAKE, ks=None, offs=FAKE, total=100, w=FAKE, wh=64 * 128, state=FAKE,
+            num_slots=8, slots=FAKE):
+    ks = ks or _st(req=0)
+    P = ctypes.c_void_p
+    return lib.bha_state_prefill(ctypes.byref(dims) if dims is not None else None, P(k), P(v),
+                                 ctypes.byref(ks), P(offs), total, P(w), wh, P(state), num_slots, P(slots), P(0))
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, None) == NULL
+    assert prefill(lib, _dims(num_requests=0), k=0, v=0, offs=0, w=0, state=0, slots=0) == OK
+    assert prefill(lib, _dims(), total=0) == OK  # nothing to fold; no pointer is read
+    assert prefill(lib, _dims(), total=-1) == DIMS
+    assert prefill(lib, _dims(), offs=0) == NULL
+    assert prefill(lib, _dims(), offs=FAKE + 2) == ALIGN
+    assert prefill(lib, _dims(), k=0) == NULL
+    assert prefill(lib, _dims(), v=FAKE + 8) == ALIGN
+    assert prefill(lib, _dims(), ks=_st(req=0, tok=2 * 128 + 4)) == STRIDE
+    assert prefill(lib, _dims(), w=0) == NULL
+    assert prefill(lib, _dims(), slots=0) == NULL
+    assert prefill(lib, _dims(), num_slots=0) == DIMS
+    assert prefill(lib, _dims(head_dim=96)) == UNSUP
+    assert prefill(lib, _dims(), total=1 << 40) == DIMS

@@ -247,3 +247,78 @@ def test_bitwise_deterministic(dev):
     run.state.copy_(s0)
     run.commit_active()
     assert torch.equal(run.state, s1)
+
+
+@pytest.mark.parametrize("io,d,fw", [("bf16", 128, 64), ("bf16", 64, 128), ("bf16", 128, 32), ("bf16", 128, 128),
+                                     ("f32", 64, 32), ("f32", 128, 64)])
+def test_prefill_ragged_matches_oracle_build(dev, io, d, fw):
+    # ragged prompts of 0..100 tokens (packed), folded in two prefill calls
+    # (first part, then the rest, so the second call adds to a non-empty
+    # state), against the oracle's state built from scratch over all tokens
+    case = synth.make_case("tiny", R=7, H=2, d=d, FW=fw, B=1, io=io, blocks=(0, 100), gamma="uniform")
+    lens = case.n_blocks.copy()
+    lens[:3] = [0, 1, 33]
+    H, F = case.H, case.F
+    first = lens // 2
+    parts = []
+    for lo_frac in (0, 1):
+        ks, vs, offs = [], [], [0]
+        for r in range(case.R):
+            a, b = (0, int(first[r])) if lo_frac == 0 else (int(first[r]), int(lens[r]))
+            ks.append(case.prefix_k[r][a:b])
+            vs.append(case.prefix_v[r][a:b])
+            offs.append(offs[-1] + (b - a))
+        parts.append((np.concatenate(ks), np.concatenate(vs), np.array(offs, dtype=np.int32)))
+    w = to_device(case.w, io, dev)
+    slots = torch.from_numpy(case.slot_ids).to(dev)
+    state = bha.new_state(case.num_slots, H, d, fw, dev)
+    for kp, vp, offs in parts:
+        bha.state_prefill(to_device(kp, io, dev), to_device(vp, io, dev), torch.from_numpy(offs).to(dev), w,
+                          state, slots)
+    torch.cuda.synchronize()
+    S, Z = record_to_plain(state.cpu().numpy()[case.slot_ids], d, F)
+    worst = 0.0
+    for r in range(case.R):
+        n = int(lens[r])
+        k_all = case.prefix_k[r][:n].astype(np.float64)
+        v_all = case.prefix_v[r][:n].astype(np.float64)
+        for h in range(H):
+            S_ref, Z_ref = oracle.state_build(k_all[:, h], v_all[:, h], case.w[h])
+            if n == 0:
+                assert np.all(S[r, h] == 0) and np.all(Z[r, h] == 0)
+                continue
+            worst = max(worst, normwise_err(S[r, h], S_ref, None), normwise_err(Z[r, h], Z_ref, None))
+    _log(f"[prefill] io={io} d={d} FW={fw} lens={lens.tolist()} err {worst:.2e}")
+    assert worst <= TOL[io]
+
+
+def test_prefill_long_prompts_fused_kv(dev):
+    # prompts of several thousand tokens (many 32-token chunks per work-group),
+    # k and v as views of one fused [T][2][H][d] tensor, slots in shuffled order
+    case = synth.make_case("tiny", R=4, H=4, d=128, FW=64, B=64, io="bf16", blocks=(20, 70),
+                           gamma="uniform")
+    lens = case.n_blocks * case.B - np.array([0, 7, 31, 33])[:case.R]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    kp = np.concatenate([case.prefix_k[r][:lens[r]] for r in range(case.R)])
+    vp = np.concatenate([case.prefix_v[r][:lens[r]] for r in range(case.R)])
+    fused = to_device(np.stack([kp, vp], axis=1), "bf16", dev)
+    state = bha.new_state(case.num_slots, case.H, case.d, case.FW, dev)
+    bha.state_prefill(fused[:, 0], fused[:, 1], torch.from_numpy(offs).to(dev), to_device(case.w, "bf16", dev),
+                      state, torch.from_numpy(case.slot_ids).to(dev))
+    torch.cuda.synchronize()
+    S, Z = record_to_plain(state.cpu().numpy()[case.slot_ids], case.d, case.F)
+    S_ref = np.zeros_like(S)
+    Z_ref = np.zeros_like(Z)
+    k_all = np.ascontiguousarray(np.transpose(kp, (1, 0, 2))).astype(np.float64)
+    v_all = np.ascontiguousarray(np.transpose(vp, (1, 0, 2))).astype(np.float64)
+    for r in range(case.R):
+        for h in range(case.H):
+            S_ref[r, h], Z_ref[r, h] = oracle.state_build(k_all[h, offs[r]:offs[r + 1]],
+                                                          v_all[h, offs[r]:offs[r + 1]], case.w[h])
+    e_s = normwise_err(S, S_ref, (2, 3))
+    e_z = normwise_err(Z, Z_ref, (2,))
+    _log(f"[prefill-long] lens={lens.tolist()} S err {e_s:.2e} Z err {e_z:.2e}")
+    assert e_s <= TOL["bf16"] and e_z <= TOL["bf16"]
+    # untouched slots stay zero
+    rest = np.setdiff1d(np.arange(case.num_slots), case.slot_ids)
+    assert not state.cpu().numpy()[rest].any()
