@@ -11,7 +11,8 @@ do not find its 270 MB state in the 256 MB Infinity Cache.
 
 Default workload (decode256): 256 requests x 16 heads, d = 128, FW = 64
 (F = 128), B = 32, ragged prefixes of UniformInt{8..256} blocks (256..8,192
-tokens) committed into the states before timing, bf16 Q/K/V/W/O, fp32 states.
+tokens) folded into the states before timing (one ragged prefill launch per
+layer, itself timed and reported), bf16 Q/K/V/W/O, fp32 states.
 
 Prints ONE JSON line: value = active-block tokens per second through
 block-hybrid attention (each forward moves R * B tokens through one layer),
@@ -49,6 +50,14 @@ def commit_bytes(R, H, d, FW, B, es=2):
     the state record read and written back, K and V read; W once per head."""
     F = 2 * FW
     return R * H * (2 * (d * F * 4 + F * 4) + 2 * B * d * es) + H * FW * d * es
+
+
+def prefill_bytes(T, R, H, d, FW, es=2):
+    """Algorithmic HBM bytes of one bha_state_prefill launch over T packed tokens:
+    K and V of every token and head read once, each (request, head) state record
+    read and written once, W once per head, the offsets and slot ids."""
+    F = 2 * FW
+    return T * H * 2 * d * es + R * H * 2 * (d * F * 4 + F * 4) + H * FW * d * es + (2 * R + 1) * 4
 
 
 def kernel_source_hash() -> str:
@@ -170,25 +179,38 @@ def main() -> int:
     nl, nd = args.layers, args.denoise
     slots = torch.from_numpy(case.slot_ids).to(dev)
     max_blocks = int(case.n_blocks.max())
-    act = [torch.from_numpy(case.slot_ids[case.n_blocks > i]).to(dev) for i in range(max_blocks)]
+    T = int(case.n_blocks.sum()) * B
 
+    # each layer's states are built from its whole ragged prefix by one prefill
+    # launch (timed); the first launch goes into a scratch pool as a warm-up
     t_setup = time.perf_counter()
-    layers = []
+    layers, prefill_ms = [], []
     for L in range(nl):
         w, gamma = synth.device_layer_params(args.config, L, dev)
         state = bha.new_state(case.num_slots, H, d, FW, dev)
-        for i in range(max_blocks):
-            kb, vb = synth.device_blocks(args.config, i, act[i].numel(), dev, layer=L)
-            bha.state_commit(kb, vb, w, state, act[i])
+        pk, pv, offs = synth.device_packed_prefix(args.config, case.n_blocks, dev, layer=L)
+        if L == 0:
+            bha.state_prefill(pk, pv, offs, w, bha.new_state(case.num_slots, H, d, FW, dev), slots)
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record()
+        bha.state_prefill(pk, pv, offs, w, state, slots)
+        p1.record()
+        torch.cuda.synchronize()
+        prefill_ms.append(p0.elapsed_time(p1))
+        del pk, pv
         q, k, v = synth.device_step_qkv(args.config, 0, R, dev, layer=L)
         out = torch.empty_like(q)
         layers.append(dict(w=w, gamma=gamma, state=state, q=q, k=k, v=v, out=out,
                            fwd=bha.prepare_forward(q, k, v, w, gamma, state, slots, out),
                            com=bha.prepare_commit(k, v, w, state, slots)))
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    pre_avg = sum(prefill_ms) / len(prefill_ms) * 1e-3
+    pb = prefill_bytes(T, R, H, d, FW)
     log(f"setup: {nl} layers x {R} requests, prefixes {int(case.n_blocks.min()) * B}.."
-        f"{max_blocks * B} tokens ({int(case.n_blocks.sum()) * B} total), "
-        f"{time.perf_counter() - t_setup:.1f} s")
+        f"{max_blocks * B} tokens ({T} total), {time.perf_counter() - t_setup:.1f} s")
+    log(f"prefill: avg {pre_avg * 1e6:.1f} us/launch over {nl} layers, {T / pre_avg / 1e6:.1f} M tokens/s, "
+        f"{pb / pre_avg / 1e9:.0f} GB/s algorithmic ({pb / 1e9:.2f} GB/launch)")
 
     n_fwd, n_com = nd * nl, nl
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -302,6 +324,15 @@ def main() -> int:
             "bytes_per_launch": cb,
             "achieved_GBps": cb / com_avg / 1e9,
             "frac": cb / com_avg / 1e9 / PEAK_HBM_GBS,
+        },
+        "prefill": {
+            "workload": f"one bha_state_prefill launch per layer over all {R} requests' packed prefixes "
+                        f"({T} tokens x {H} heads)",
+            "avg_launch_us": pre_avg * 1e6,
+            "tokens_per_s": T / pre_avg,
+            "bytes_per_launch": pb,
+            "achieved_GBps": pb / pre_avg / 1e9,
+            "frac": pb / pre_avg / 1e9 / PEAK_HBM_GBS,
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(layers[0], case, nd,
                                                                           args.cpu_sample_requests, log),

@@ -207,3 +207,31 @@ def device_step_qkv(name: str, step: int, R: int, device, *, layer: int = 0, **o
     qkv = torch.randn((3, R, B, H, d), generator=gen, device=device, dtype=torch.float32)
     qkv = qkv.to(_io_torch(cfg["io"]))
     return qkv[0], qkv[1], qkv[2]
+
+
+def device_packed_prefix(name: str, n_blocks, device, *, layer: int = 0, **over):
+    """Every request's whole prefix packed token-major for a ragged prefill:
+    returns (k, v, seq_offsets) with k, v [T][H][d] and seq_offsets int32 [R+1],
+    request r owning rows seq_offsets[r] .. seq_offsets[r+1]-1. The tokens are
+    exactly those ``device_blocks`` draws for block indices 0 .. n_blocks[r]-1
+    (same seeds), so a prefill over them and chained commits of those blocks
+    fold the same values."""
+    import torch
+
+    cfg = dict(CONFIGS[name])
+    cfg.update(over)
+    B, H, d = cfg["B"], cfg["H"], cfg["d"]
+    n_blocks = np.asarray(n_blocks, dtype=np.int64)
+    offs = np.concatenate([[0], np.cumsum(n_blocks * B)])
+    T = int(offs[-1])
+    k = torch.empty((T, H, d), dtype=_io_torch(cfg["io"]), device=device)
+    v = torch.empty_like(k)
+    offs_dev = torch.from_numpy(offs).to(device)
+    tok = torch.arange(B, device=device)
+    for i in range(int(n_blocks.max(initial=0))):
+        act = torch.from_numpy(np.nonzero(n_blocks > i)[0]).to(device)
+        kb, vb = device_blocks(name, i, int(act.numel()), device, layer=layer, **over)
+        rows = (offs_dev[act][:, None] + i * B + tok[None, :]).reshape(-1)
+        k[rows] = kb.reshape(-1, H, d)
+        v[rows] = vb.reshape(-1, H, d)
+    return k, v, torch.from_numpy(offs.astype(np.int32)).to(device)

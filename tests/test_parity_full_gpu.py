@@ -7,7 +7,9 @@ oracle then checks, one pair at a time:
   * sampled forward outputs, from the same fp32 state bytes the kernel read;
   * the commit on sampled pairs, from the same pre-commit state;
   * the chained GPU state of the shortest and longest requests against the
-    oracle's state built from scratch over their whole prefix.
+    oracle's state built from scratch over their whole prefix;
+  * one ragged prefill launch over the same prefix tokens (packed): every pair
+    against the chained state, the tracked requests against the oracle.
 Bars: normwise 2e-2 (bf16 I/O, fp32 accumulation and state).
 """
 import os
@@ -35,6 +37,17 @@ def dev():
     return torch.device("cuda:0")
 
 
+def _pairwise_err(got, ref, d, F):
+    # normwise error per (request, head) record, max over pairs: (S part, Z part)
+    got, ref = got.double(), ref.double()
+    out = []
+    for lo, hi in ((0, d * F), (d * F, (d + 1) * F)):
+        num = (got[..., lo:hi] - ref[..., lo:hi]).abs().amax(dim=-1)
+        den = ref[..., lo:hi].abs().amax(dim=-1).clamp_min(1e-300)
+        out.append(float((num / den).max()))
+    return out
+
+
 def _run_full(name, dev, n_pairs=24, seed=0):
     case = synth.make_case(name, with_prefix=False, with_qkv=False)
     R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B
@@ -55,6 +68,19 @@ def _run_full(name, dev, n_pairs=24, seed=0):
                 j = int(np.searchsorted(act, r))
                 kept[r][0].append(kb[j].float().cpu().numpy())
                 kept[r][1].append(vb[j].float().cpu().numpy())
+    sel = torch.from_numpy(case.slot_ids.astype(np.int64)).to(dev)
+    pk, pv, offs = synth.device_packed_prefix(name, case.n_blocks, dev, layer=0)
+    state_p = bha.new_state(case.num_slots, H, d, FW, dev)
+    bha.state_prefill(pk, pv, offs, w, state_p, slots)
+    torch.cuda.synchronize()
+    del pk, pv
+    e_pc = _pairwise_err(state_p[sel], state[sel], d, F)
+    prefilled = state_p[sel].cpu().numpy()
+    del state_p
+    print(f"[{name}] prefill vs chained commits over all {R * H} pairs: S err {e_pc[0]:.2e}, Z err {e_pc[1]:.2e}",
+          flush=True)
+    assert e_pc[0] <= TOL and e_pc[1] <= TOL
+
     q, k, v = synth.device_step_qkv(name, 0, R, dev, layer=0)
     out = bha.block_forward(q, k, v, w, gamma, state, slots)
     torch.cuda.synchronize()
@@ -93,6 +119,11 @@ def _run_full(name, dev, n_pairs=24, seed=0):
         e_z = normwise_err(Zg, Z_ref[0], (1,))
         print(f"[{name}] chained state of request {r} ({kp.shape[0]} prefix tokens): S err {e_s:.2e}, "
               f"Z err {e_z:.2e}", flush=True)
+        assert e_s <= TOL and e_z <= TOL
+        Sp, Zp = record_to_plain(prefilled[r], d, F)
+        e_s = normwise_err(Sp, S_ref[0], (1, 2))
+        e_z = normwise_err(Zp, Z_ref[0], (1,))
+        print(f"[{name}] prefilled state of request {r}: S err {e_s:.2e}, Z err {e_z:.2e}", flush=True)
         assert e_s <= TOL and e_z <= TOL
 
 
