@@ -31,6 +31,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
 {
@@ -66,6 +67,31 @@ __device__ __forceinline__ bf16x8 vt_frag(const uint16_t* Vs, int c0, int kb, in
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// Tiles read transposed with no padding, stored in 8-byte pieces: piece p of
+// row t (RB pieces per row) sits at position p ^ lds_piece_swizzle<RB>(t).
+// The swizzle is even, so 16-byte chunks stay whole, and it is chosen for the
+// 64 banks of the LDS: the four rows one half-wave's transposed read touches
+// fall into four distinct 64-byte bank groups, and the sixteen rows a 16-lane
+// group writes at one column land in sixteen distinct pieces.
+template <int RB>
+__device__ __forceinline__ int lds_piece_swizzle(int t)
+{
+    return RB >= 32 ? 8 * (t & 3) + 2 * ((t >> 2) & 3) : 8 * ((t >> 1) & 1) + 2 * ((t >> 2) & 3);
+}
+
+// vt_frag for a piece-swizzled tile of RB pieces per row.
+template <int RB>
+__device__ __forceinline__ bf16x8 vt_frag_ps(const uint16_t* Xs, int c0, int kb, int lane)
+{
+    const int m = lane & 15, q = lane >> 4, g = lane >> 5;
+    const int piece = (c0 >> 2) + 4 * (q & 1) + (m & 3);
+    const int row = 16 * kb + 4 * g + (m >> 2);
+    const i16x4 lo = lds_read_tr(Xs + row * (4 * RB) + ((piece ^ lds_piece_swizzle<RB>(row)) << 2));
+    const i16x4 hi = lds_read_tr(Xs + (row + 8) * (4 * RB) + ((piece ^ lds_piece_swizzle<RB>(row + 8)) << 2));
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 template <int D, int FW>
 struct Cfg {
     static constexpr int F = 2 * FW;
@@ -93,18 +119,18 @@ __device__ __forceinline__ void load_state_slice(const float* rec_slice, int lan
     for (int t = 0; t < NSL; ++t) sv[t] = __builtin_nontemporal_load(p + t * 64);
 }
 
-// A thread's share of the 16-byte chunks of a 32-row x D bf16 token block,
+// A thread's share of the 16-byte chunks of a ROWS x D bf16 token block,
 // held in registers between the global loads and the LDS writes so that all
 // global loads of a work-group can be issued back to back. Rows >= nrows are
 // zero.
-template <int D, int NT>
+template <int D, int NT, int ROWS = 32>
 struct RowChunks {
     static constexpr int CH = D / 8;
-    static constexpr int N = 32 * CH / NT;
+    static constexpr int N = ROWS * CH / NT;
     uint4 v[N];
 
-    // tok: token stride in elements; the launcher guarantees 32 * tok fits in
-    // 31 bits. Rows >= nrows read row nrows - 1 (always present) and are
+    // tok: token stride in elements; the launcher guarantees ROWS * tok fits
+    // in 31 bits. Rows >= nrows read row nrows - 1 (always present) and are
     // zeroed, so the loads need no divergent branches.
     __device__ __forceinline__ void load(const uint16_t* src, int tok, int nrows, int tid)
     {
@@ -115,6 +141,19 @@ struct RowChunks {
             const uint4 x = *reinterpret_cast<const uint4*>(src + (tr * tok + ch * 8));
             const bool keep = t < nrows;
             v[i] = make_uint4(keep ? x.x : 0u, keep ? x.y : 0u, keep ? x.z : 0u, keep ? x.w : 0u);
+        }
+    }
+    // the same rows without the zeroing: rows >= nrows hold a copy of row
+    // nrows - 1, for callers whose weights for those rows are zero. The loaded
+    // registers are not touched until they are stored, so the loads stay in
+    // flight until then.
+    __device__ __forceinline__ void load_clamped(const uint16_t* src, int tok, int nrows, int tid)
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
+            const int tr = t < nrows ? t : nrows - 1;
+            v[i] = *reinterpret_cast<const uint4*>(src + (tr * tok + ch * 8));
         }
     }
     // row-major copy, row stride RS
@@ -562,29 +601,248 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
 }
 
 // ---------------------------------------------------------------------------
-// Prefill: one work-group per (request, head) folds the request's whole packed
-// token range into the state, 32 tokens per step, with the state slice held in
-// registers throughout (one read and one write of the record). Per step: the
-// chunk's K and V rows go to LDS (the next chunk's loads are issued before the
-// arithmetic), every wave computes phi(k_t) for the 32 tokens (lane = token),
-// the waves write disjoint row ranges of phi(K)^T into LDS (fp32), and each
-// wave adds phi(K)^T V for its 32 value columns into its slice by MFMA, V being
-// read transposed with ds_read_b64_tr_b16; Z accumulates in fp32.
+// Prefill: one work-group of four waves per (request, head) folds the
+// request's whole packed token range into the state; the record is read once
+// and written once, the state staying in registers throughout. Wave w owns the
+// state rows [r0, r0 + RW) of the value columns [32 cs, 32 cs + 32): with
+// d = 128 one column slice and all F features (cs = w), with d = 64 one column
+// slice and one feature half. Tokens go in chunks of CT = 64, 16 per wave:
+//   * each wave computes phi(k_t) for its own 16 tokens with 16x16x32 tiles
+//     (lane = token n, k-group q: features 16 T + 4 q + {0..3}); the
+//     contraction over d is fed in the order q, k-step ks -> elements
+//     q d/4 + 8 ks .. + 7, the same for W, so each lane's K fragments are one
+//     contiguous d/4-element run of its token's row, loaded straight from
+//     global memory into registers; the per-token max, min and sums over the
+//     features combine the four k-group lanes;
+//   * phi(K) goes to LDS once as bf16 rows and V rows are copied to LDS; both
+//     are read back transposed (ds_read_b64_tr_b16) as the A and B operands of
+//     dS = phi(K)^T V, accumulated straight into the state tiles. Rows past
+//     the end of the request hold copies of its last row, with zero phi;
+//   * Z accumulates in fp32 per lane (token slot) and is reduced across slots
+//     once, at the end, in a fixed order.
+// The loop is software pipelined: phi of chunk c + 1 and dS of chunk c run
+// between two barriers, from opposite LDS buffers; the K and V loads of chunk
+// c + 2 are issued during chunk c + 1's phi. LDS (80 KiB
+// at d = 128, F = 128) and registers are sized so that two work-groups share a
+// CU and cover each other's barrier and memory waits.
 // ---------------------------------------------------------------------------
-template <int D, int FW>
-__global__ __launch_bounds__(64 * (D / 32)) void prefill_mfma_kernel(CommitArgs a)
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
 {
-    using C = Cfg<D, FW>;
-    constexpr int F = C::F;
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D, int FW>
+struct PCfg {
+    static constexpr int F = 2 * FW;
+    static constexpr int NC = D / 32;                   // 32-column slices of the state
+    static constexpr int NWV = F * NC > 512 ? 8 : 4;    // waves: at most 128 state rows each
+    static constexpr int NT = 64 * NWV;
+    static constexpr int CT = 16 * NWV;                 // tokens per chunk, 16 per wave
+    static constexpr int RW = F * NC / NWV;             // state rows of one wave
+    static constexpr int VC = D / 8;                    // 16-byte chunks per row of V and W
+    static constexpr int KS = D / 32;                   // k-steps of the 16x16x32 logits
+    static constexpr int PD = 1;                        // chunks whose loads run ahead of phi
+    static constexpr int VQ = CT * VC / NT;             // 16-byte V chunks per thread per chunk
+    // two LDS buffers of V and phi(K) (pipelined loop) when they fit
+    static constexpr int NBUF = 2 * (2 * CT * (D + F) + FW * D) <= 160 * 1024 ? 2 : 1;
+    static constexpr int MAIN = 2 * (NBUF * CT * (D + F) + FW * D);
+    static constexpr int ZRED = 4 * CT * F;             // fp32 Z partials of every token slot
+    static constexpr int LDS = MAIN > ZRED ? MAIN : ZRED;
+};
+
+// W in LDS as the logits' A fragments in read order: block ks FW/16 + T
+// (1 KiB) holds, at 16-byte slot lane = n16 + 16 q, the elements
+// q d/4 + 8 ks .. + 7 of row 16 T + n16, so each fragment read is one
+// contiguous, conflict-free 1 KiB.
+template <int D, int FW>
+__device__ __forceinline__ bf16x8 w_frag(const uint16_t* Ws, int T, int ks, int lane)
+{
+    return lds_frag(Ws + ((ks * (FW / 16) + T) * 64 + lane) * 8);
+}
+
+// Per-pair constants of the prefill loop.
+template <int D, int FW>
+struct PrefillPair {
+    const uint16_t* kbase;  // first token row of the request, this head
+    const uint16_t* vbase;
+    int64_t tok64;          // token stride (elements)
+    int tok;
+    int n;                  // tokens of the request
+    int nchunks;
+};
+
+template <int D, int FW>
+__device__ __forceinline__ int prefill_chunk_rows(const PrefillPair<D, FW>& pp, int c)
+{
+    constexpr int CT = PCfg<D, FW>::CT;
+    return pp.n - CT * c < CT ? pp.n - CT * c : CT;
+}
+
+// V rows of chunk c: thread tid's 16-byte chunks; rows past the end read the
+// request's last row (their phi is zero). Nothing consumes the registers until
+// they are stored, so the loads stay in flight.
+template <int D, int FW>
+__device__ __forceinline__ void prefill_load_v(const PrefillPair<D, FW>& pp, int c, int tid,
+                                               u32x4 (&vr)[PCfg<D, FW>::VQ])
+{
+    using P = PCfg<D, FW>;
+    const int nc = prefill_chunk_rows(pp, c);
+    const uint16_t* src = pp.vbase + static_cast<int64_t>(P::CT) * c * pp.tok64;
+#pragma unroll
+    for (int i = 0; i < P::VQ; ++i) {
+        const int idx = tid + i * P::NT, t = idx / P::VC, ch = idx % P::VC;
+        const int tr = t < nc ? t : nc - 1;
+        vr[i] = *reinterpret_cast<const u32x4*>(src + (tr * pp.tok + ch * 8));
+    }
+}
+
+template <int D, int FW>
+__device__ __forceinline__ void prefill_store_v(uint16_t* Vb, int tid, const u32x4 (&vr)[PCfg<D, FW>::VQ])
+{
+    using P = PCfg<D, FW>;
+#pragma unroll
+    for (int i = 0; i < P::VQ; ++i) {
+        const int idx = tid + i * P::NT, t = idx / P::VC, ch = idx % P::VC;
+        *reinterpret_cast<u32x4*>(Vb + t * D + (((2 * ch) ^ lds_piece_swizzle<D / 4>(t)) << 2)) = vr[i];
+    }
+}
+
+// K fragments of wave wv's 16 tokens of chunk c for lane (n16, q): the run
+// q d/4 .. q d/4 + d/4 - 1 of the token's row.
+template <int D, int FW>
+__device__ __forceinline__ void prefill_load_k(const PrefillPair<D, FW>& pp, int c, int wv, int n16, int q,
+                                               bf16x8 (&kf)[D / 32])
+{
+    constexpr int CT = PCfg<D, FW>::CT;
+    const int nc = prefill_chunk_rows(pp, c);
+    const int t = 16 * wv + n16;
+    const int tr = t < nc ? t : nc - 1;
+    const uint16_t* src = pp.kbase + static_cast<int64_t>(CT) * c * pp.tok64 + (tr * pp.tok + q * (D / 4));
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) kf[ks] = *reinterpret_cast<const bf16x8*>(src + 8 * ks);
+}
+
+// First half of chunk c: V rows to LDS, the loads PD chunks ahead issued,
+// phi(K) of this wave's 16 tokens to LDS and into the Z partials. Safe for
+// c == nchunks (one past the end): no loads, zero phi, buffers unused.
+template <int D, int FW>
+__device__ __forceinline__ void prefill_phi(const PrefillPair<D, FW>& pp, int c, int tid, uint16_t* Vs,
+                                            uint16_t* Ps, const uint16_t* Ws, u32x4 (&vr)[PCfg<D, FW>::VQ],
+                                            bf16x8 (&kf)[D / 32], float (&zl)[FW / 2])
+{
+    using P = PCfg<D, FW>;
+    constexpr int F = P::F, CT = P::CT, KS = P::KS, PD = P::PD;
+    constexpr float kLog2e = 1.4426950408889634f;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int n16 = lane & 15, q = lane >> 4;
+    const int nc = prefill_chunk_rows(pp, c);
+    uint16_t* const Vb = Vs + (P::NBUF == 2 ? (c & 1) : 0) * (CT * D);
+    uint16_t* const Pb = Ps + (P::NBUF == 2 ? (c & 1) : 0) * (CT * F);
+    prefill_store_v<D, FW>(Vb, tid, vr);
+    if (c + PD < pp.nchunks) prefill_load_v(pp, c + PD, tid, vr);
+
+    // feature logits of this wave's 16 tokens (base 2)
+    f32x4 u[FW / 16];
+#pragma unroll
+    for (int T = 0; T < FW / 16; ++T) u[T] = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int T = 0; T < FW / 16; ++T) u[T] = mfma16(w_frag<D, FW>(Ws, T, ks, lane), kf[ks], u[T]);
+    if (c + PD < pp.nchunks) prefill_load_k(pp, c + PD, wv, n16, q, kf);
+    float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+    for (int T = 0; T < FW / 16; ++T)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            u[T][e] *= kLog2e;
+            mx = fmaxf(mx, u[T][e]);
+            mn = fminf(mn, u[T][e]);
+        }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mn = fminf(mn, __shfl_xor(mn, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mn = fminf(mn, __shfl_xor(mn, 32, 64));
+    f32x4 en[FW / 16];
+    float sp = 0.0f, sn = 0.0f;
+#pragma unroll
+    for (int T = 0; T < FW / 16; ++T)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float ea = __builtin_amdgcn_exp2f(u[T][e] - mx);
+            const float eb = __builtin_amdgcn_exp2f(mn - u[T][e]);
+            u[T][e] = ea;
+            en[T][e] = eb;
+            sp += ea;
+            sn += eb;
+        }
+    sp += __shfl_xor(sp, 16, 64);
+    sn += __shfl_xor(sn, 16, 64);
+    sp += __shfl_xor(sp, 32, 64);
+    sn += __shfl_xor(sn, 32, 64);
+    const bool valid = 16 * wv + n16 < nc;
+    const float ip = valid ? __builtin_amdgcn_rcpf(sp) : 0.0f;
+    const float in = valid ? __builtin_amdgcn_rcpf(sn) : 0.0f;
+    const int prow_t = 16 * wv + n16;
+    uint16_t* const prow = Pb + prow_t * F;
+    const int psw = lds_piece_swizzle<F / 4>(prow_t);
+#pragma unroll
+    for (int T = 0; T < FW / 16; ++T) {
+        uint16_t hp[4], hn[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float pp_ = u[T][e] * ip, pn = en[T][e] * in;
+            zl[4 * T + e] += pp_;
+            zl[FW / 4 + 4 * T + e] += pn;
+            hp[e] = bf16_bits(pp_);
+            hn[e] = bf16_bits(pn);
+        }
+        // features 16 T + 4 q .. + 3 are piece 4 T + q (+ FW / 4 for the - half)
+        const int jp = 4 * T + q, jn = FW / 4 + jp;
+        *reinterpret_cast<uint2*>(prow + ((jp ^ psw) << 2)) =
+            make_uint2(hp[0] | (uint32_t(hp[1]) << 16), hp[2] | (uint32_t(hp[3]) << 16));
+        *reinterpret_cast<uint2*>(prow + ((jn ^ psw) << 2)) =
+            make_uint2(hn[0] | (uint32_t(hn[1]) << 16), hn[2] | (uint32_t(hn[3]) << 16));
+    }
+}
+
+// Second half of chunk c: dS = phi(K)^T V over the chunk, this wave's state
+// rows and value columns, accumulated into its state tiles.
+template <int D, int FW>
+__device__ __forceinline__ void prefill_ds(int c, int tid, const uint16_t* Vs, const uint16_t* Ps,
+                                           f32x16 (&st)[PCfg<D, FW>::RW / 32])
+{
+    using P = PCfg<D, FW>;
+    constexpr int F = P::F, NC = P::NC, CT = P::CT, RW = P::RW;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int cs = wv % NC, r0 = (wv / NC) * RW;
+    const uint16_t* const Vb = Vs + (P::NBUF == 2 ? (c & 1) : 0) * (CT * D);
+    const uint16_t* const Pb = Ps + (P::NBUF == 2 ? (c & 1) : 0) * (CT * F);
+#pragma unroll
+    for (int kb = 0; kb < CT / 16; ++kb) {
+        const bf16x8 bv = vt_frag_ps<D / 4>(Vb, 32 * cs, kb, lane);
+#pragma unroll
+        for (int ft = 0; ft < RW / 32; ++ft) st[ft] = mfma32(vt_frag_ps<F / 4>(Pb, r0 + 32 * ft, kb, lane), bv, st[ft]);
+    }
+}
+
+template <int D, int FW>
+__global__ __launch_bounds__(64 * (2 * FW * (D / 32) > 512 ? 8 : 4)) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_mfma_kernel(CommitArgs a)
+{
+    using P = PCfg<D, FW>;
+    constexpr int F = P::F, NC = P::NC, NT = P::NT, CT = P::CT, RW = P::RW, KS = P::KS, VQ = P::VQ;
     const int pair = blockIdx.x;
     const int r = pair / a.H, h = pair % a.H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int ln = lane & 31, g = lane >> 5;
+    const int cs = wv % NC, r0 = (wv / NC) * RW;
+    const int n16 = lane & 15, q = lane >> 4;
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[32 * C::RS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[32 * C::RS];
-    __shared__ __attribute__((aligned(16))) uint16_t Ws[FW * C::RS];
-    __shared__ __attribute__((aligned(16))) float Pt[F * C::PS];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[P::LDS];
+    uint16_t* const Vs = reinterpret_cast<uint16_t*>(smem);
+    uint16_t* const Ps = Vs + P::NBUF * CT * D;
+    uint16_t* const Ws = Ps + P::NBUF * CT * F;
+    float* const Zr = reinterpret_cast<float*>(smem);
 
     const int slot = a.slot_ids[r];
     if (slot < 0 || slot >= a.num_slots) return;
@@ -594,106 +852,95 @@ __global__ __launch_bounds__(64 * (D / 32)) void prefill_mfma_kernel(CommitArgs 
     if (n == 0) return;
     float* rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * F;
     const int64_t base = first_row * a.ks.tok + static_cast<int64_t>(h) * a.ks.head;
-    const uint16_t* kb = static_cast<const uint16_t*>(a.k) + base;
-    const uint16_t* vb = static_cast<const uint16_t*>(a.v) + base;
-    const int tok = static_cast<int>(a.ks.tok);
+    PrefillPair<D, FW> pp;
+    pp.kbase = static_cast<const uint16_t*>(a.k) + base;
+    pp.vbase = static_cast<const uint16_t*>(a.v) + base;
+    pp.tok64 = a.ks.tok;
+    pp.tok = static_cast<int>(a.ks.tok);
+    pp.n = n;
+    pp.nchunks = (n + CT - 1) / CT;
 
-    RowChunks<D, C::NT> kc, vc;
     {
-        WChunks<D, FW, C::NT> wc;
-        wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
-        kc.load(kb, tok, n < 32 ? n : 32, tid);
-        vc.load(vb, tok, n < 32 ? n : 32, tid);
-        wc.template store_rows<C::RS>(Ws, tid);
-    }
-    f32x4 sv[C::NSL];
-    load_state_slice(rec + wv * F * 32, lane, sv);
-    float zacc[(F + C::NT - 1) / C::NT];
+        const uint16_t* w = static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh;
+        constexpr int NWC = FW * P::VC / NT;  // 16-byte chunks of W per thread
+        u32x4 wr[NWC];
 #pragma unroll
-    for (int i = 0; i < (F + C::NT - 1) / C::NT; ++i) zacc[i] = 0.0f;
-
-    const int nchunks = (n + 31) / 32;
-    for (int c = 0; c < nchunks; ++c) {
-        const int nc = n - 32 * c < 32 ? n - 32 * c : 32;
-        __syncthreads();  // every wave is done with the previous chunk's LDS data
-        kc.template store_rows<C::RS>(Ks, tid);
-        vc.template store_rows<C::RS>(Vs, tid);
-        __syncthreads();
-        if (c + 1 < nchunks) {
-            const int rem = n - 32 * (c + 1);
-            kc.load(kb + static_cast<int64_t>(32 * (c + 1)) * a.ks.tok, tok, rem < 32 ? rem : 32, tid);
-            vc.load(vb + static_cast<int64_t>(32 * (c + 1)) * a.ks.tok, tok, rem < 32 ? rem : 32, tid);
+        for (int i = 0; i < NWC; ++i) {
+            const int idx = tid + i * NT, row = idx / P::VC, ch = idx % P::VC;
+            wr[i] = *reinterpret_cast<const u32x4*>(w + row * D + ch * 8);
         }
-
-        // phi(k_t) for token ln, normalised; tokens beyond the chunk give zero
-        f32x16 u[FW / 32];
-        feature_logits<D, FW, C::RS>(Ws, Ks, ln, g, u);
-        float mx, mn;
-        logit_range<FW>(u, mx, mn);
-        float sp = 0.0f, sn = 0.0f;
 #pragma unroll
-        for (int T = 0; T < FW / 32; ++T)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                sp += __expf(u[T][v] - mx);
-                sn += __expf(mn - u[T][v]);
-            }
-        sp += __shfl_xor(sp, 32, 64);
-        sn += __shfl_xor(sn, 32, 64);
-        const float ip = ln < nc ? 1.0f / sp : 0.0f;
-        const float in = ln < nc ? 1.0f / sn : 0.0f;
-        // phi(K)^T rows of the feature tiles T = wv, wv + NW, ... (disjoint across waves)
-#pragma unroll
-        for (int T = 0; T < FW / 32; ++T) {
-            if (T % C::NW != wv) continue;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int fw = 32 * T + 8 * (v >> 2) + 4 * g + (v & 3);
-                Pt[fw * C::PS + ln] = __expf(u[T][v] - mx) * ip;
-                Pt[(FW + fw) * C::PS + ln] = __expf(mn - u[T][v]) * in;
-            }
-        }
-        __syncthreads();
-
-        // dS = phi(K)^T V over this wave's 32 columns, added into the slice
-#pragma unroll
-        for (int ft = 0; ft < F / 32; ++ft) {
-            f32x16 acc = f32x16{};
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) {
-                const float* pr = Pt + (32 * ft + ln) * C::PS + 16 * kb2 + 4 * g;
-                const f32x4 p0 = *reinterpret_cast<const f32x4*>(pr);
-                const f32x4 p1 = *reinterpret_cast<const f32x4*>(pr + 8);
-                bf16x8 ap;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ap[e] = static_cast<__bf16>(p0[e]);
-                    ap[4 + e] = static_cast<__bf16>(p1[e]);
-                }
-                acc = mfma32(ap, vt_frag<C::RS>(Vs, 32 * wv, kb2, lane), acc);
-            }
-#pragma unroll
-            for (int v = 0; v < 16; ++v) sv[4 * ft + (v >> 2)][v & 3] += acc[v];
-        }
-        // dZ in fp32, fixed summation order
-#pragma unroll
-        for (int i = 0; i < (F + C::NT - 1) / C::NT; ++i) {
-            const int f = tid + i * C::NT;
-            if (f < F) {
-                float z = 0.0f;
-#pragma unroll
-                for (int t = 0; t < 32; ++t) z += Pt[f * C::PS + t];
-                zacc[i] += z;
-            }
+        for (int i = 0; i < NWC; ++i) {
+            // chunk ch of row 16 T + n16 is k-group q = ch / KS, k-step ks = ch % KS
+            const int idx = tid + i * NT, row = idx / P::VC, ch = idx % P::VC;
+            const int blk = (ch % KS) * (FW / 16) + row / 16, slot = (ch / KS) * 16 + row % 16;
+            *reinterpret_cast<u32x4*>(Ws + (blk * 64 + slot) * 8) = wr[i];
         }
     }
-    f32x4* dst = reinterpret_cast<f32x4*>(rec + wv * F * 32) + lane;
+
+    // state tiles: rows r0 + 32 ft + (C layout), columns 32 cs + lane % 32
+    f32x16 st[RW / 32];
+    const f32x4* const sp4 = reinterpret_cast<const f32x4*>(rec + 32 * (cs * F + r0)) + lane;
 #pragma unroll
-    for (int t = 0; t < C::NSL; ++t) __builtin_nontemporal_store(sv[t], dst + t * 64);
+    for (int ft = 0; ft < RW / 32; ++ft)
 #pragma unroll
-    for (int i = 0; i < (F + C::NT - 1) / C::NT; ++i) {
-        const int f = tid + i * C::NT;
-        if (f < F) rec[D * F + f] += zacc[i];
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 x = __builtin_nontemporal_load(sp4 + (4 * ft + i) * 64);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[ft][4 * i + e] = x[e];
+        }
+    float zl[FW / 2];  // this lane's token slot: features 16 T + 4 q + e of the + half, then the - half
+#pragma unroll
+    for (int i = 0; i < FW / 2; ++i) zl[i] = 0.0f;
+
+    // one register set: chunk c's loads are issued while chunk c - 1's phi is
+    // computed, and consumed by chunk c's
+    u32x4 vr[VQ];
+    bf16x8 kf[KS];
+    prefill_load_v(pp, 0, tid, vr);
+    prefill_load_k(pp, 0, wv, n16, q, kf);
+    if constexpr (P::NBUF == 2) {
+        __syncthreads();  // W rows visible to every wave
+        prefill_phi(pp, 0, tid, Vs, Ps, Ws, vr, kf, zl);
+        __syncthreads();
+        for (int c = 0; c < pp.nchunks; ++c) {
+            prefill_phi(pp, c + 1, tid, Vs, Ps, Ws, vr, kf, zl);
+            prefill_ds<D, FW>(c, tid, Vs, Ps, st);
+            __syncthreads();
+        }
+    } else {
+        // one buffer: phi and dS of a chunk between barriers
+        for (int c = 0; c < pp.nchunks; ++c) {
+            __syncthreads();  // W rows staged; every wave is done with the previous chunk
+            prefill_phi(pp, c, tid, Vs, Ps, Ws, vr, kf, zl);
+            __syncthreads();
+            prefill_ds<D, FW>(c, tid, Vs, Ps, st);
+        }
+        __syncthreads();
+    }
+
+    f32x4* const dst = reinterpret_cast<f32x4*>(rec + 32 * (cs * F + r0)) + lane;
+#pragma unroll
+    for (int ft = 0; ft < RW / 32; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 x = {st[ft][4 * i], st[ft][4 * i + 1], st[ft][4 * i + 2], st[ft][4 * i + 3]};
+            __builtin_nontemporal_store(x, dst + (4 * ft + i) * 64);
+        }
+
+    // Z: the token slots' fp32 partials, reduced in a fixed order
+    float* const zrow = Zr + (16 * wv + n16) * F + 4 * q;
+#pragma unroll
+    for (int T = 0; T < FW / 16; ++T) {
+        *reinterpret_cast<f32x4*>(zrow + 16 * T) = f32x4{zl[4 * T], zl[4 * T + 1], zl[4 * T + 2], zl[4 * T + 3]};
+        *reinterpret_cast<f32x4*>(zrow + FW + 16 * T) =
+            f32x4{zl[FW / 4 + 4 * T], zl[FW / 4 + 4 * T + 1], zl[FW / 4 + 4 * T + 2], zl[FW / 4 + 4 * T + 3]};
+    }
+    __syncthreads();
+    for (int f = tid; f < F; f += NT) {
+        float z = 0.0f;
+        for (int sl = 0; sl < CT; ++sl) z += Zr[sl * F + f];
+        rec[D * F + f] += z;
     }
 }
 
@@ -741,11 +988,11 @@ static hipError_t forward_by_fw(const ForwardArgs& a, hipStream_t s)
 template <int D>
 static hipError_t prefill_by_fw(const CommitArgs& a, hipStream_t s)
 {
-    const dim3 grid(static_cast<uint32_t>(a.R * a.H)), block(64 * (D / 32));
+    const dim3 grid(static_cast<uint32_t>(a.R * a.H));
     switch (a.FW) {
-        case 32: hipLaunchKernelGGL((prefill_mfma_kernel<D, 32>), grid, block, 0, s, a); break;
-        case 64: hipLaunchKernelGGL((prefill_mfma_kernel<D, 64>), grid, block, 0, s, a); break;
-        case 128: hipLaunchKernelGGL((prefill_mfma_kernel<D, 128>), grid, block, 0, s, a); break;
+        case 32: hipLaunchKernelGGL((prefill_mfma_kernel<D, 32>), grid, dim3(PCfg<D, 32>::NT), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((prefill_mfma_kernel<D, 64>), grid, dim3(PCfg<D, 64>::NT), 0, s, a); break;
+        case 128: hipLaunchKernelGGL((prefill_mfma_kernel<D, 128>), grid, dim3(PCfg<D, 128>::NT), 0, s, a); break;
         default: return hipErrorNotSupported;
     }
     return hipGetLastError();
@@ -781,7 +1028,8 @@ hipError_t launch_forward_mfma(const ForwardArgs& a, hipStream_t s)
 hipError_t launch_prefill_mfma(const CommitArgs& a, hipStream_t s)
 {
     if (a.io != BHA_BF16 || a.seq_offsets == nullptr) return hipErrorNotSupported;
-    if (!small_token_stride(a.ks.tok)) return hipErrorNotSupported;
+    // in-chunk offsets (up to 128 rows) are 32-bit
+    if (a.ks.tok >= (int64_t(1) << 23)) return hipErrorNotSupported;
     if (a.d == 128) return prefill_by_fw<128>(a, s);
     if (a.d == 64) return prefill_by_fw<64>(a, s);
     return hipErrorNotSupported;
