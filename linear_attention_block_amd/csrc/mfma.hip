@@ -121,39 +121,24 @@ __device__ __forceinline__ void load_state_slice(const float* rec_slice, int lan
 
 // A thread's share of the 16-byte chunks of a ROWS x D bf16 token block,
 // held in registers between the global loads and the LDS writes so that all
-// global loads of a work-group can be issued back to back. Rows >= nrows are
-// zero.
+// global loads of a work-group can be issued back to back.
 template <int D, int NT, int ROWS = 32>
 struct RowChunks {
     static constexpr int CH = D / 8;
     static constexpr int N = ROWS * CH / NT;
-    uint4 v[N];
+    u32x4 v[N];
 
     // tok: token stride in elements; the launcher guarantees ROWS * tok fits
-    // in 31 bits. Rows >= nrows read row nrows - 1 (always present) and are
-    // zeroed, so the loads need no divergent branches.
+    // in 31 bits. Rows >= nrows read row nrows - 1 (always present): callers
+    // give those rows zero weight. Nothing touches the registers until they
+    // are stored, so the loads stay in flight until then.
     __device__ __forceinline__ void load(const uint16_t* src, int tok, int nrows, int tid)
     {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
             const int tr = t < nrows ? t : nrows - 1;
-            const uint4 x = *reinterpret_cast<const uint4*>(src + (tr * tok + ch * 8));
-            const bool keep = t < nrows;
-            v[i] = make_uint4(keep ? x.x : 0u, keep ? x.y : 0u, keep ? x.z : 0u, keep ? x.w : 0u);
-        }
-    }
-    // the same rows without the zeroing: rows >= nrows hold a copy of row
-    // nrows - 1, for callers whose weights for those rows are zero. The loaded
-    // registers are not touched until they are stored, so the loads stay in
-    // flight until then.
-    __device__ __forceinline__ void load_clamped(const uint16_t* src, int tok, int nrows, int tid)
-    {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
-            const int tr = t < nrows ? t : nrows - 1;
-            v[i] = *reinterpret_cast<const uint4*>(src + (tr * tok + ch * 8));
+            v[i] = *reinterpret_cast<const u32x4*>(src + (tr * tok + ch * 8));
         }
     }
     // row-major copy, row stride RS
@@ -163,7 +148,7 @@ struct RowChunks {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
-            *reinterpret_cast<uint4*>(dst + t * RS + ch * 8) = v[i];
+            *reinterpret_cast<u32x4*>(dst + t * RS + ch * 8) = v[i];
         }
     }
     // transposed copy dst[c][t], row stride VS
@@ -173,7 +158,7 @@ struct RowChunks {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
-            const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            const uint32_t w4[4] = {v[i][0], v[i][1], v[i][2], v[i][3]};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 dst[(ch * 8 + 2 * e) * VS + t] = static_cast<uint16_t>(w4[e] & 0xFFFFu);
@@ -188,14 +173,14 @@ template <int D, int FW, int NT>
 struct WChunks {
     static constexpr int CH = D / 8;
     static constexpr int N = FW * CH / NT;
-    uint4 v[N];
+    u32x4 v[N];
 
     __device__ __forceinline__ void load(const uint16_t* src, int tid)
     {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT, j = idx / CH, ch = idx % CH;
-            v[i] = *reinterpret_cast<const uint4*>(src + j * D + ch * 8);
+            v[i] = *reinterpret_cast<const u32x4*>(src + j * D + ch * 8);
         }
     }
     template <int RS>
@@ -204,7 +189,7 @@ struct WChunks {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT, j = idx / CH, ch = idx % CH;
-            *reinterpret_cast<uint4*>(dst + j * RS + ch * 8) = v[i];
+            *reinterpret_cast<u32x4*>(dst + j * RS + ch * 8) = v[i];
         }
     }
 };
@@ -264,18 +249,19 @@ struct PairOperands {
     f32x4 z;
     const float* rec;  // the pair's state record; nullptr for an out-of-range slot
 
-    __device__ __forceinline__ void load(const ForwardArgs& a, int p, int tid)
+    // slot: the pair's slot id, read one pair ahead by the caller so that
+    // waiting for it does not drain the loads issued since
+    __device__ __forceinline__ void load(const ForwardArgs& a, int p, int slot, int tid)
     {
         const int r = p / a.H, h = p % a.H;
-        const int slot = a.slot_ids[r];
-        rec = nullptr;
-        if (slot < 0 || slot >= a.num_slots) return;
-        rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * C::F;
         const int64_t base = static_cast<int64_t>(r) * a.qs.req + static_cast<int64_t>(h) * a.qs.head;
         const int tok = static_cast<int>(a.qs.tok);
         q.load(static_cast<const uint16_t*>(a.q) + base, tok, a.B, tid);
         k.load(static_cast<const uint16_t*>(a.k) + base, tok, a.B, tid);
         v.load(static_cast<const uint16_t*>(a.v) + base, tok, a.B, tid);
+        rec = nullptr;
+        if (slot < 0 || slot >= a.num_slots) return;
+        rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * C::F;
         z = reinterpret_cast<const f32x4*>(rec + D * C::F)[tid % (C::F / 4)];
     }
 
@@ -457,19 +443,24 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
         wc.template store_rows<C::RS>(sm.Ws, tid);
     }
 
+    // slot ids run one pair ahead of the operand loads (index clamped in range)
+    auto slot_of = [&](int pp) { return a.slot_ids[(pp < npairs ? pp : npairs - 1) / a.H]; };
     PairOperands<D, FW> op;
     f32x4 sv[C::NSL];
-    op.load(a, p, tid);
+    op.load(a, p, slot_of(p), tid);
     if (op.rec) load_state_slice(op.rec + wv * F * 32, lane, sv);
+    int slot_next = slot_of(p + G);
     for (;;) {
         const int pn = p + G;
         const bool more = pn < npairs;
         const bool valid = op.rec != nullptr;
         const int r = p / a.H;
+        const int slot_after = slot_of(pn + G);
         __syncthreads();  // every wave is done with the previous pair's LDS operands
         if (valid) op.store(sm, tid);
         __syncthreads();
-        if (more) op.load(a, pn, tid);
+        if (more) op.load(a, pn, slot_next, tid);
+        slot_next = slot_after;
         f32x16 lacc, vacc;
         float sp, sn, den, m, l;
         if (valid) {
@@ -517,20 +508,18 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
     float* Pt = reinterpret_cast<float*>(WP);
 
     const int B = a.B;
+    // K, V and W do not depend on the slot: their loads go out first
     const int slot = a.slot_ids[r];
-    if (slot < 0 || slot >= a.num_slots) return;
-    float* rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * F;
-
     const int64_t base = static_cast<int64_t>(r) * a.ks.req + static_cast<int64_t>(h) * a.ks.head;
     RowChunks<D, C::NT> kc, vc;
     WChunks<D, FW, C::NT> wc;
     kc.load(static_cast<const uint16_t*>(a.k) + base, static_cast<int>(a.ks.tok), B, tid);
     vc.load(static_cast<const uint16_t*>(a.v) + base, static_cast<int>(a.ks.tok), B, tid);
     wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
-    __builtin_amdgcn_sched_barrier(0);
+    if (slot < 0 || slot >= a.num_slots) return;
+    float* rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * F;
     f32x4 sv[C::NSL];
     load_state_slice(rec + wv * F * 32, lane, sv);
-    __builtin_amdgcn_sched_barrier(0);
     kc.template store_rows<C::RS>(Ks, tid);
     vc.template store_transposed<C::VS>(Vt, tid);
     wc.template store_rows<C::RS>(Ws, tid);
@@ -660,6 +649,40 @@ __device__ __forceinline__ bf16x8 w_frag(const uint16_t* Ws, int T, int ks, int 
     return lds_frag(Ws + ((ks * (FW / 16) + T) * 64 + lane) * 8);
 }
 
+// All-reductions over the lane pairs (L, L ^ 16) and (L, L ^ 32) with the
+// gfx950 row-swap instructions (VALU, no LDS round trip): swapping a value
+// with itself leaves each lane holding its own and its partner's.
+__device__ __forceinline__ float max_xor16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float min_xor16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float min_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Per-pair constants of the prefill loop.
 template <int D, int FW>
 struct PrefillPair {
@@ -741,7 +764,7 @@ __device__ __forceinline__ void prefill_phi(const PrefillPair<D, FW>& pp, int c,
     prefill_store_v<D, FW>(Vb, tid, vr);
     if (c + PD < pp.nchunks) prefill_load_v(pp, c + PD, tid, vr);
 
-    // feature logits of this wave's 16 tokens (base 2)
+    // feature logits of this wave's 16 tokens
     f32x4 u[FW / 16];
 #pragma unroll
     for (int T = 0; T < FW / 16; ++T) u[T] = f32x4{};
@@ -750,36 +773,33 @@ __device__ __forceinline__ void prefill_phi(const PrefillPair<D, FW>& pp, int c,
 #pragma unroll
         for (int T = 0; T < FW / 16; ++T) u[T] = mfma16(w_frag<D, FW>(Ws, T, ks, lane), kf[ks], u[T]);
     if (c + PD < pp.nchunks) prefill_load_k(pp, c + PD, wv, n16, q, kf);
+    // per-token extremes and sums over the four k-group lanes (L, L ^ 16,
+    // L ^ 32, L ^ 48); the exponentials are base 2 of the scaled differences
     float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
     for (int T = 0; T < FW / 16; ++T)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            u[T][e] *= kLog2e;
             mx = fmaxf(mx, u[T][e]);
             mn = fminf(mn, u[T][e]);
         }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mn = fminf(mn, __shfl_xor(mn, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    mn = fminf(mn, __shfl_xor(mn, 32, 64));
+    mx = max_xor32(max_xor16(mx)) * kLog2e;
+    mn = min_xor32(min_xor16(mn)) * kLog2e;
     f32x4 en[FW / 16];
     float sp = 0.0f, sn = 0.0f;
 #pragma unroll
     for (int T = 0; T < FW / 16; ++T)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float ea = __builtin_amdgcn_exp2f(u[T][e] - mx);
-            const float eb = __builtin_amdgcn_exp2f(mn - u[T][e]);
+            const float ea = __builtin_amdgcn_exp2f(fmaf(u[T][e], kLog2e, -mx));
+            const float eb = __builtin_amdgcn_exp2f(fmaf(u[T][e], -kLog2e, mn));
             u[T][e] = ea;
             en[T][e] = eb;
             sp += ea;
             sn += eb;
         }
-    sp += __shfl_xor(sp, 16, 64);
-    sn += __shfl_xor(sn, 16, 64);
-    sp += __shfl_xor(sp, 32, 64);
-    sn += __shfl_xor(sn, 32, 64);
+    sp = sum_xor32(sum_xor16(sp));
+    sn = sum_xor32(sum_xor16(sn));
     const bool valid = 16 * wv + n16 < nc;
     const float ip = valid ? __builtin_amdgcn_rcpf(sp) : 0.0f;
     const float in = valid ? __builtin_amdgcn_rcpf(sn) : 0.0f;
@@ -900,6 +920,7 @@ void prefill_mfma_kernel(CommitArgs a)
     prefill_load_v(pp, 0, tid, vr);
     prefill_load_k(pp, 0, wv, n16, q, kf);
     if constexpr (P::NBUF == 2) {
+        // chunk c lives in LDS buffer c % 2
         __syncthreads();  // W rows visible to every wave
         prefill_phi(pp, 0, tid, Vs, Ps, Ws, vr, kf, zl);
         __syncthreads();
