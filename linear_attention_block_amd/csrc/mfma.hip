@@ -112,11 +112,11 @@ struct Cfg {
 // (n, g) = (lane % 32, lane / 32) the features 8t + 4g .. 8t + 4g + 3 of
 // column 32w + n.
 template <int NSL>
-__device__ __forceinline__ void load_state_slice(const float* rec_slice, int lane, f32x4 (&sv)[NSL])
+__device__ __forceinline__ void load_state_slice(const float* rec_slice, int lane, f32x4 (&sv)[NSL], int live = 1)
 {
-    const f32x4* p = reinterpret_cast<const f32x4*>(rec_slice) + lane;
+    const f32x4* p = reinterpret_cast<const f32x4*>(rec_slice) + lane * live;
 #pragma unroll
-    for (int t = 0; t < NSL; ++t) sv[t] = __builtin_nontemporal_load(p + t * 64);
+    for (int t = 0; t < NSL; ++t) sv[t] = __builtin_nontemporal_load(p + t * 64 * live);
 }
 
 // A thread's share of the 16-byte chunks of a ROWS x D bf16 token block,
@@ -132,13 +132,15 @@ struct RowChunks {
     // in 31 bits. Rows >= nrows read row nrows - 1 (always present): callers
     // give those rows zero weight. Nothing touches the registers until they
     // are stored, so the loads stay in flight until then.
-    __device__ __forceinline__ void load(const uint16_t* src, int tok, int nrows, int tid)
+    // live = 0 points every lane at src itself (a placeholder load of one
+    // 16-byte location, for loops that keep their load sequence fixed).
+    __device__ __forceinline__ void load(const uint16_t* src, int tok, int nrows, int tid, int live = 1)
     {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
             const int tr = t < nrows ? t : nrows - 1;
-            v[i] = *reinterpret_cast<const u32x4*>(src + (tr * tok + ch * 8));
+            v[i] = *reinterpret_cast<const u32x4*>(src + (tr * tok + ch * 8) * live);
         }
     }
     // row-major copy, row stride RS
@@ -247,22 +249,24 @@ struct PairOperands {
     using C = Cfg<D, FW>;
     RowChunks<D, C::NT> q, k, v;
     f32x4 z;
-    const float* rec;  // the pair's state record; nullptr for an out-of-range slot
+    const float* rec;  // the state record the slice loads read (slot 0's for an out-of-range slot)
+    bool valid;        // the slot id is in range
 
-    // slot: the pair's slot id, read one pair ahead by the caller so that
-    // waiting for it does not drain the loads issued since
-    __device__ __forceinline__ void load(const ForwardArgs& a, int p, int slot, int tid)
+    // Issues the same loads whatever the pair: the loop's memory operations
+    // are then a fixed sequence and every wait covers exactly the loads it
+    // needs. slot: the pair's slot id, read one pair ahead by the caller;
+    // live = 0 collapses the loads onto one location (no next pair).
+    __device__ __forceinline__ void load(const ForwardArgs& a, int p, int slot, int tid, int live = 1)
     {
         const int r = p / a.H, h = p % a.H;
         const int64_t base = static_cast<int64_t>(r) * a.qs.req + static_cast<int64_t>(h) * a.qs.head;
         const int tok = static_cast<int>(a.qs.tok);
-        q.load(static_cast<const uint16_t*>(a.q) + base, tok, a.B, tid);
-        k.load(static_cast<const uint16_t*>(a.k) + base, tok, a.B, tid);
-        v.load(static_cast<const uint16_t*>(a.v) + base, tok, a.B, tid);
-        rec = nullptr;
-        if (slot < 0 || slot >= a.num_slots) return;
-        rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * C::F;
-        z = reinterpret_cast<const f32x4*>(rec + D * C::F)[tid % (C::F / 4)];
+        q.load(static_cast<const uint16_t*>(a.q) + base, tok, a.B, tid, live);
+        k.load(static_cast<const uint16_t*>(a.k) + base, tok, a.B, tid, live);
+        v.load(static_cast<const uint16_t*>(a.v) + base, tok, a.B, tid, live);
+        valid = slot >= 0 && slot < a.num_slots;
+        rec = a.state + (static_cast<int64_t>(valid ? slot : 0) * a.H + h) * static_cast<int64_t>(D + 1) * C::F;
+        z = reinterpret_cast<const f32x4*>(rec + D * C::F)[(tid % (C::F / 4)) * live];
     }
 
     __device__ __forceinline__ void store(FwdLds<D, FW>& sm, int tid) const
@@ -390,12 +394,14 @@ __device__ __forceinline__ f32x16 block_softmax_pv(const ForwardArgs& a, const F
 
 // Merge of the two branches for token ln and store of this wave's 32 columns.
 __device__ __forceinline__ void merge_store(const ForwardArgs& a, const f32x16& vacc, const f32x16& lacc, float gamma,
-                                            float m, float l, float den, float sn, int r, int h, int wv, int ln, int g)
+                                            float m, float l, float den, float sn, int r, int h, int wv, int ln, int g,
+                                            bool valid)
 {
     if (ln >= a.B) return;
     float al, be;
     merge_weights(gamma, m, al, be);
-    const float inv = __builtin_amdgcn_rcpf(al * l + be * den);
+    // an out-of-range slot stores NaN rows
+    const float inv = valid ? __builtin_amdgcn_rcpf(al * l + be * den) : __builtin_nanf("");
     const float bl = be * __builtin_amdgcn_rcpf(sn);
     uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
                      static_cast<int64_t>(h) * a.os.head + (ln * static_cast<int>(a.os.tok) + 32 * wv + 4 * g);
@@ -445,42 +451,45 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
 
     // slot ids run one pair ahead of the operand loads (index clamped in range)
     auto slot_of = [&](int pp) { return a.slot_ids[(pp < npairs ? pp : npairs - 1) / a.H]; };
+    const int count = (npairs - p + G - 1) / G;  // pairs of this work-group
     PairOperands<D, FW> op;
     f32x4 sv[C::NSL];
+    // issue order as in the loop (operands, then the slice, then the next
+    // slot id), so the waits at the loop head are the same from either side
     op.load(a, p, slot_of(p), tid);
-    if (op.rec) load_state_slice(op.rec + wv * F * 32, lane, sv);
+    __builtin_amdgcn_sched_barrier(0);
+    load_state_slice(op.rec + wv * F * 32, lane, sv);
+    __builtin_amdgcn_sched_barrier(0);
     int slot_next = slot_of(p + G);
-    for (;;) {
-        const int pn = p + G;
-        const bool more = pn < npairs;
-        const bool valid = op.rec != nullptr;
+    for (int k = 0; k < count; ++k) {
+        // the last pair issues placeholder loads, so every trip runs the same
+        // memory operations
+        const int live = k + 1 < count ? 1 : 0;
+        const int pn = live ? p + G : p;
+        const bool valid = op.valid;
         const int r = p / a.H;
-        const int slot_after = slot_of(pn + G);
+        int slot_after = slot_of(pn + G);
         __syncthreads();  // every wave is done with the previous pair's LDS operands
-        if (valid) op.store(sm, tid);
+        op.store(sm, tid);
         __syncthreads();
-        if (more) op.load(a, pn, slot_next, tid);
-        slot_next = slot_after;
+        op.load(a, pn, __builtin_amdgcn_readfirstlane(slot_next), tid, live);
         f32x16 lacc, vacc;
         float sp, sn, den, m, l;
-        if (valid) {
+        {
             bf16x8 pb[F / 16];
             phi_operands<D, FW>(sm, ln, g, pb, sp, sn, den);
             vacc = block_softmax_pv<D, FW>(a, sm, wv, ln, g, m, l);
             lacc = linear_read<D, FW>(sv, pb, sp, sn);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (more && op.rec) load_state_slice(op.rec + wv * F * 32, lane, sv);
+        load_state_slice(op.rec + wv * F * 32, lane, sv, live);
         __builtin_amdgcn_sched_barrier(0);
-        if (valid) {
-            merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, ln, g);
-        } else {
-            uint16_t* out = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
-                            static_cast<int64_t>(h) * a.os.head;
-            for (int idx = tid; idx < a.B * D; idx += C::NT)
-                out[static_cast<int64_t>(idx / D) * a.os.tok + idx % D] = 0x7FC0u;  // NaN
-        }
-        if (!more) break;
+        merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, ln, g, valid);
+        // the slot id read at the top of this trip crosses the loop in a
+        // vector register: its wait lands here, a whole trip after the load,
+        // and covers no load issued since
+        asm volatile("" : "+v"(slot_after));
+        slot_next = slot_after;
         p = pn;
     }
 }
