@@ -3,9 +3,10 @@
 
 One step is one block cycle of the model's block-hybrid layers on a
 continuous-batching decode batch: for each of the 32 denoising steps of the
-active block every layer runs ``bha_block_forward`` over all requests and heads,
-and then every layer folds the finished block into its state with
-``bha_state_commit``. Each layer instance has its own state pool, W and gate,
+active block every layer runs ``bha_block_forward`` over all requests and heads;
+the last step is ``bha_block_forward_commit``, which also folds the finished
+block into the states in the same pass (``--separate-commit``: 32 plain
+forwards, then ``bha_state_commit``). Each layer instance has its own state pool, W and gate,
 as the model's six block-hybrid layers do, so consecutive forwards of one layer
 do not find its 270 MB state in the 256 MB Infinity Cache.
 
@@ -50,6 +51,13 @@ def commit_bytes(R, H, d, FW, B, es=2):
     the state record read and written back, K and V read; W once per head."""
     F = 2 * FW
     return R * H * (2 * (d * F * 4 + F * 4) + 2 * B * d * es) + H * FW * d * es
+
+
+def forward_commit_bytes(R, H, d, FW, B, es=2):
+    """Algorithmic HBM bytes of one bha_block_forward_commit launch: the
+    forward's bytes plus the state record written back (every request commits)."""
+    F = 2 * FW
+    return forward_bytes(R, H, d, FW, B, es) + R * H * (d * F * 4 + F * 4)
 
 
 def prefill_bytes(T, R, H, d, FW, es=2):
@@ -151,6 +159,9 @@ def main() -> int:
     ap.add_argument("--denoise", type=int, default=32, help="denoising forwards per block")
     ap.add_argument("--cpu-sample-requests", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-commit", action="store_true",
+                    help="run every denoising step as a plain forward and commit with bha_state_commit "
+                         "(default: the last step of the block is bha_block_forward_commit)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -202,7 +213,8 @@ def main() -> int:
         out = torch.empty_like(q)
         layers.append(dict(w=w, gamma=gamma, state=state, q=q, k=k, v=v, out=out,
                            fwd=bha.prepare_forward(q, k, v, w, gamma, state, slots, out),
-                           com=bha.prepare_commit(k, v, w, state, slots)))
+                           com=(bha.prepare_commit(k, v, w, state, slots) if args.separate_commit else
+                                bha.prepare_forward_commit(q, k, v, w, gamma, state, slots, out))))
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     pre_avg = sum(prefill_ms) / len(prefill_ms) * 1e-3
@@ -212,13 +224,16 @@ def main() -> int:
     log(f"prefill: avg {pre_avg * 1e6:.1f} us/launch over {nl} layers, {T / pre_avg / 1e6:.1f} M tokens/s, "
         f"{pb / pre_avg / 1e9:.0f} GB/s algorithmic ({pb / 1e9:.2f} GB/launch)")
 
-    n_fwd, n_com = nd * nl, nl
+    # a block cycle: nd denoising steps in every layer; the last one either is
+    # the fused forward + commit, or a plain forward followed by a commit
+    nd_plain = nd if args.separate_commit else nd - 1
+    n_fwd, n_com = nd_plain * nl, nl
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps * (n_fwd + n_com))]
 
     def step(evs):
         it = iter(evs) if evs is not None else None
-        for _ in range(nd):
+        for _ in range(nd_plain):
             for lay in layers:
                 if it is not None:
                     e0, e1 = next(it)
@@ -253,13 +268,15 @@ def main() -> int:
         com_ms += [a.elapsed_time(b) for a, b in blk[n_fwd:]]
     fwd_avg = sum(fwd_ms) / len(fwd_ms) * 1e-3
     com_avg = sum(com_ms) / len(com_ms) * 1e-3
-    fb, cb = forward_bytes(R, H, d, FW, B), commit_bytes(R, H, d, FW, B)
+    fb = forward_bytes(R, H, d, FW, B)
+    cb = commit_bytes(R, H, d, FW, B) if args.separate_commit else forward_commit_bytes(R, H, d, FW, B)
+    com_name = "commit" if args.separate_commit else "forward+commit"
     tokens = args.steps * nd * nl * R * B
     value = tokens / elapsed
     log(f"forward: avg {fwd_avg * 1e6:.1f} us/launch, {fb / fwd_avg / 1e9:.0f} GB/s algorithmic "
-        f"({fb / 1e6:.1f} MB/launch); commit: avg {com_avg * 1e6:.1f} us/launch, "
+        f"({fb / 1e6:.1f} MB/launch); {com_name}: avg {com_avg * 1e6:.1f} us/launch, "
         f"{cb / com_avg / 1e9:.0f} GB/s ({cb / 1e6:.1f} MB/launch)")
-    log(f"step: {elapsed / args.steps * 1e3:.2f} ms ({nd} x {nl} forwards + {nl} commits); "
+    log(f"step: {elapsed / args.steps * 1e3:.2f} ms ({nd_plain} x {nl} forwards + {nl} {com_name}); "
         f"{value / 1e6:.1f} M tokens/s")
 
     if args.copy_calibration_mib > 0:
@@ -302,8 +319,9 @@ def main() -> int:
         "config": {
             "workload": (f"{args.config}: continuous-batching decode, {R} requests x {H} heads, d={d}, "
                          f"FW={FW} (F={2 * FW}), B={B}, ragged prefixes {int(case.n_blocks.min()) * B}-"
-                         f"{max_blocks * B} tokens; per step {nd} denoising forwards then 1 commit "
-                         f"in each of {nl} block-hybrid layers"),
+                         f"{max_blocks * B} tokens; per step {nd} denoising forwards in each of {nl} "
+                         f"block-hybrid layers, the block committed "
+                         + ("by a separate commit" if args.separate_commit else "within the last forward")),
             "requests": R, "heads": H, "head_dim": d, "feat_half": FW, "block": B,
             "denoise_steps": nd, "layers": nl, "state_dtype": "f32", "io_dtype": "bf16",
         },
@@ -320,6 +338,8 @@ def main() -> int:
         },
         "context": {"torch_copy_GBps": copy_gbps},
         "commit": {
+            "kernel": ("bha_state_commit" if args.separate_commit
+                       else "bha_block_forward_commit (last denoising step and commit, one pass)"),
             "avg_launch_us": com_avg * 1e6,
             "bytes_per_launch": cb,
             "achieved_GBps": cb / com_avg / 1e9,

@@ -147,6 +147,27 @@ int bha_state_commit(const bha_dims* dims, const void* k, const void* v, const b
                      const int32_t* slot_ids, hipStream_t stream);
 
 /*
+ * bha_block_forward_commit -- the last denoising step of a block: the forward
+ * of bha_block_forward, from the state as it stands (committed blocks only),
+ * and then, for the requests whose commit_mask entry is non-zero, the commit
+ * of bha_state_commit with the same k and v (gist.science "Architecture
+ * Design": the states change only when a block is committed; "Key
+ * Contributions": the state is kept per request so that requests at
+ * different points join one continuously batched step). Equal to
+ * bha_block_forward followed by bha_state_commit on the committing requests,
+ * with each record read once and written once.
+ *   commit_mask : uint8 [R] device, or NULL for every request.
+ *   state       : read and, for committing requests, updated in place; slot
+ *                 ids of committing requests must be distinct.
+ * Other arguments as for bha_block_forward.
+ */
+int bha_block_forward_commit(const bha_dims* dims, const void* q, const void* k, const void* v,
+                             const bha_strides* qkv, const void* w, int64_t w_head_stride,
+                             const float* gamma, float* state, int32_t num_slots,
+                             const int32_t* slot_ids, const uint8_t* commit_mask, void* out,
+                             const bha_strides* outs, hipStream_t stream);
+
+/*
  * bha_state_prefill -- fold a whole run of tokens per request into its state
  * in one launch: a prompt of any length, or several finished blocks at once.
  * For request r the tokens are rows seq_offsets[r] .. seq_offsets[r+1]-1 of

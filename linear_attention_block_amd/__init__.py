@@ -41,7 +41,7 @@ BHA_BF16 = 1
 
 # Every symbol include/bha.h declares.
 EXPORTED_SYMBOLS = (
-    "bha_feature_map", "bha_block_forward", "bha_state_commit", "bha_state_prefill",
+    "bha_feature_map", "bha_block_forward", "bha_block_forward_commit", "bha_state_commit", "bha_state_prefill",
     "bha_state_record_floats", "bha_status_string", "bha_version",
 )
 
@@ -89,6 +89,8 @@ def load_library():
     lib.bha_feature_map.argtypes = [PD, P, PS, P, I64, P, P]
     lib.bha_block_forward.argtypes = [PD, P, P, P, PS, P, I64, P, P, I32, P, P, PS, P]
     lib.bha_state_commit.argtypes = [PD, P, P, PS, P, I64, P, I32, P, P]
+    lib.bha_block_forward_commit.argtypes = [PD, P, P, P, PS, P, I64, P, P, I32, P, P, P, PS, P]
+    lib.bha_block_forward_commit.restype = ctypes.c_int
     lib.bha_state_prefill.argtypes = [PD, P, P, PS, P, I64, P, I64, P, I32, P, P]
     lib.bha_state_prefill.restype = ctypes.c_int
     lib.bha_state_record_floats.argtypes = [I32, I32]
@@ -214,6 +216,20 @@ def _forward_args(q, k, v, w, gamma, state, slot_ids, out, scale, stream):
             _stream(q.device, stream)), (dims, qs, os_)
 
 
+def _forward_commit_args(q, k, v, w, gamma, state, slot_ids, commit_mask, out, scale, stream):
+    args, keep = _forward_args(q, k, v, w, gamma, state, slot_ids, out, scale, stream)
+    if commit_mask is None:
+        mask_ptr = ctypes.c_void_p(0)
+    else:
+        if commit_mask.dtype not in (torch.uint8, torch.bool) or commit_mask.numel() != q.shape[0] or \
+                not commit_mask.is_contiguous():
+            raise ValueError("commit_mask must be a contiguous uint8 (or bool) [R] tensor")
+        _check_device(q.device, commit_mask)
+        mask_ptr = _ptr(commit_mask)
+    # forward arguments with the commit mask inserted after slot_ids
+    return args[:11] + (mask_ptr,) + args[11:], keep
+
+
 def _commit_args(k, v, w, state, slot_ids, stream):
     ks = _tok_strides(k, "k")
     R, B, H, d = k.shape
@@ -250,6 +266,21 @@ def block_forward(q, k, v, w, gamma, state, slot_ids, *, out=None, scale: float 
     st = lib.bha_block_forward(*args)
     if st != 0:
         raise BhaError("bha_block_forward", st)
+    return out
+
+
+def block_forward_commit(q, k, v, w, gamma, state, slot_ids, *, commit_mask=None, out=None,
+                         scale: float = 0.0, stream=None) -> torch.Tensor:
+    """The last denoising step of a block: the forward from the state as it
+    stands, then the commit of (k, v) for the requests whose ``commit_mask``
+    entry is non-zero (every request when it is None); returns ``out``."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    args, _keep = _forward_commit_args(q, k, v, w, gamma, state, slot_ids, commit_mask, out, scale, stream)
+    st = lib.bha_block_forward_commit(*args)
+    if st != 0:
+        raise BhaError("bha_block_forward_commit", st)
     return out
 
 
@@ -311,6 +342,14 @@ def prepare_forward(q, k, v, w, gamma, state, slot_ids, out, *, scale: float = 0
     args, keep = _forward_args(q, k, v, w, gamma, state, slot_ids, out, scale, stream)
     keep = keep + (q, k, v, w, gamma, state, slot_ids, out)
     return _Prepared(load_library().bha_block_forward, "bha_block_forward", args, keep)
+
+
+def prepare_forward_commit(q, k, v, w, gamma, state, slot_ids, out, *, commit_mask=None, scale: float = 0.0,
+                           stream=None):
+    """Marshal a bha_block_forward_commit call once, for launch-rate-bound loops."""
+    args, keep = _forward_commit_args(q, k, v, w, gamma, state, slot_ids, commit_mask, out, scale, stream)
+    keep = keep + (q, k, v, w, gamma, state, slot_ids, out, commit_mask)
+    return _Prepared(load_library().bha_block_forward_commit, "bha_block_forward_commit", args, keep)
 
 
 def prepare_commit(k, v, w, state, slot_ids, *, stream=None):

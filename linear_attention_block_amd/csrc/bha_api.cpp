@@ -78,9 +78,51 @@ extern "C" int bha_state_commit(const bha_dims* dims, const void* k, const void*
     a.FW = dims->feat_half; a.B = dims->block_size; a.io = dims->io_dtype;
     a.k = k; a.v = v; a.ks = *kv; a.w = w; a.wh = w_head_stride;
     a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids;
-    a.seq_offsets = nullptr; a.total_tokens = 0;
+    a.seq_offsets = nullptr; a.total_tokens = 0; a.commit_mask = nullptr;
     hipError_t e = launch_commit_mfma(a, stream);
     if (e == hipErrorNotSupported) e = launch_commit_generic(a, stream);
+    return launch_status(e);
+}
+
+extern "C" int bha_block_forward_commit(const bha_dims* dims, const void* q, const void* k, const void* v,
+                                        const bha_strides* qkv, const void* w, int64_t w_head_stride,
+                                        const float* gamma, float* state, int32_t num_slots,
+                                        const int32_t* slot_ids, const uint8_t* commit_mask, void* out,
+                                        const bha_strides* outs, hipStream_t stream)
+{
+    int st = validate_dims(dims);
+    if (st != BHA_OK) return st;
+    if (dims->num_requests == 0) return BHA_OK;
+    if ((st = validate_tokens(q, qkv, dims, false)) != BHA_OK) return st;
+    if ((st = validate_tokens(k, qkv, dims, false)) != BHA_OK) return st;
+    if ((st = validate_tokens(v, qkv, dims, false)) != BHA_OK) return st;
+    if ((st = validate_w(w, w_head_stride, dims)) != BHA_OK) return st;
+    if (!gamma) return BHA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(gamma) % 4 != 0) return BHA_ERR_ALIGN;
+    if ((st = validate_state(state, num_slots, slot_ids, dims)) != BHA_OK) return st;
+    if ((st = validate_tokens(out, outs, dims, true)) != BHA_OK) return st;
+    ForwardArgs a;
+    a.R = dims->num_requests; a.H = dims->num_heads; a.d = dims->head_dim;
+    a.FW = dims->feat_half; a.B = dims->block_size; a.io = dims->io_dtype;
+    a.scale = dims->scale > 0.0f ? dims->scale : 1.0f / sqrtf((float)dims->head_dim);
+    a.q = q; a.k = k; a.v = v; a.qs = *qkv; a.w = w; a.wh = w_head_stride; a.gamma = gamma;
+    a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids; a.out = out; a.os = *outs;
+    CommitArgs c;
+    c.R = a.R; c.H = a.H; c.d = a.d; c.FW = a.FW; c.B = a.B; c.io = a.io;
+    c.k = k; c.v = v; c.ks = *qkv; c.w = w; c.wh = w_head_stride;
+    c.state = state; c.num_slots = num_slots; c.slot_ids = slot_ids;
+    c.seq_offsets = nullptr; c.total_tokens = 0; c.commit_mask = commit_mask;
+    hipError_t e = launch_forward_commit_mfma(a, c, stream);
+    if (e == hipErrorNotSupported) {
+        // the same result in two launches: the forward reads the state before
+        // the commit changes it (both on the caller's stream)
+        e = launch_forward_mfma(a, stream);
+        if (e == hipErrorNotSupported) e = launch_forward_generic(a, stream);
+        if (e == hipSuccess) {
+            e = launch_commit_mfma(c, stream);
+            if (e == hipErrorNotSupported) e = launch_commit_generic(c, stream);
+        }
+    }
     return launch_status(e);
 }
 
@@ -112,7 +154,7 @@ extern "C" int bha_state_prefill(const bha_dims* dims, const void* k, const void
     a.FW = dims->feat_half; a.B = dims->block_size; a.io = dims->io_dtype;
     a.k = k; a.v = v; a.ks = ps; a.w = w; a.wh = w_head_stride;
     a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids;
-    a.seq_offsets = seq_offsets; a.total_tokens = total_tokens;
+    a.seq_offsets = seq_offsets; a.total_tokens = total_tokens; a.commit_mask = nullptr;
     hipError_t e = launch_prefill_mfma(a, stream);
     if (e == hipErrorNotSupported) e = launch_commit_generic(a, stream);
     return launch_status(e);

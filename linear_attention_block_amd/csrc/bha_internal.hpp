@@ -38,11 +38,18 @@ struct CommitArgs {
     // (of total_tokens); nullptr for a commit of B tokens per request
     const int32_t* seq_offsets;
     int64_t total_tokens;
+    // requests with commit_mask[r] == 0 are left untouched; nullptr: all commit
+    const uint8_t* commit_mask;
 };
 
 // Token range of request r in a commit or prefill, clamped as documented.
 __device__ __forceinline__ void commit_rows(const CommitArgs& a, int r, int64_t& first_row, int& n)
 {
+    if (a.commit_mask != nullptr && a.commit_mask[r] == 0) {
+        first_row = -1;
+        n = 0;
+        return;
+    }
     if (a.seq_offsets == nullptr) {
         first_row = -1;  // rows r*req + t*tok
         n = a.B;
@@ -75,6 +82,9 @@ hipError_t launch_feature_map_generic(const PhiArgs& a, hipStream_t s);
 hipError_t launch_forward_mfma(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_commit_mfma(const CommitArgs& a, hipStream_t s);
 hipError_t launch_prefill_mfma(const CommitArgs& a, hipStream_t s);
+// Forward of the block's last denoising step and the commit of its K, V in one
+// pass over each pair's state (bf16, B <= 32); c carries the commit mask.
+hipError_t launch_forward_commit_mfma(const ForwardArgs& a, const CommitArgs& c, hipStream_t s);
 
 // Host-side argument checks (no HIP calls); see bha_validate.cpp.
 int validate_dims(const bha_dims* d);

@@ -216,3 +216,26 @@ def test_prefill_validation(lib):
     assert prefill(lib, _dims(), num_slots=0) == DIMS
     assert prefill(lib, _dims(head_dim=96)) == UNSUP
     assert prefill(lib, _dims(), total=1 << 40) == DIMS
+
+
+def fwd_commit(lib, dims, q=FAKE, k=FAKE, v=FAKE, w=FAKE, gamma=FAKE, state=FAKE, num_slots=8, slots=FAKE,
+               mask=0, out=FAKE + (1 << 24), qs=None, outs=None):
+    qs = qs or _st()
+    outs = outs or _st()
+    P = ctypes.c_void_p
+    return lib.bha_block_forward_commit(ctypes.byref(dims) if dims is not None else None, P(q), P(k), P(v),
+                                        ctypes.byref(qs), P(w), 64 * 128, P(gamma), P(state), num_slots, P(slots),
+                                        P(mask), P(out), ctypes.byref(outs), P(0))
+
+
+def test_forward_commit_validation(lib):
+    assert fwd_commit(lib, None) == NULL
+    assert fwd_commit(lib, _dims(num_requests=0), q=0, k=0, v=0, w=0, gamma=0, state=0, slots=0, out=0) == OK
+    for name in ("q", "k", "v", "w", "gamma", "state", "slots", "out"):
+        assert fwd_commit(lib, _dims(), **{name: 0}) == NULL, name
+    assert fwd_commit(lib, _dims(), gamma=FAKE + 2) == ALIGN
+    assert fwd_commit(lib, _dims(), state=FAKE + 4) == ALIGN
+    assert fwd_commit(lib, _dims(head_dim=96)) == UNSUP
+    assert fwd_commit(lib, _dims(io_dtype=5)) == DTYPE
+    assert fwd_commit(lib, _dims(), num_slots=0) == DIMS
+    assert fwd_commit(lib, _dims(), outs=bha_strides(0, 256, 128)) == STRIDE

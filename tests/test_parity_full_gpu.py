@@ -85,9 +85,21 @@ def _run_full(name, dev, n_pairs=24, seed=0):
     out = bha.block_forward(q, k, v, w, gamma, state, slots)
     torch.cuda.synchronize()
     pre = state[torch.from_numpy(case.slot_ids.astype(np.int64)).to(dev)].cpu().numpy()  # [R][H][rec]
+    state_f = state.clone()
     bha.state_commit(k, v, w, state, slots)
     torch.cuda.synchronize()
     post = state[torch.from_numpy(case.slot_ids.astype(np.int64)).to(dev)].cpu().numpy()
+
+    # the fused last step on a copy of the same states: the same output, and the
+    # same committed states on every pair
+    out_f = bha.block_forward_commit(q, k, v, w, gamma, state_f, slots)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f, out)
+    e_fc = _pairwise_err(state_f[sel], state[sel], d, F)
+    del state_f, out_f
+    print(f"[{name}] fused forward+commit vs forward then commit over all {R * H} pairs: output identical, "
+          f"S err {e_fc[0]:.2e}, Z err {e_fc[1]:.2e}", flush=True)
+    assert e_fc[0] <= 1e-5 and e_fc[1] <= 1e-5
 
     w64 = w.float().cpu().numpy().astype(np.float64)
     g64 = gamma.cpu().numpy().astype(np.float64)

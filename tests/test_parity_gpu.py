@@ -322,3 +322,64 @@ def test_prefill_long_prompts_fused_kv(dev):
     # untouched slots stay zero
     rest = np.setdiff1d(np.arange(case.num_slots), case.slot_ids)
     assert not state.cpu().numpy()[rest].any()
+
+
+FUSED = [("bf16", 128, 64, 32), ("bf16", 128, 64, 17), ("bf16", 64, 32, 32), ("bf16", 128, 128, 32),
+         ("bf16", 64, 128, 8), ("bf16", 128, 64, 40), ("f32", 128, 64, 32), ("f32", 64, 32, 5)]
+
+
+@pytest.mark.parametrize("io,d,fw,b", FUSED)
+def test_forward_commit_matches_oracle(dev, io, d, fw, b):
+    # last denoising step of a block: the forward from the committed state, then
+    # the commit of the block's k, v for the requests flagged in the mask; one
+    # request has an out-of-range slot (NaN output, no commit)
+    case = synth.make_case("tiny", R=6, H=3, d=d, FW=fw, B=b, io=io, blocks=(0, 3), gamma="uniform")
+    run = Run(case, dev)
+    run.build_state()
+    S0, Z0 = run.plain_state()
+    bad = case.slot_ids.copy()
+    bad[4] = case.num_slots
+    run.slots = torch.from_numpy(bad).to(dev)
+    before = run.state.cpu().numpy()
+    mask = np.array([1, 0, 1, 1, 1, 1], dtype=np.uint8)
+    q, k, v = (to_device(x, io, dev) for x in (case.q, case.k, case.v))
+    y = to_host(bha.block_forward_commit(q, k, v, run.w, run.gamma, run.state, run.slots,
+                                         commit_mask=torch.from_numpy(mask).to(dev)))
+    torch.cuda.synchronize()
+    after = run.state.cpu().numpy()
+    good = np.array([0, 1, 2, 3, 5])
+    assert np.all(np.isnan(y[4]))
+    ref = run.oracle_forward(S0, Z0)
+    err_f = normwise_err(pairs(y)[good], ref[good], (2, 3))
+    S1, Z1 = record_to_plain(after[case.slot_ids], d, case.F)
+    S_ref, Z_ref = S0.copy(), Z0.copy()
+    oracle.state_commit_batch(S_ref, Z_ref, pairs(case.k), pairs(case.v), case.w.astype(np.float64),
+                              nthreads=NTHREADS)
+    on = np.array([0, 2, 3, 5])
+    err_s = normwise_err(S1[on], S_ref[on], (2, 3))
+    err_z = normwise_err(Z1[on], Z_ref[on], (2,))
+    _log(f"[fused] io={io} d={d} FW={fw} B={b} forward err {err_f:.2e}, commit S err {err_s:.2e} Z err {err_z:.2e}")
+    # masked-off request, the request with the bad slot's own slot, and unused slots are untouched
+    keep = np.concatenate([case.slot_ids[[1, 4]], np.setdiff1d(np.arange(case.num_slots), case.slot_ids)])
+    assert np.array_equal(after[keep], before[keep])
+    assert err_f <= TOL[io] and err_s <= TOL[io] and err_z <= TOL[io]
+
+
+@pytest.mark.parametrize("io,b", [("bf16", 32), ("bf16", 9), ("f32", 32)])
+def test_forward_commit_equals_forward_then_commit(dev, io, b):
+    case = synth.make_case("tiny", R=5, H=4, d=128, FW=64, B=b, io=io, blocks=(1, 3), gamma="uniform")
+    run = Run(case, dev)
+    run.build_state()
+    s0 = run.state.clone()
+    q, k, v = (to_device(x, io, dev) for x in (case.q, case.k, case.v))
+    y_sep = bha.block_forward(q, k, v, run.w, run.gamma, run.state, run.slots).clone()
+    bha.state_commit(k, v, run.w, run.state, run.slots)
+    s_sep = run.state.clone()
+    run.state.copy_(s0)
+    y_fused = bha.block_forward_commit(q, k, v, run.w, run.gamma, run.state, run.slots)
+    torch.cuda.synchronize()
+    # same forward arithmetic; the commit's sums may run in another order
+    assert torch.equal(y_fused, y_sep)
+    S_f, Z_f = record_to_plain(run.state.cpu().numpy()[case.slot_ids], case.d, case.F)
+    S_s, Z_s = record_to_plain(s_sep.cpu().numpy()[case.slot_ids], case.d, case.F)
+    assert normwise_err(S_f, S_s, (2, 3)) <= 1e-5 and normwise_err(Z_f, Z_s, (2,)) <= 1e-5
