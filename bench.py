@@ -162,6 +162,10 @@ def main() -> int:
     ap.add_argument("--separate-commit", action="store_true",
                     help="run every denoising step as a plain forward and commit with bha_state_commit "
                          "(default: the last step of the block is bha_block_forward_commit)")
+    ap.add_argument("--staggered", action="store_true",
+                    help="continuous batching with staggered blocks: request r finishes its block at denoising "
+                         "step r mod 32, so every step is one bha_block_forward_commit whose mask commits "
+                         "1/32 of the requests")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -177,6 +181,7 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
+    import numpy as np
     import torch
 
     import linear_attention_block_amd as bha
@@ -211,7 +216,10 @@ def main() -> int:
         del pk, pv
         q, k, v = synth.device_step_qkv(args.config, 0, R, dev, layer=L)
         out = torch.empty_like(q)
+        masks = [torch.from_numpy((np.arange(R) % nd == i).astype(np.uint8)).to(dev) for i in range(nd)]
         layers.append(dict(w=w, gamma=gamma, state=state, q=q, k=k, v=v, out=out,
+                           stag=[bha.prepare_forward_commit(q, k, v, w, gamma, state, slots, out, commit_mask=m)
+                                 for m in masks] if args.staggered else None,
                            fwd=bha.prepare_forward(q, k, v, w, gamma, state, slots, out),
                            com=(bha.prepare_commit(k, v, w, state, slots) if args.separate_commit else
                                 bha.prepare_forward_commit(q, k, v, w, gamma, state, slots, out))))
@@ -228,11 +236,24 @@ def main() -> int:
     # the fused forward + commit, or a plain forward followed by a commit
     nd_plain = nd if args.separate_commit else nd - 1
     n_fwd, n_com = nd_plain * nl, nl
+    if args.staggered:
+        nd_plain, n_fwd, n_com = nd, nd * nl, 0
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps * (n_fwd + n_com))]
 
     def step(evs):
         it = iter(evs) if evs is not None else None
+        if args.staggered:
+            for i in range(nd):
+                for lay in layers:
+                    if it is not None:
+                        e0, e1 = next(it)
+                        e0.record()
+                        lay["stag"][i]()
+                        e1.record()
+                    else:
+                        lay["stag"][i]()
+            return
         for _ in range(nd_plain):
             for lay in layers:
                 if it is not None:
@@ -267,17 +288,26 @@ def main() -> int:
         fwd_ms += [a.elapsed_time(b) for a, b in blk[:n_fwd]]
         com_ms += [a.elapsed_time(b) for a, b in blk[n_fwd:]]
     fwd_avg = sum(fwd_ms) / len(fwd_ms) * 1e-3
-    com_avg = sum(com_ms) / len(com_ms) * 1e-3
+    com_avg = sum(com_ms) / len(com_ms) * 1e-3 if com_ms else None
     fb = forward_bytes(R, H, d, FW, B)
+    if args.staggered:
+        # every launch writes back the records of the 1/nd of requests it commits
+        F_ = 2 * FW
+        fb += sum(1 for r in range(R) if r % nd == 0) * H * (d * F_ * 4 + F_ * 4)
     cb = commit_bytes(R, H, d, FW, B) if args.separate_commit else forward_commit_bytes(R, H, d, FW, B)
     com_name = "commit" if args.separate_commit else "forward+commit"
     tokens = args.steps * nd * nl * R * B
     value = tokens / elapsed
-    log(f"forward: avg {fwd_avg * 1e6:.1f} us/launch, {fb / fwd_avg / 1e9:.0f} GB/s algorithmic "
-        f"({fb / 1e6:.1f} MB/launch); {com_name}: avg {com_avg * 1e6:.1f} us/launch, "
-        f"{cb / com_avg / 1e9:.0f} GB/s ({cb / 1e6:.1f} MB/launch)")
-    log(f"step: {elapsed / args.steps * 1e3:.2f} ms ({nd_plain} x {nl} forwards + {nl} {com_name}); "
-        f"{value / 1e6:.1f} M tokens/s")
+    if args.staggered:
+        log(f"staggered forward+commit: avg {fwd_avg * 1e6:.1f} us/launch, {fb / fwd_avg / 1e9:.0f} GB/s "
+            f"algorithmic ({fb / 1e6:.1f} MB/launch)")
+        log(f"step: {elapsed / args.steps * 1e3:.2f} ms ({nd} x {nl} launches); {value / 1e6:.1f} M tokens/s")
+    else:
+        log(f"forward: avg {fwd_avg * 1e6:.1f} us/launch, {fb / fwd_avg / 1e9:.0f} GB/s algorithmic "
+            f"({fb / 1e6:.1f} MB/launch); {com_name}: avg {com_avg * 1e6:.1f} us/launch, "
+            f"{cb / com_avg / 1e9:.0f} GB/s ({cb / 1e6:.1f} MB/launch)")
+        log(f"step: {elapsed / args.steps * 1e3:.2f} ms ({nd_plain} x {nl} forwards + {nl} {com_name}); "
+            f"{value / 1e6:.1f} M tokens/s")
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
@@ -321,7 +351,9 @@ def main() -> int:
                          f"FW={FW} (F={2 * FW}), B={B}, ragged prefixes {int(case.n_blocks.min()) * B}-"
                          f"{max_blocks * B} tokens; per step {nd} denoising forwards in each of {nl} "
                          f"block-hybrid layers, the block committed "
-                         + ("by a separate commit" if args.separate_commit else "within the last forward")),
+                         + ("by a separate commit" if args.separate_commit else
+                            "with staggered blocks (1/32 of requests per step)" if args.staggered else
+                            "within the last forward")),
             "requests": R, "heads": H, "head_dim": d, "feat_half": FW, "block": B,
             "denoise_steps": nd, "layers": nl, "state_dtype": "f32", "io_dtype": "bf16",
         },
@@ -331,13 +363,15 @@ def main() -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
-            "traffic": read_traffic(args.config),
-            "kernel": f"bha_block_forward: forward_mfma_kernel<{d},{FW}> (persistent, bf16 MFMA)",
+            "traffic": None if args.staggered else read_traffic(args.config),
+            "kernel": (f"bha_block_forward_commit: forward_commit_mfma_kernel<{d},{FW}> (1/{nd} of requests "
+                       f"commit per launch)" if args.staggered else
+                       f"bha_block_forward: forward_mfma_kernel<{d},{FW}> (persistent, bf16 MFMA)"),
             "bytes_per_launch": fb,
             "avg_launch_us": fwd_avg * 1e6,
         },
         "context": {"torch_copy_GBps": copy_gbps},
-        "commit": {
+        "commit": None if args.staggered else {
             "kernel": ("bha_state_commit" if args.separate_commit
                        else "bha_block_forward_commit (last denoising step and commit, one pass)"),
             "avg_launch_us": com_avg * 1e6,
