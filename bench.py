@@ -19,7 +19,10 @@ Prints ONE JSON line: value = active-block tokens per second through
 block-hybrid attention (each forward moves R * B tokens through one layer),
 the roofline of the dominant kernel (the forward; algorithmic bytes per launch
 divided by its HIP-event-timed average launch duration, against 8 TB/s), and
-the fp64 CPU oracle timed on a bounded sample of the same workload.
+the fp64 CPU oracle timed on a bounded sample of the same workload. Beside
+it, outside the timed region: exact softmax attention of the same batch over the
+whole prefixes (``bha_prefix_attention``), the per-step cost the hybrid layer
+removes.
 """
 from __future__ import annotations
 
@@ -36,7 +39,8 @@ if ROOT not in sys.path:
 
 METRIC = "active-block tokens/s through block-hybrid attn; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
-KERNEL_SOURCES = ("linear_attention_block_amd/csrc/mfma.hip", "linear_attention_block_amd/csrc/bha_device.hpp")
+KERNEL_SOURCES = ("linear_attention_block_amd/csrc/mfma.hip", "linear_attention_block_amd/csrc/bha_device.hpp",
+                  "linear_attention_block_amd/csrc/bha_mfma.hpp")
 
 
 def forward_bytes(R, H, d, FW, B, es=2):
@@ -66,6 +70,13 @@ def prefill_bytes(T, R, H, d, FW, es=2):
     read and written once, W once per head, the offsets and slot ids."""
     F = 2 * FW
     return T * H * 2 * d * es + R * H * 2 * (d * F * 4 + F * 4) + H * FW * d * es + (2 * R + 1) * 4
+
+
+def prefix_attention_bytes(T, R, H, d, B, es=2):
+    """Algorithmic HBM bytes of one bha_prefix_attention launch: K and V of
+    every packed prefix token and head read once, the block's Q, K, V read and
+    O written, the offsets."""
+    return T * H * 2 * d * es + R * H * 4 * B * d * es + (R + 1) * 4
 
 
 def kernel_source_hash() -> str:
@@ -213,6 +224,8 @@ def main() -> int:
         p1.record()
         torch.cuda.synchronize()
         prefill_ms.append(p0.elapsed_time(p1))
+        if L == 0:
+            prefix0 = (pk, pv, offs)  # for the softmax prefix-attention comparison
         del pk, pv
         q, k, v = synth.device_step_qkv(args.config, 0, R, dev, layer=L)
         out = torch.empty_like(q)
@@ -309,6 +322,28 @@ def main() -> int:
         log(f"step: {elapsed / args.steps * 1e3:.2f} ms ({nd_plain} x {nl} forwards + {nl} {com_name}); "
             f"{value / 1e6:.1f} M tokens/s")
 
+    # comparison: exact softmax attention of the same batch over each request's
+    # whole prefix and block (what the hybrid forward replaces), layer 0's
+    # tokens, timed outside the timed region above
+    pk, pv, offs = prefix0
+    l0 = layers[0]
+    sm_out = torch.empty_like(l0["q"])
+    sm = bha.prepare_prefix_attention(l0["q"], l0["k"], l0["v"], pk, pv, offs, sm_out)
+    sm()
+    sm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for e0, e1 in sm_ev:
+        e0.record()
+        sm()
+        e1.record()
+    torch.cuda.synchronize()
+    sm_avg = sum(a.elapsed_time(b) for a, b in sm_ev) / len(sm_ev) * 1e-3
+    smb = prefix_attention_bytes(T, R, H, d, B)
+    del sm, sm_out, pk, pv, offs, prefix0
+    torch.cuda.empty_cache()
+    log(f"softmax prefix attention (same batch, whole prefixes): avg {sm_avg * 1e6:.1f} us/launch, "
+        f"{smb / sm_avg / 1e9:.0f} GB/s algorithmic ({smb / 1e9:.2f} GB/launch); "
+        f"{sm_avg / fwd_avg:.1f}x the hybrid step's launch")
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -387,6 +422,15 @@ def main() -> int:
             "bytes_per_launch": pb,
             "achieved_GBps": pb / pre_avg / 1e9,
             "frac": pb / pre_avg / 1e9 / PEAK_HBM_GBS,
+        },
+        "softmax_prefix_attention": {
+            "workload": f"bha_prefix_attention on layer 0's batch: the {R * B} block queries attend to their "
+                        f"request's whole prefix and block ({T} prefix tokens x {H} heads)",
+            "avg_launch_us": sm_avg * 1e6,
+            "bytes_per_launch": smb,
+            "achieved_GBps": smb / sm_avg / 1e9,
+            "frac": smb / sm_avg / 1e9 / PEAK_HBM_GBS,
+            "launch_time_over_hybrid_step": sm_avg / fwd_avg,
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(layers[0], case, nd,
                                                                           args.cpu_sample_requests, log),

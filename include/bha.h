@@ -187,6 +187,30 @@ int bha_state_prefill(const bha_dims* dims, const void* k, const void* v, const 
                       int64_t w_head_stride, float* state, int32_t num_slots,
                       const int32_t* slot_ids, hipStream_t stream);
 
+/*
+ * bha_prefix_attention -- exact softmax attention of the active block's
+ * queries over the request's whole prefix and the block itself: the attention
+ * block-hybrid attention replaces, whose cost grows with the prefix
+ * (gist.science "Problem Statement": every denoising step attends to all
+ * previous blocks). For query i of request r and head h, over the prefix rows
+ * t = seq_offsets[r] .. seq_offsets[r+1]-1 of kp, vp and then the B block
+ * tokens (no mask):
+ *   out_i = sum_t e^{s_it - m_i} v_t / sum_t e^{s_it - m_i},
+ *   s_it = scale q_i . k_t, m_i = max_t s_it.
+ *   q, k, v, out : as for bha_block_forward.
+ *   kp, vp       : packed prefix tokens, element (t, h, c) at
+ *                  t*kvp->tok + h*kvp->head + c for t < total_tokens
+ *                  (kvp->req is not used); may be NULL when total_tokens == 0.
+ *   seq_offsets  : int32 [R + 1] device, clamped on the device to
+ *                  0 <= seq_offsets[r] <= seq_offsets[r+1] <= total_tokens.
+ *   dims->feat_half must be a supported value but is not used.
+ * No state is read; nothing is written but out.
+ */
+int bha_prefix_attention(const bha_dims* dims, const void* q, const void* k, const void* v,
+                         const bha_strides* qkv, const void* kp, const void* vp, const bha_strides* kvp,
+                         const int32_t* seq_offsets, int64_t total_tokens, void* out,
+                         const bha_strides* outs, hipStream_t stream);
+
 /* Floats in one (slot, head) state record: (d + 1) * 2 * FW. Returns -1 for
  * unsupported sizes. Host only; touches no device. */
 int64_t bha_state_record_floats(int32_t head_dim, int32_t feat_half);

@@ -42,6 +42,7 @@ BHA_BF16 = 1
 # Every symbol include/bha.h declares.
 EXPORTED_SYMBOLS = (
     "bha_feature_map", "bha_block_forward", "bha_block_forward_commit", "bha_state_commit", "bha_state_prefill",
+    "bha_prefix_attention",
     "bha_state_record_floats", "bha_status_string", "bha_version",
 )
 
@@ -93,6 +94,8 @@ def load_library():
     lib.bha_block_forward_commit.restype = ctypes.c_int
     lib.bha_state_prefill.argtypes = [PD, P, P, PS, P, I64, P, I64, P, I32, P, P]
     lib.bha_state_prefill.restype = ctypes.c_int
+    lib.bha_prefix_attention.argtypes = [PD, P, P, P, PS, P, P, PS, P, I64, P, PS, P]
+    lib.bha_prefix_attention.restype = ctypes.c_int
     lib.bha_state_record_floats.argtypes = [I32, I32]
     lib.bha_state_record_floats.restype = I64
     lib.bha_status_string.argtypes = [ctypes.c_int]
@@ -323,6 +326,49 @@ def state_prefill(k, v, seq_offsets, w, state, slot_ids, *, stream=None) -> None
         raise BhaError("bha_state_prefill", st)
 
 
+def _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream):
+    qs = _tok_strides(q, "q")
+    R, B, H, d = q.shape
+    for t, n in ((k, "k"), (v, "v")):
+        if t.shape != q.shape or (t.stride(0), t.stride(1), t.stride(2)) != (qs.req, qs.tok, qs.head) or \
+                t.stride(3) != 1:
+            raise ValueError(f"{n} must match q in shape and strides")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{n} must have the dtype of q")
+    if kp.dim() != 3 or vp.shape != kp.shape or kp.shape[1:] != (H, d) or kp.stride(2) != 1 or vp.stride(2) != 1:
+        raise ValueError("kp and vp must be [T][H][d] with a contiguous last dimension")
+    if (vp.stride(0), vp.stride(1)) != (kp.stride(0), kp.stride(1)):
+        raise ValueError("vp must have the strides of kp")
+    if kp.dtype != q.dtype or vp.dtype != q.dtype:
+        raise TypeError("kp and vp must have the dtype of q")
+    if seq_offsets.dtype != torch.int32 or seq_offsets.numel() != R + 1 or not seq_offsets.is_contiguous():
+        raise ValueError("seq_offsets must be a contiguous int32 [R + 1] tensor")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    os_ = _tok_strides(out, "out")
+    _check_device(q.device, k, v, kp, vp, seq_offsets, out)
+    # feat_half is not used by this call; any supported value passes
+    dims = bha_dims(R, H, d, 64, B, _io_dtype(q), float(scale))
+    ps = bha_strides(0, kp.stride(0), kp.stride(1))
+    T = kp.shape[0]
+    return (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(qs), _ptr(kp), _ptr(vp), ctypes.byref(ps),
+            _ptr(seq_offsets), T, _ptr(out), ctypes.byref(os_), _stream(q.device, stream)), (dims, qs, ps, os_)
+
+
+def prefix_attention(q, k, v, kp, vp, seq_offsets, *, out=None, scale: float = 0.0, stream=None) -> torch.Tensor:
+    """Exact softmax attention of each block's queries over its request's
+    packed prefix (rows seq_offsets[r] .. seq_offsets[r+1]-1 of kp, vp,
+    [T][H][d]) and the block's own keys; returns ``out`` [R][B][H][d]."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    args, _keep = _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream)
+    st = lib.bha_prefix_attention(*args)
+    if st != 0:
+        raise BhaError("bha_prefix_attention", st)
+    return out
+
+
 class _Prepared:
     """A C-ABI call whose arguments were checked and marshalled once; calling it
     enqueues the same call again (on the stream captured at preparation). The
@@ -350,6 +396,13 @@ def prepare_forward_commit(q, k, v, w, gamma, state, slot_ids, out, *, commit_ma
     args, keep = _forward_commit_args(q, k, v, w, gamma, state, slot_ids, commit_mask, out, scale, stream)
     keep = keep + (q, k, v, w, gamma, state, slot_ids, out, commit_mask)
     return _Prepared(load_library().bha_block_forward_commit, "bha_block_forward_commit", args, keep)
+
+
+def prepare_prefix_attention(q, k, v, kp, vp, seq_offsets, out, *, scale: float = 0.0, stream=None):
+    """Marshal a bha_prefix_attention call once, for launch-rate-bound loops."""
+    args, keep = _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream)
+    keep = keep + (q, k, v, kp, vp, seq_offsets, out)
+    return _Prepared(load_library().bha_prefix_attention, "bha_prefix_attention", args, keep)
 
 
 def prepare_commit(k, v, w, state, slot_ids, *, stream=None):

@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libbha.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["bha_api.cpp", "bha_validate.cpp", "generic.hip", "mfma.hip"]
+SOURCES = ["bha_api.cpp", "bha_validate.cpp", "generic.hip", "mfma.hip", "softmax_attn.hip"]
 
 
 def hipcc() -> str:

@@ -160,6 +160,47 @@ extern "C" int bha_state_prefill(const bha_dims* dims, const void* k, const void
     return launch_status(e);
 }
 
+extern "C" int bha_prefix_attention(const bha_dims* dims, const void* q, const void* k, const void* v,
+                                    const bha_strides* qkv, const void* kp, const void* vp, const bha_strides* kvp,
+                                    const int32_t* seq_offsets, int64_t total_tokens, void* out,
+                                    const bha_strides* outs, hipStream_t stream)
+{
+    int st = validate_dims(dims);
+    if (st != BHA_OK) return st;
+    if (dims->num_requests == 0) return BHA_OK;
+    if ((st = validate_tokens(q, qkv, dims, false)) != BHA_OK) return st;
+    if ((st = validate_tokens(k, qkv, dims, false)) != BHA_OK) return st;
+    if ((st = validate_tokens(v, qkv, dims, false)) != BHA_OK) return st;
+    if ((st = validate_tokens(out, outs, dims, true)) != BHA_OK) return st;
+    if (total_tokens < 0 || total_tokens > INT32_MAX) return BHA_ERR_DIMS;
+    if (!seq_offsets || !kvp) return BHA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(seq_offsets) % 4 != 0) return BHA_ERR_ALIGN;
+    bha_strides ps = *kvp;
+    ps.req = 0;
+    if (total_tokens > 0) {
+        // the packed prefix, checked as one "request" of total_tokens rows
+        bha_dims packed = *dims;
+        packed.num_requests = 1;
+        packed.block_size = static_cast<int32_t>(total_tokens);
+        if ((st = validate_tokens(kp, &ps, &packed, false)) != BHA_OK) return st;
+        if ((st = validate_tokens(vp, &ps, &packed, false)) != BHA_OK) return st;
+    } else {
+        kp = k;  // no prefix rows are read
+        vp = v;
+        ps.tok = qkv->tok;
+        ps.head = qkv->head;
+    }
+    PrefixArgs a;
+    a.R = dims->num_requests; a.H = dims->num_heads; a.d = dims->head_dim;
+    a.B = dims->block_size; a.io = dims->io_dtype;
+    a.scale = dims->scale > 0.0f ? dims->scale : 1.0f / sqrtf((float)dims->head_dim);
+    a.q = q; a.k = k; a.v = v; a.qs = *qkv; a.kp = kp; a.vp = vp; a.ps = ps;
+    a.seq_offsets = seq_offsets; a.total_tokens = total_tokens; a.out = out; a.os = *outs;
+    hipError_t e = launch_prefix_attention_mfma(a, stream);
+    if (e == hipErrorNotSupported) e = launch_prefix_attention_generic(a, stream);
+    return launch_status(e);
+}
+
 extern "C" int64_t bha_state_record_floats(int32_t head_dim, int32_t feat_half)
 {
     if (head_dim != 64 && head_dim != 128) return -1;

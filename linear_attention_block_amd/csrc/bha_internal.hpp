@@ -63,6 +63,21 @@ __device__ __forceinline__ void commit_rows(const CommitArgs& a, int r, int64_t&
     n = len > 0x7fffffff ? 0x7fffffff : static_cast<int>(len);
 }
 
+// Softmax attention of the block's queries over the request's prefix and the
+// block: prefix rows seq_offsets[r] .. seq_offsets[r+1]-1 of kp, vp (clamped).
+struct PrefixArgs {
+    int R, H, d, B, io;
+    float scale;  // resolved: never 0
+    const void *q, *k, *v;
+    bha_strides qs;
+    const void *kp, *vp;
+    bha_strides ps;  // ps.req unused
+    const int32_t* seq_offsets;
+    int64_t total_tokens;
+    void* out;
+    bha_strides os;
+};
+
 struct PhiArgs {
     int R, H, d, FW, B, io;
     const void* x;
@@ -71,6 +86,11 @@ struct PhiArgs {
     int64_t wh;
     float* phi;
 };
+
+// Softmax prefix attention: matrix-core kernel (bf16, B <= 32) and the plain
+// kernel for every size and both I/O dtypes.
+hipError_t launch_prefix_attention_mfma(const PrefixArgs& a, hipStream_t s);
+hipError_t launch_prefix_attention_generic(const PrefixArgs& a, hipStream_t s);
 
 // Plain fp32-arithmetic kernels: every supported size and both I/O dtypes.
 hipError_t launch_forward_generic(const ForwardArgs& a, hipStream_t s);

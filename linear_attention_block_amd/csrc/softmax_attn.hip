@@ -1,0 +1,337 @@
+// Exact softmax attention of the active block's queries over the request's
+// whole prefix and the block itself -- the attention that block-hybrid
+// attention replaces in the converted layers, whose cost grows with the prefix
+// (gist.science "Problem Statement": every denoising step attends to all
+// previous blocks; pith.science "What carries the argument": full attention is
+// kept within the block only). For query i of request r and head h:
+//   s_it = c q_i . k_t over the prefix rows t and the block's B tokens,
+//   out_i = sum_t e^{s_it - m_i} v_t / sum_t e^{s_it - m_i},  m_i = max_t s_it.
+//
+// bf16 path (B <= 32): one work-group of four waves per (request, head). Wave
+// w takes the 32-key chunks w, w + 4, ... of the prefix-then-block key
+// sequence and keeps its own running maximum, normaliser and 32 x d output
+// accumulator per query (online softmax); the four partial results are merged
+// through LDS at the end, so the main loop has no work-group barrier. Per
+// chunk: s^T = K Q^T with v_mfma_f32_32x32x16_bf16 (lane = query), K fragments
+// loaded straight from global memory as one contiguous d/2-element run per
+// lane (the contraction over d is fed in the order g, k-step kb -> elements
+// g d/2 + 8 kb .. + 7 for both K and the Q fragments held in registers); the
+// chunk's V rows go to the wave's own LDS tile and are read transposed
+// (ds_read_b64_tr_b16) as the A operand of P V, P coming straight from the
+// score accumulators. The next chunk's K and V loads are issued before the
+// current chunk's arithmetic.
+#include "bha_device.hpp"
+#include "bha_internal.hpp"
+#include "bha_mfma.hpp"
+
+namespace bha {
+
+namespace {
+
+// Key row t of the key sequence (prefix rows first, then the block).
+struct KeySource {
+    const uint16_t* prefix;  // row 0 of the request's prefix, this head
+    const uint16_t* block;   // token 0 of the block, this head
+    int64_t ptok, btok;      // token strides (elements)
+    int np, nk;              // prefix rows, keys in all (np + B)
+
+    __device__ __forceinline__ const uint16_t* row(int t) const
+    {
+        t = t < nk ? t : nk - 1;  // past the end: the last key (masked)
+        return t < np ? prefix + t * ptok : block + (t - np) * btok;
+    }
+};
+
+template <int D>
+struct SaCfg {
+    static constexpr int NKB = D / 16;         // k-steps of the score contraction
+    static constexpr int CT = D / 32;          // 32-column output tiles per wave
+    static constexpr int VQ = 32 * (D / 8) / 64;  // 16-byte V chunks per lane per key chunk
+    static constexpr int TILE = 32 * D;        // bf16 elements of one wave's V tile
+    static constexpr int LDS_LOOP = 4 * TILE * 2;
+    static constexpr int LDS_MERGE = 4 * D * 32 * 4 + 2 * 4 * 32 * 4;
+    static constexpr int LDS = LDS_LOOP > LDS_MERGE ? LDS_LOOP : LDS_MERGE;
+};
+
+template <int D>
+__device__ __forceinline__ void sa_load_chunk(const KeySource& ks, int c, int lane, bf16x8 (&kf)[D / 16],
+                                              u32x4 (&vr)[SaCfg<D>::VQ], const uint16_t* vprefix,
+                                              const uint16_t* vblock)
+{
+    constexpr int CH = D / 8;
+    const int m = lane & 31, g = lane >> 5;
+    const uint16_t* kr = ks.row(32 * c + m) + g * (D / 2);
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb) kf[kb] = *reinterpret_cast<const bf16x8*>(kr + 8 * kb);
+    // V rows: the same key rows, from the value tensors
+#pragma unroll
+    for (int i = 0; i < SaCfg<D>::VQ; ++i) {
+        const int idx = lane + 64 * i, t = idx / CH, ch = idx % CH;
+        int tt = 32 * c + t;
+        tt = tt < ks.nk ? tt : ks.nk - 1;
+        const uint16_t* vrow = tt < ks.np ? vprefix + tt * ks.ptok : vblock + (tt - ks.np) * ks.btok;
+        vr[i] = *reinterpret_cast<const u32x4*>(vrow + ch * 8);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefix_attn_mfma_kernel(PrefixArgs a)
+{
+    using C = SaCfg<D>;
+    constexpr int CH = D / 8;
+    const int pair = blockIdx.x;
+    const int r = pair / a.H, h = pair % a.H;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int ln = lane & 31, g = lane >> 5;
+
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
+    uint16_t* const Vt = reinterpret_cast<uint16_t*>(smem) + wv * C::TILE;
+
+    int64_t s0 = a.seq_offsets[r], s1 = a.seq_offsets[r + 1];
+    s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);
+    s1 = s1 < s0 ? s0 : (s1 > a.total_tokens ? a.total_tokens : s1);
+    KeySource ks;
+    const int64_t hoff = static_cast<int64_t>(h) * a.ps.head;
+    const int64_t boff = static_cast<int64_t>(r) * a.qs.req + static_cast<int64_t>(h) * a.qs.head;
+    ks.prefix = static_cast<const uint16_t*>(a.kp) + s0 * a.ps.tok + hoff;
+    ks.block = static_cast<const uint16_t*>(a.k) + boff;
+    ks.ptok = a.ps.tok;
+    ks.btok = a.qs.tok;
+    ks.np = static_cast<int>(s1 - s0 < 0x7fffff00 ? s1 - s0 : 0x7fffff00);
+    ks.nk = ks.np + a.B;
+    const uint16_t* vprefix = static_cast<const uint16_t*>(a.vp) + s0 * a.ps.tok + hoff;
+    const uint16_t* vblock = static_cast<const uint16_t*>(a.v) + boff;
+    const int nch = (ks.nk + 31) / 32;
+
+    // Q fragments: query ln (rows past B read row B - 1; never stored)
+    bf16x8 qf[C::NKB];
+    {
+        const int qi = ln < a.B ? ln : a.B - 1;
+        const uint16_t* qr = static_cast<const uint16_t*>(a.q) + boff + qi * a.qs.tok + g * (D / 2);
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) qf[kb] = *reinterpret_cast<const bf16x8*>(qr + 8 * kb);
+    }
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x16 acc[C::CT];
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct) acc[ct] = f32x16{};
+    bf16x8 kf[C::NKB];
+    u32x4 vr[C::VQ];
+    if (wv < nch) sa_load_chunk<D>(ks, wv, lane, kf, vr, vprefix, vblock);
+
+    for (int c = wv; c < nch; c += 4) {
+        // V rows of this chunk into the wave's tile (LDS operations of one
+        // wave execute in order, so no barrier is needed)
+#pragma unroll
+        for (int i = 0; i < C::VQ; ++i) {
+            const int idx = lane + 64 * i, t = idx / CH, ch = idx % CH;
+            *reinterpret_cast<u32x4*>(Vt + t * D + (((2 * ch) ^ lds_piece_swizzle<D / 4>(t)) << 2)) = vr[i];
+        }
+        f32x16 sacc = f32x16{};
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) sacc = mfma32(kf[kb], qf[kb], sacc);
+        if (c + 4 < nch) sa_load_chunk<D>(ks, c + 4, lane, kf, vr, vprefix, vblock);
+
+        // online softmax of query ln over the chunk's keys 8 (v/4) + 4 g + v%4
+        float mc = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int j = 32 * c + 8 * (v >> 2) + 4 * g + (v & 3);
+            const float sv = j < ks.nk ? sacc[v] * a.scale : -INFINITY;
+            sacc[v] = sv;
+            mc = fmaxf(mc, sv);
+        }
+        mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
+        const float m_new = fmaxf(m_run, mc);
+        const float alpha = __expf(m_run - m_new);
+        bf16x8 pp[2];
+        float ls = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float p = __expf(sacc[v] - m_new);
+            ls += p;
+            pp[v >> 3][v & 7] = static_cast<__bf16>(p);
+        }
+        ls += __shfl_xor(ls, 32, 64);
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+#pragma unroll
+        for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[ct][v] *= alpha;
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int ct = 0; ct < C::CT; ++ct) acc[ct] = mfma32(vt_frag_ps<D / 4>(Vt, 32 * ct, kb, lane), pp[kb], acc[ct]);
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // merge the four waves: acc as [w][d][query], then m and l per [w][query]
+    __syncthreads();
+    float* const Ma = reinterpret_cast<float*>(smem);
+    float* const Mm = Ma + 4 * D * 32;
+    float* const Ml = Mm + 4 * 32;
+#pragma unroll
+    for (int ct = 0; ct < C::CT; ++ct)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int dcol = 32 * ct + 8 * (v >> 2) + 4 * g + (v & 3);
+            Ma[(wv * D + dcol) * 32 + ln] = acc[ct][v];
+        }
+    if (g == 0) {
+        Mm[wv * 32 + ln] = m_run;
+        Ml[wv * 32 + ln] = l_run;
+    }
+    __syncthreads();
+    // thread -> (query, 8 columns), 16-byte row stores
+    for (int idx = tid; idx < 32 * CH; idx += 256) {
+        const int qi = idx / CH, c8 = (idx % CH) * 8;
+        if (qi >= a.B) continue;
+        float mw[4], M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            mw[w] = Mm[w * 32 + qi];
+            M = fmaxf(M, mw[w]);
+        }
+        float den = 0.0f, sc[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            sc[w] = __expf(mw[w] - M);
+            den += sc[w] * Ml[w * 32 + qi];
+        }
+        const float inv = 1.0f / den;
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float y[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int dcol = c8 + 2 * e + u;
+                float num = 0.0f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) num += sc[w] * Ma[(w * D + dcol) * 32 + qi];
+                y[u] = num * inv;
+            }
+            pk[e] = static_cast<uint32_t>(bf16_bits(y[0])) | (static_cast<uint32_t>(bf16_bits(y[1])) << 16);
+        }
+        uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
+                         static_cast<int64_t>(h) * a.os.head + static_cast<int64_t>(qi) * a.os.tok + c8;
+        *reinterpret_cast<u32x4*>(orow) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    }
+}
+
+// Plain kernel for every size and both I/O dtypes, fp32 arithmetic with
+// accurate exponentials: one work-group per (request, head, query); 256 keys
+// per step, one thread per key for the scores and one per column for the
+// weighted sum of the values.
+constexpr int kGenThreads = 256;
+
+__device__ __forceinline__ float block_max(float x, float* red)
+{
+    x = wave_max(x);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (lane == 0) red[wv] = x;
+    __syncthreads();
+    float y = red[0];
+    for (int w = 1; w < kGenThreads / 64; ++w) y = fmaxf(y, red[w]);
+    __syncthreads();
+    return y;
+}
+
+__device__ __forceinline__ float block_sum(float x, float* red)
+{
+    x = wave_sum(x);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (lane == 0) red[wv] = x;
+    __syncthreads();
+    float y = 0.0f;
+    for (int w = 0; w < kGenThreads / 64; ++w) y += red[w];
+    __syncthreads();
+    return y;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kGenThreads) void prefix_attn_generic_kernel(PrefixArgs a)
+{
+    const int64_t blk = blockIdx.x;
+    const int i = static_cast<int>(blk % a.B);
+    const int64_t pr = blk / a.B;
+    const int h = static_cast<int>(pr % a.H);
+    const int r = static_cast<int>(pr / a.H);
+    const int tid = threadIdx.x;
+    __shared__ float qs[128];
+    __shared__ float ps[kGenThreads];
+    __shared__ float red[kGenThreads / 64];
+
+    int64_t s0 = a.seq_offsets[r], s1 = a.seq_offsets[r + 1];
+    s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);
+    s1 = s1 < s0 ? s0 : (s1 > a.total_tokens ? a.total_tokens : s1);
+    const int64_t np = s1 - s0, nk = np + a.B;
+    const int64_t hoff = static_cast<int64_t>(h) * a.ps.head;
+    const int64_t boff = static_cast<int64_t>(r) * a.qs.req + static_cast<int64_t>(h) * a.qs.head;
+    const T* kp = static_cast<const T*>(a.kp) + s0 * a.ps.tok + hoff;
+    const T* vp = static_cast<const T*>(a.vp) + s0 * a.ps.tok + hoff;
+    const T* kb = static_cast<const T*>(a.k) + boff;
+    const T* vb = static_cast<const T*>(a.v) + boff;
+    if (tid < a.d) qs[tid] = ld_elem(static_cast<const T*>(a.q), boff + i * a.qs.tok + tid);
+    __syncthreads();
+
+    float m = -INFINITY, l = 0.0f, acc = 0.0f;
+    for (int64_t t0 = 0; t0 < nk; t0 += kGenThreads) {
+        const int64_t t = t0 + tid;
+        float s = -INFINITY;
+        if (t < nk) {
+            const T* kr = t < np ? kp + t * a.ps.tok : kb + (t - np) * a.qs.tok;
+            float dot = 0.0f;
+            for (int e = 0; e < a.d; ++e) dot = fmaf(qs[e], ld_elem(kr, e), dot);
+            s = dot * a.scale;
+        }
+        const float m_new = fmaxf(m, block_max(s, red));
+        const float alpha = expf(m - m_new);
+        const float p = t < nk ? expf(s - m_new) : 0.0f;
+        ps[tid] = p;
+        l = l * alpha + block_sum(p, red);
+        if (tid < a.d) {
+            acc *= alpha;
+            const int64_t tn = nk - t0 < kGenThreads ? nk - t0 : kGenThreads;
+            for (int64_t j = 0; j < tn; ++j) {
+                const int64_t tt = t0 + j;
+                const T* vr = tt < np ? vp + tt * a.ps.tok : vb + (tt - np) * a.qs.tok;
+                acc = fmaf(ps[j], ld_elem(vr, tid), acc);
+            }
+        }
+        m = m_new;
+        __syncthreads();
+    }
+    if (tid < a.d) {
+        T* out = static_cast<T*>(a.out) + static_cast<int64_t>(r) * a.os.req + static_cast<int64_t>(h) * a.os.head +
+                 static_cast<int64_t>(i) * a.os.tok;
+        st_elem(out, tid, acc / l);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefix_attention_mfma(const PrefixArgs& a, hipStream_t s)
+{
+    if (a.io != BHA_BF16 || a.B > 32) return hipErrorNotSupported;
+    // per-lane offsets within a block and a chunk are 32-bit
+    if (a.qs.tok >= (int64_t(1) << 25) || a.ps.tok >= (int64_t(1) << 25)) return hipErrorNotSupported;
+    const dim3 grid(static_cast<uint32_t>(a.R * a.H)), block(256);
+    if (a.d == 128) hipLaunchKernelGGL(prefix_attn_mfma_kernel<128>, grid, block, 0, s, a);
+    else if (a.d == 64) hipLaunchKernelGGL(prefix_attn_mfma_kernel<64>, grid, block, 0, s, a);
+    else return hipErrorNotSupported;
+    return hipGetLastError();
+}
+
+hipError_t launch_prefix_attention_generic(const PrefixArgs& a, hipStream_t s)
+{
+    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * a.B)), block(kGenThreads);
+    if (a.io == BHA_BF16) hipLaunchKernelGGL(prefix_attn_generic_kernel<uint16_t>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(prefix_attn_generic_kernel<float>, grid, block, 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace bha

@@ -239,3 +239,30 @@ def test_forward_commit_validation(lib):
     assert fwd_commit(lib, _dims(io_dtype=5)) == DTYPE
     assert fwd_commit(lib, _dims(), num_slots=0) == DIMS
     assert fwd_commit(lib, _dims(), outs=bha_strides(0, 256, 128)) == STRIDE
+
+
+def prefix_attn(lib, dims, q=FAKE, k=FAKE, v=FAKE, kp=FAKE, vp=FAKE, kps=None, offs=FAKE, total=100,
+                out=FAKE + (1 << 24), qs=None, outs=None):
+    qs = qs or _st()
+    outs = outs or _st()
+    kps = kps or _st(req=0)
+    P = ctypes.c_void_p
+    return lib.bha_prefix_attention(ctypes.byref(dims) if dims is not None else None, P(q), P(k), P(v),
+                                    ctypes.byref(qs), P(kp), P(vp), ctypes.byref(kps), P(offs), total, P(out),
+                                    ctypes.byref(outs), P(0))
+
+
+def test_prefix_attention_validation(lib):
+    assert prefix_attn(lib, None) == NULL
+    assert prefix_attn(lib, _dims(num_requests=0), q=0, k=0, v=0, kp=0, vp=0, offs=0, out=0) == OK
+    for name in ("q", "k", "v", "kp", "vp", "offs", "out"):
+        assert prefix_attn(lib, _dims(), **{name: 0}) == NULL, name
+    assert prefix_attn(lib, _dims(), offs=FAKE + 2) == ALIGN
+    assert prefix_attn(lib, _dims(), kp=FAKE + 8) == ALIGN
+    assert prefix_attn(lib, _dims(), total=-1) == DIMS
+    assert prefix_attn(lib, _dims(), total=1 << 40) == DIMS
+    assert prefix_attn(lib, _dims(), kps=_st(req=0, tok=2 * 128 + 4)) == STRIDE
+    assert prefix_attn(lib, _dims(), outs=bha_strides(0, 256, 128)) == STRIDE
+    assert prefix_attn(lib, _dims(head_dim=96)) == UNSUP
+    assert prefix_attn(lib, _dims(block_size=65)) == UNSUP
+    assert prefix_attn(lib, _dims(io_dtype=3)) == DTYPE

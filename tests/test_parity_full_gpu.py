@@ -9,7 +9,9 @@ oracle then checks, one pair at a time:
   * the chained GPU state of the shortest and longest requests against the
     oracle's state built from scratch over their whole prefix;
   * one ragged prefill launch over the same prefix tokens (packed): every pair
-    against the chained state, the tracked requests against the oracle.
+    against the chained state, the tracked requests against the oracle;
+  * one softmax prefix-attention launch over the same packed prefix and block,
+    on sampled pairs (the shortest and longest prefixes among them).
 Bars: normwise 2e-2 (bf16 I/O, fp32 accumulation and state).
 """
 import os
@@ -48,6 +50,25 @@ def _pairwise_err(got, ref, d, F):
     return out
 
 
+def _check_prefix_attention(name, q, k, v, pk, pv, offs, y, track, seed, n_pairs=6):
+    # sampled (request, head) pairs, the shortest and longest prefixes among them
+    R, B, H, d = q.shape
+    rng = np.random.default_rng(seed + 1)
+    rs = list(track) + [int(x) for x in rng.integers(0, R, size=n_pairs - len(track))]
+    hs = rng.integers(0, H, size=len(rs))
+    o = offs.cpu().numpy()
+    err = 0.0
+    for r, h in zip(rs, hs):
+        a, b = int(o[r]), int(o[r + 1])
+        ref = oracle.prefix_attention(to_host(q[r, :, h]), to_host(k[r, :, h]), to_host(v[r, :, h]),
+                                      to_host(pk[a:b, h]), to_host(pv[a:b, h]))
+        err = max(err, normwise_err(to_host(y[r, :, h]), ref, None))
+    lens = [int(o[r + 1] - o[r]) for r in rs]
+    print(f"[{name}] softmax prefix attention err {err:.2e} over {len(rs)} sampled pairs "
+          f"(prefix tokens {min(lens)}..{max(lens)})", flush=True)
+    assert err <= TOL
+
+
 def _run_full(name, dev, n_pairs=24, seed=0):
     case = synth.make_case(name, with_prefix=False, with_qkv=False)
     R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B
@@ -69,11 +90,15 @@ def _run_full(name, dev, n_pairs=24, seed=0):
                 kept[r][0].append(kb[j].float().cpu().numpy())
                 kept[r][1].append(vb[j].float().cpu().numpy())
     sel = torch.from_numpy(case.slot_ids.astype(np.int64)).to(dev)
+    q, k, v = synth.device_step_qkv(name, 0, R, dev, layer=0)
     pk, pv, offs = synth.device_packed_prefix(name, case.n_blocks, dev, layer=0)
     state_p = bha.new_state(case.num_slots, H, d, FW, dev)
     bha.state_prefill(pk, pv, offs, w, state_p, slots)
+    # the softmax attention over the whole prefix that the hybrid step replaces
+    y_sm = bha.prefix_attention(q, k, v, pk, pv, offs)
     torch.cuda.synchronize()
-    del pk, pv
+    _check_prefix_attention(name, q, k, v, pk, pv, offs, y_sm, track, seed)
+    del pk, pv, y_sm
     e_pc = _pairwise_err(state_p[sel], state[sel], d, F)
     prefilled = state_p[sel].cpu().numpy()
     del state_p
@@ -81,7 +106,6 @@ def _run_full(name, dev, n_pairs=24, seed=0):
           flush=True)
     assert e_pc[0] <= TOL and e_pc[1] <= TOL
 
-    q, k, v = synth.device_step_qkv(name, 0, R, dev, layer=0)
     out = bha.block_forward(q, k, v, w, gamma, state, slots)
     torch.cuda.synchronize()
     pre = state[torch.from_numpy(case.slot_ids.astype(np.int64)).to(dev)].cpu().numpy()  # [R][H][rec]

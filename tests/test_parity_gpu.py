@@ -383,3 +383,71 @@ def test_forward_commit_equals_forward_then_commit(dev, io, b):
     S_f, Z_f = record_to_plain(run.state.cpu().numpy()[case.slot_ids], case.d, case.F)
     S_s, Z_s = record_to_plain(s_sep.cpu().numpy()[case.slot_ids], case.d, case.F)
     assert normwise_err(S_f, S_s, (2, 3)) <= 1e-5 and normwise_err(Z_f, Z_s, (2,)) <= 1e-5
+
+
+PREFIX = [("bf16", 128, 32), ("bf16", 128, 17), ("bf16", 64, 32), ("bf16", 64, 5), ("bf16", 128, 40),
+          ("f32", 128, 32), ("f32", 64, 9)]
+
+
+@pytest.mark.parametrize("io,d,b", PREFIX)
+def test_prefix_attention_matches_oracle(dev, io, d, b):
+    # softmax attention over ragged packed prefixes of 0, 1, 33, 127, 300 and
+    # ~330 tokens plus the block; q, k, v as views of one fused tensor and the
+    # prefix k, v as views of another
+    nb = -(-330 // b)
+    case = synth.make_case("tiny", R=6, H=2, d=d, FW=64, B=b, io=io, blocks=(nb, nb + 1), gamma="uniform")
+    lens = np.minimum(np.array([0, 1, 33, 127, 300, 10**6]), case.n_blocks * b)
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    kp = np.concatenate([case.prefix_k[r][:lens[r]] for r in range(case.R)])
+    vp = np.concatenate([case.prefix_v[r][:lens[r]] for r in range(case.R)])
+    kvp = to_device(np.stack([kp, vp], axis=1), io, dev)  # [T][2][H][d]
+    qkv = to_device(np.stack([case.q, case.k, case.v], axis=2), io, dev)  # [R][B][3][H][d]
+    y = to_host(bha.prefix_attention(qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2], kvp[:, 0], kvp[:, 1],
+                                     torch.from_numpy(offs).to(dev)))
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(y))
+    worst = 0.0
+    for r in range(case.R):
+        for h in range(case.H):
+            ref = oracle.prefix_attention(case.q[r, :, h], case.k[r, :, h], case.v[r, :, h],
+                                          kp[offs[r]:offs[r + 1], h], vp[offs[r]:offs[r + 1], h])
+            worst = max(worst, normwise_err(y[r, :, h], ref, None))
+    _log(f"[prefix-attn] io={io} d={d} B={b} lens={lens.tolist()} err {worst:.2e}")
+    assert worst <= TOL[io]
+
+
+def test_prefix_attention_empty_prefix_is_block_softmax(dev):
+    # with no prefix rows (total_tokens 0, kp/vp empty) the result is plain
+    # softmax attention within the block: the oracle's block forward at gate 0
+    case = synth.make_case("tiny", R=3, H=2, d=128, FW=64, B=32, io="bf16", blocks=(0, 0), gamma="uniform")
+    q, k, v = (to_device(x, "bf16", dev) for x in (case.q, case.k, case.v))
+    empty = torch.empty((0, case.H, case.d), dtype=torch.bfloat16, device=dev)
+    offs = torch.zeros(case.R + 1, dtype=torch.int32, device=dev)
+    y = to_host(bha.prefix_attention(q, k, v, empty, empty, offs))
+    S = np.zeros((case.R, case.H, case.F, case.d))
+    Z = np.zeros((case.R, case.H, case.F))
+    ref = oracle.block_forward_batch(pairs(case.q), pairs(case.k), pairs(case.v), case.w,
+                                     np.zeros(case.H, dtype=np.float32), S, Z, nthreads=NTHREADS)
+    err = normwise_err(pairs(y), ref, (2, 3))
+    _log(f"[prefix-attn] empty prefix err {err:.2e}")
+    assert err <= TOL["bf16"]
+
+
+def test_prefix_attention_offsets_are_clamped(dev):
+    # each request's range is clamped on the device to
+    # 0 <= seq_offsets[r] <= seq_offsets[r+1] <= total_tokens; every request's
+    # output equals a one-request call over its clamped range
+    case = synth.make_case("tiny", R=4, H=2, d=64, FW=64, B=16, io="bf16", blocks=(6, 6), gamma="uniform")
+    kp = np.concatenate([case.prefix_k[r] for r in range(case.R)])
+    vp = np.concatenate([case.prefix_v[r] for r in range(case.R)])
+    T = kp.shape[0]
+    q, k, v = (to_device(x, "bf16", dev) for x in (case.q, case.k, case.v))
+    kd, vd = to_device(kp, "bf16", dev), to_device(vp, "bf16", dev)
+    bad = [-5, 40, 20, T + 50, T + 100]
+    clamped = [(0, 40), (40, 40), (20, T), (T, T)]
+    y = bha.prefix_attention(q, k, v, kd, vd, torch.tensor(bad, dtype=torch.int32, device=dev))
+    for r, (a, b) in enumerate(clamped):
+        y_r = bha.prefix_attention(q[r:r + 1], k[r:r + 1], v[r:r + 1], kd, vd,
+                                   torch.tensor([a, b], dtype=torch.int32, device=dev))
+        torch.cuda.synchronize()
+        assert torch.equal(y[r], y_r[0]), r
