@@ -159,6 +159,74 @@ def cpu_baseline(layer, case, denoise, n_req, log):
     }
 
 
+def prefix_sweep(requests, prefixes, log) -> dict:
+    """Kernel-level comparison of one block-hybrid step with exact softmax
+    attention over the prefix: a 32-token block (16 heads, d = 128, FW = 64)
+    of each of ``requests`` requests over a prefix of P tokens, for every P in
+    ``prefixes``. Each launch is timed with HIP events on its stream, cold (a
+    1 GiB buffer is read between launches, outside the events, so the
+    256 MB Infinity Cache and L2 start without the operands; a read leaves no
+    dirty lines whose write-back would be charged to the timed launch) and warm
+    (back to back); medians of 10 and 20 launches."""
+    import numpy as np
+    import torch
+
+    import linear_attention_block_amd as bha
+    import synth
+
+    dev = torch.device("cuda:0")
+    name = "longctx2k"  # 16 heads, d = 128, FW = 64, B = 32, bf16
+    H, d, FW, B = 16, 128, 64, 32
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def timed(fn, n, cold):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for _ in range(3):
+            fn()
+        for e0, e1 in evs:
+            if cold:
+                torch.sum(flush, dim=0, out=flush_sink)
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+    rows = []
+    for R in requests:
+        w, gamma = synth.device_layer_params(name, 0, dev)
+        q, k, v = synth.device_step_qkv(name, 0, R, dev, layer=0)
+        slots = torch.arange(R, dtype=torch.int32, device=dev)
+        for P in prefixes:
+            pk, pv, offs = synth.device_packed_prefix(name, np.full(R, P // B), dev, layer=0)
+            state = bha.new_state(R, H, d, FW, dev)
+            bha.state_prefill(pk, pv, offs, w, state, slots)
+            out_h, out_s = torch.empty_like(q), torch.empty_like(q)
+            hyb = bha.prepare_forward(q, k, v, w, gamma, state, slots, out_h)
+            sm = bha.prepare_prefix_attention(q, k, v, pk, pv, offs, out_s)
+            fb = forward_bytes(R, H, d, FW, B)
+            sb = prefix_attention_bytes(R * P, R, H, d, B)
+            row = {"requests": R, "prefix": P,
+                   "splits": bha.prefix_attention_workspace(R, H, d, B, R * P) // (R * H * (32 * d + 64) * 4) or 1}
+            for tag, cold, n in (("cold", True, 10), ("warm", False, 20)):
+                th, ts = timed(hyb, n, cold), timed(sm, n, cold)
+                row[f"hybrid_us_{tag}"] = th
+                row[f"softmax_us_{tag}"] = ts
+                row[f"softmax_over_hybrid_{tag}"] = ts / th
+                row[f"hybrid_GBps_{tag}"] = fb / th / 1e3
+                row[f"softmax_GBps_{tag}"] = sb / ts / 1e3
+            log(f"sweep R={R} P={P}: hybrid {row['hybrid_us_cold']:.1f} us cold / {row['hybrid_us_warm']:.1f} warm, "
+                f"softmax {row['softmax_us_cold']:.1f} / {row['softmax_us_warm']:.1f} us "
+                f"({row['splits']} splits, {row['softmax_GBps_cold']:.0f} GB/s cold); "
+                f"ratio {row['softmax_over_hybrid_cold']:.1f}x cold, {row['softmax_over_hybrid_warm']:.1f}x warm")
+            rows.append(row)
+            del hyb, sm, pk, pv, offs, state, out_h, out_s
+            torch.cuda.empty_cache()
+    return {"comparison": "one block-hybrid forward vs exact softmax attention over the prefix "
+                          f"(B={B}, H={H}, d={d}, FW={FW}, bf16; per-launch medians)", "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +245,10 @@ def main() -> int:
                     help="continuous batching with staggered blocks: request r finishes its block at denoising "
                          "step r mod 32, so every step is one bha_block_forward_commit whose mask commits "
                          "1/32 of the requests")
+    ap.add_argument("--prefix-sweep", action="store_true",
+                    help="instead of the block cycle: the kernel-level comparison of one block-hybrid forward "
+                         "with softmax attention over prefixes of 1K..32K tokens (prints its own JSON line)")
+    ap.add_argument("--sweep-requests", default="1,64")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -201,6 +273,10 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     bha.load_library()
+    if args.prefix_sweep:
+        reqs = [int(x) for x in args.sweep_requests.split(",")]
+        print(json.dumps(prefix_sweep(reqs, [1024, 2048, 4096, 8192, 16384, 32768], log)), flush=True)
+        return 0
     case = synth.make_case(args.config, with_prefix=False, with_qkv=False)
     R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B
     nl, nd = args.layers, args.denoise

@@ -203,13 +203,25 @@ int bha_state_prefill(const bha_dims* dims, const void* k, const void* v, const 
  *                  (kvp->req is not used); may be NULL when total_tokens == 0.
  *   seq_offsets  : int32 [R + 1] device, clamped on the device to
  *                  0 <= seq_offsets[r] <= seq_offsets[r+1] <= total_tokens.
+ *   workspace    : device scratch of workspace_bytes (16-byte aligned), owned
+ *                  by the caller, or NULL. When the (request, head) pairs are
+ *                  too few to fill the GPU, each pair's keys are split over
+ *                  several work-groups whose partial results go here; with a
+ *                  shorter (or no) workspace the call splits less (or not at
+ *                  all) and is slower but gives the same result up to rounding.
+ *                  bha_prefix_attention_workspace gives the size for the full
+ *                  split. Calls that share a workspace must not overlap.
  *   dims->feat_half must be a supported value but is not used.
- * No state is read; nothing is written but out.
+ * No state is read; nothing is written but out and the workspace.
  */
 int bha_prefix_attention(const bha_dims* dims, const void* q, const void* k, const void* v,
                          const bha_strides* qkv, const void* kp, const void* vp, const bha_strides* kvp,
-                         const int32_t* seq_offsets, int64_t total_tokens, void* out,
-                         const bha_strides* outs, hipStream_t stream);
+                         const int32_t* seq_offsets, int64_t total_tokens, void* workspace,
+                         int64_t workspace_bytes, void* out, const bha_strides* outs, hipStream_t stream);
+
+/* Workspace bytes bha_prefix_attention uses for these dims and total_tokens
+ * (0: no split), or a negative bha_status for invalid arguments. */
+int64_t bha_prefix_attention_workspace(const bha_dims* dims, int64_t total_tokens);
 
 /* Floats in one (slot, head) state record: (d + 1) * 2 * FW. Returns -1 for
  * unsupported sizes. Host only; touches no device. */

@@ -42,7 +42,7 @@ BHA_BF16 = 1
 # Every symbol include/bha.h declares.
 EXPORTED_SYMBOLS = (
     "bha_feature_map", "bha_block_forward", "bha_block_forward_commit", "bha_state_commit", "bha_state_prefill",
-    "bha_prefix_attention",
+    "bha_prefix_attention", "bha_prefix_attention_workspace",
     "bha_state_record_floats", "bha_status_string", "bha_version",
 )
 
@@ -94,8 +94,10 @@ def load_library():
     lib.bha_block_forward_commit.restype = ctypes.c_int
     lib.bha_state_prefill.argtypes = [PD, P, P, PS, P, I64, P, I64, P, I32, P, P]
     lib.bha_state_prefill.restype = ctypes.c_int
-    lib.bha_prefix_attention.argtypes = [PD, P, P, P, PS, P, P, PS, P, I64, P, PS, P]
+    lib.bha_prefix_attention.argtypes = [PD, P, P, P, PS, P, P, PS, P, I64, P, I64, P, PS, P]
     lib.bha_prefix_attention.restype = ctypes.c_int
+    lib.bha_prefix_attention_workspace.argtypes = [PD, I64]
+    lib.bha_prefix_attention_workspace.restype = ctypes.c_int64
     lib.bha_state_record_floats.argtypes = [I32, I32]
     lib.bha_state_record_floats.restype = I64
     lib.bha_status_string.argtypes = [ctypes.c_int]
@@ -326,7 +328,7 @@ def state_prefill(k, v, seq_offsets, w, state, slot_ids, *, stream=None) -> None
         raise BhaError("bha_state_prefill", st)
 
 
-def _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream):
+def _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream, workspace):
     qs = _tok_strides(q, "q")
     R, B, H, d = q.shape
     for t, n in ((k, "k"), (v, "v")):
@@ -351,18 +353,39 @@ def _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream):
     dims = bha_dims(R, H, d, 64, B, _io_dtype(q), float(scale))
     ps = bha_strides(0, kp.stride(0), kp.stride(1))
     T = kp.shape[0]
+    if workspace is None:
+        need = load_library().bha_prefix_attention_workspace(ctypes.byref(dims), T)
+        if need < 0:
+            raise BhaError("bha_prefix_attention_workspace", int(need))
+        workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=q.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    _check_device(q.device, workspace)
     return (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(qs), _ptr(kp), _ptr(vp), ctypes.byref(ps),
-            _ptr(seq_offsets), T, _ptr(out), ctypes.byref(os_), _stream(q.device, stream)), (dims, qs, ps, os_)
+            _ptr(seq_offsets), T, _ptr(workspace), workspace.numel(), _ptr(out), ctypes.byref(os_),
+            _stream(q.device, stream)), (dims, qs, ps, os_, workspace)
 
 
-def prefix_attention(q, k, v, kp, vp, seq_offsets, *, out=None, scale: float = 0.0, stream=None) -> torch.Tensor:
+def prefix_attention_workspace(R, H, d, B, total_tokens, dtype=torch.bfloat16) -> int:
+    """Workspace bytes prefix_attention uses for these sizes (0: none)."""
+    dims = bha_dims(R, H, d, 64, B, BHA_BF16 if dtype == torch.bfloat16 else BHA_F32, 0.0)
+    n = load_library().bha_prefix_attention_workspace(ctypes.byref(dims), int(total_tokens))
+    if n < 0:
+        raise BhaError("bha_prefix_attention_workspace", int(n))
+    return int(n)
+
+
+def prefix_attention(q, k, v, kp, vp, seq_offsets, *, out=None, scale: float = 0.0, workspace=None,
+                     stream=None) -> torch.Tensor:
     """Exact softmax attention of each block's queries over its request's
     packed prefix (rows seq_offsets[r] .. seq_offsets[r+1]-1 of kp, vp,
-    [T][H][d]) and the block's own keys; returns ``out`` [R][B][H][d]."""
+    [T][H][d]) and the block's own keys; returns ``out`` [R][B][H][d].
+    ``workspace`` (uint8 device tensor) holds split partial results; when None
+    one of the size bha_prefix_attention_workspace gives is allocated."""
     lib = load_library()
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
-    args, _keep = _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream)
+    args, _keep = _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream, workspace)
     st = lib.bha_prefix_attention(*args)
     if st != 0:
         raise BhaError("bha_prefix_attention", st)
@@ -398,9 +421,11 @@ def prepare_forward_commit(q, k, v, w, gamma, state, slot_ids, out, *, commit_ma
     return _Prepared(load_library().bha_block_forward_commit, "bha_block_forward_commit", args, keep)
 
 
-def prepare_prefix_attention(q, k, v, kp, vp, seq_offsets, out, *, scale: float = 0.0, stream=None):
-    """Marshal a bha_prefix_attention call once, for launch-rate-bound loops."""
-    args, keep = _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream)
+def prepare_prefix_attention(q, k, v, kp, vp, seq_offsets, out, *, scale: float = 0.0, workspace=None,
+                             stream=None):
+    """Marshal a bha_prefix_attention call once (its workspace included), for
+    launch-rate-bound loops."""
+    args, keep = _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream, workspace)
     keep = keep + (q, k, v, kp, vp, seq_offsets, out)
     return _Prepared(load_library().bha_prefix_attention, "bha_prefix_attention", args, keep)
 

@@ -160,10 +160,26 @@ extern "C" int bha_state_prefill(const bha_dims* dims, const void* k, const void
     return launch_status(e);
 }
 
+static int64_t prefix_workspace_bytes(const bha_dims* d, int splits)
+{
+    if (splits < 2) return 0;
+    return static_cast<int64_t>(d->num_requests) * d->num_heads * splits * prefix_part_floats(d->head_dim) * 4;
+}
+
+extern "C" int64_t bha_prefix_attention_workspace(const bha_dims* dims, int64_t total_tokens)
+{
+    int st = validate_dims(dims);
+    if (st != BHA_OK) return st;
+    if (total_tokens < 0 || total_tokens > INT32_MAX) return BHA_ERR_DIMS;
+    if (dims->num_requests == 0) return 0;
+    return prefix_workspace_bytes(dims, prefix_attention_splits(dims->num_requests, dims->num_heads, dims->head_dim,
+                                                                dims->block_size, dims->io_dtype, total_tokens));
+}
+
 extern "C" int bha_prefix_attention(const bha_dims* dims, const void* q, const void* k, const void* v,
                                     const bha_strides* qkv, const void* kp, const void* vp, const bha_strides* kvp,
-                                    const int32_t* seq_offsets, int64_t total_tokens, void* out,
-                                    const bha_strides* outs, hipStream_t stream)
+                                    const int32_t* seq_offsets, int64_t total_tokens, void* workspace,
+                                    int64_t workspace_bytes, void* out, const bha_strides* outs, hipStream_t stream)
 {
     int st = validate_dims(dims);
     if (st != BHA_OK) return st;
@@ -190,7 +206,18 @@ extern "C" int bha_prefix_attention(const bha_dims* dims, const void* q, const v
         ps.tok = qkv->tok;
         ps.head = qkv->head;
     }
+    if (workspace_bytes < 0) return BHA_ERR_DIMS;
+    if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return BHA_ERR_ALIGN;
+    // the split the workspace allows (fewer splits, down to none, when it is short)
+    int splits = prefix_attention_splits(dims->num_requests, dims->num_heads, dims->head_dim, dims->block_size,
+                                         dims->io_dtype, total_tokens);
+    const int64_t per_split = prefix_workspace_bytes(dims, 2) / 2;
+    const int64_t fit = workspace ? workspace_bytes / per_split : 0;
+    if (splits > fit) splits = static_cast<int>(fit);
+    if (splits < 2) splits = 1;
     PrefixArgs a;
+    a.part = splits > 1 ? static_cast<float*>(workspace) : nullptr;
+    a.splits = splits;
     a.R = dims->num_requests; a.H = dims->num_heads; a.d = dims->head_dim;
     a.B = dims->block_size; a.io = dims->io_dtype;
     a.scale = dims->scale > 0.0f ? dims->scale : 1.0f / sqrtf((float)dims->head_dim);

@@ -76,7 +76,21 @@ struct PrefixArgs {
     int64_t total_tokens;
     void* out;
     bha_strides os;
+    // key-sequence split: with splits > 1 each (request, head) pair is spread
+    // over `splits` work-groups that leave fp32 partial results in `part`
+    // (splits * R * H records of prefix_part_floats(d) floats), merged by a
+    // second launch
+    float* part;
+    int splits;
 };
+
+// Floats of one partial-result record of the split prefix attention: the
+// unnormalised output [32][d], then the running maximum and normaliser [32] each.
+__host__ __device__ inline int64_t prefix_part_floats(int d) { return 32 * static_cast<int64_t>(d) + 64; }
+
+// Key-sequence splits the matrix-core prefix attention uses for these sizes
+// (1 when the pairs alone fill the GPU or the path does not apply).
+int prefix_attention_splits(int R, int H, int d, int B, int io, int64_t total_tokens);
 
 struct PhiArgs {
     int R, H, d, FW, B, io;

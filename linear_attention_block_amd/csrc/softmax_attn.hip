@@ -20,6 +20,12 @@
 // (ds_read_b64_tr_b16) as the A operand of P V, P coming straight from the
 // score accumulators. The next chunk's K and V loads are issued before the
 // current chunk's arithmetic.
+//
+// When the (request, head) pairs alone cannot fill the GPU (a few requests
+// with long prefixes), each pair's chunk sequence is cut into `splits`
+// contiguous ranges, one work-group each; a work-group then leaves its
+// unnormalised output, maximum and normaliser in fp32, and a second launch
+// rescales the partial results to their common maximum and sums them.
 #include "bha_device.hpp"
 #include "bha_internal.hpp"
 #include "bha_mfma.hpp"
@@ -47,31 +53,38 @@ struct SaCfg {
     static constexpr int NKB = D / 16;         // k-steps of the score contraction
     static constexpr int CT = D / 32;          // 32-column output tiles per wave
     static constexpr int VQ = 32 * (D / 8) / 64;  // 16-byte V chunks per lane per key chunk
-    static constexpr int TILE = 32 * D;        // bf16 elements of one wave's V tile
-    static constexpr int LDS_LOOP = 4 * TILE * 2;
+    static constexpr int TILE = 32 * D;        // bf16 elements of one wave's K or V tile
+    static constexpr int LDS_LOOP = 2 * 4 * TILE * 2;  // K and V tiles of four waves
     static constexpr int LDS_MERGE = 4 * D * 32 * 4 + 2 * 4 * 32 * 4;
     static constexpr int LDS = LDS_LOOP > LDS_MERGE ? LDS_LOOP : LDS_MERGE;
 };
 
+// Row-contiguous loads of one 32-key chunk: 16 lanes per 256-byte row (d =
+// 128; 8 per row at d = 64), so each load instruction covers whole rows.
 template <int D>
-__device__ __forceinline__ void sa_load_chunk(const KeySource& ks, int c, int lane, bf16x8 (&kf)[D / 16],
+__device__ __forceinline__ void sa_load_chunk(const KeySource& ks, int c, int lane, u32x4 (&kr)[SaCfg<D>::VQ],
                                               u32x4 (&vr)[SaCfg<D>::VQ], const uint16_t* vprefix,
                                               const uint16_t* vblock)
 {
     constexpr int CH = D / 8;
-    const int m = lane & 31, g = lane >> 5;
-    const uint16_t* kr = ks.row(32 * c + m) + g * (D / 2);
-#pragma unroll
-    for (int kb = 0; kb < D / 16; ++kb) kf[kb] = *reinterpret_cast<const bf16x8*>(kr + 8 * kb);
-    // V rows: the same key rows, from the value tensors
 #pragma unroll
     for (int i = 0; i < SaCfg<D>::VQ; ++i) {
         const int idx = lane + 64 * i, t = idx / CH, ch = idx % CH;
         int tt = 32 * c + t;
-        tt = tt < ks.nk ? tt : ks.nk - 1;
-        const uint16_t* vrow = tt < ks.np ? vprefix + tt * ks.ptok : vblock + (tt - ks.np) * ks.btok;
-        vr[i] = *reinterpret_cast<const u32x4*>(vrow + ch * 8);
+        tt = tt < ks.nk ? tt : ks.nk - 1;  // past the end: the last key (masked)
+        const int64_t off = tt < ks.np ? tt * ks.ptok : (tt - ks.np) * ks.btok;
+        kr[i] = *reinterpret_cast<const u32x4*>((tt < ks.np ? ks.prefix : ks.block) + off + ch * 8);
+        vr[i] = *reinterpret_cast<const u32x4*>((tt < ks.np ? vprefix : vblock) + off + ch * 8);
     }
+}
+
+// Position of 16-byte chunk ch of row t in a wave's K tile: XOR-swizzled so
+// that the 16 rows one 16-lane group reads at one chunk index fall into 16
+// distinct 16-byte bank groups (rows are 256 bytes at d = 128, 128 at d = 64).
+template <int D>
+__device__ __forceinline__ int k_chunk_pos(int t, int ch)
+{
+    return D == 128 ? (ch ^ (t & 15)) : (ch ^ ((t >> 1) & 7));
 }
 
 template <int D>
@@ -79,13 +92,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 {
     using C = SaCfg<D>;
     constexpr int CH = D / 8;
-    const int pair = blockIdx.x;
+    const int pair = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
     const int r = pair / a.H, h = pair % a.H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int ln = lane & 31, g = lane >> 5;
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
     uint16_t* const Vt = reinterpret_cast<uint16_t*>(smem) + wv * C::TILE;
+    uint16_t* const Kt = reinterpret_cast<uint16_t*>(smem) + (4 + wv) * C::TILE;
 
     int64_t s0 = a.seq_offsets[r], s1 = a.seq_offsets[r + 1];
     s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);
@@ -101,7 +115,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     ks.nk = ks.np + a.B;
     const uint16_t* vprefix = static_cast<const uint16_t*>(a.vp) + s0 * a.ps.tok + hoff;
     const uint16_t* vblock = static_cast<const uint16_t*>(a.v) + boff;
-    const int nch = (ks.nk + 31) / 32;
+    // this work-group's chunks: [c_lo, c_hi) of the pair's 32-key chunks
+    const int nall = (ks.nk + 31) / 32;
+    const int c_lo = static_cast<int>(static_cast<int64_t>(nall) * sp / a.splits);
+    const int nch = static_cast<int>(static_cast<int64_t>(nall) * (sp + 1) / a.splits);
 
     // Q fragments: query ln (rows past B read row B - 1; never stored)
     bf16x8 qf[C::NKB];
@@ -116,22 +133,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     f32x16 acc[C::CT];
 #pragma unroll
     for (int ct = 0; ct < C::CT; ++ct) acc[ct] = f32x16{};
-    bf16x8 kf[C::NKB];
-    u32x4 vr[C::VQ];
-    if (wv < nch) sa_load_chunk<D>(ks, wv, lane, kf, vr, vprefix, vblock);
+    u32x4 kr[C::VQ], vr[C::VQ];
+    if (c_lo + wv < nch) sa_load_chunk<D>(ks, c_lo + wv, lane, kr, vr, vprefix, vblock);
 
-    for (int c = wv; c < nch; c += 4) {
-        // V rows of this chunk into the wave's tile (LDS operations of one
-        // wave execute in order, so no barrier is needed)
+    for (int c = c_lo + wv; c < nch; c += 4) {
+        // K and V rows of this chunk into the wave's tiles (LDS operations of
+        // one wave execute in order, so no barrier is needed)
 #pragma unroll
         for (int i = 0; i < C::VQ; ++i) {
             const int idx = lane + 64 * i, t = idx / CH, ch = idx % CH;
+            *reinterpret_cast<u32x4*>(Kt + t * D + 8 * k_chunk_pos<D>(t, ch)) = kr[i];
             *reinterpret_cast<u32x4*>(Vt + t * D + (((2 * ch) ^ lds_piece_swizzle<D / 4>(t)) << 2)) = vr[i];
         }
+        // s^T = K Q^T: lane (ln, g) feeds key row ln, elements g d/2 + 8 kb .. + 7
         f32x16 sacc = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) sacc = mfma32(kf[kb], qf[kb], sacc);
-        if (c + 4 < nch) sa_load_chunk<D>(ks, c + 4, lane, kf, vr, vprefix, vblock);
+        for (int kb = 0; kb < C::NKB; ++kb)
+            sacc = mfma32(lds_frag(Kt + ln * D + 8 * k_chunk_pos<D>(ln, g * (CH / 2) + kb)), qf[kb], sacc);
+        if (c + 4 < nch) sa_load_chunk<D>(ks, c + 4, lane, kr, vr, vprefix, vblock);
 
         // online softmax of query ln over the chunk's keys 8 (v/4) + 4 g + v%4
         float mc = -INFINITY;
@@ -198,8 +217,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float den = 0.0f, sc[4];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            sc[w] = __expf(mw[w] - M);
+            // a wave (or, split, the whole work-group) with no keys: weight 0
+            sc[w] = mw[w] == -INFINITY ? 0.0f : __expf(mw[w] - M);
             den += sc[w] * Ml[w * 32 + qi];
+        }
+        if (a.splits > 1) {
+            float* rec = a.part + (static_cast<int64_t>(pair) * a.splits + sp) * prefix_part_floats(D);
+            f32x4 nv[2];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float num = 0.0f;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) num += sc[w] * Ma[(w * D + c8 + e) * 32 + qi];
+                nv[e >> 2][e & 3] = num;
+            }
+            *reinterpret_cast<f32x4*>(rec + qi * D + c8) = nv[0];
+            *reinterpret_cast<f32x4*>(rec + qi * D + c8 + 4) = nv[1];
+            if (c8 == 0) {
+                rec[32 * D + qi] = M;
+                rec[32 * D + 32 + qi] = den;
+            }
+            continue;
         }
         const float inv = 1.0f / den;
         uint32_t pk[4];
@@ -219,6 +257,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
                          static_cast<int64_t>(h) * a.os.head + static_cast<int64_t>(qi) * a.os.tok + c8;
         *reinterpret_cast<u32x4*>(orow) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+    }
+}
+
+// Merge of the split partial results, one work-group per (request, head,
+// query): y = sum_s e^{M_s - M} num_s / sum_s e^{M_s - M} l_s, M = max_s M_s.
+// Wave 0 turns the splits' maxima and normalisers into weights; then thread
+// (g, c) sums column quad c over the splits g, g + G, ... (all of its loads
+// issued together) and the G partial sums of each quad are added through LDS.
+constexpr int kSplitMax = 64;
+
+template <int D>
+__global__ __launch_bounds__(256) void prefix_attn_merge_kernel(PrefixArgs a)
+{
+    constexpr int NQ = D / 4, G = 256 / NQ, PER = kSplitMax / G;
+    const int pair = blockIdx.x / a.B, qi = blockIdx.x % a.B;
+    const int r = pair / a.H, h = pair % a.H;
+    const int tid = threadIdx.x, cq = tid % NQ, g = tid / NQ;
+    constexpr int64_t pf = 32 * D + 64;
+    const float* base = a.part + static_cast<int64_t>(pair) * a.splits * pf;
+    __shared__ float wsh[kSplitMax];
+    __shared__ f32x4 part[256];
+    if (tid < 64) {
+        const int sc = tid < a.splits ? tid : a.splits - 1;
+        const float m = tid < a.splits ? base[sc * pf + 32 * D + qi] : -INFINITY;
+        const float l = base[sc * pf + 32 * D + 32 + qi];
+        const float M = wave_max(m);
+        const float w = m == -INFINITY ? 0.0f : expf(m - M);
+        const float den = wave_sum(w * l);
+        wsh[tid] = w / den;  // zero past the last split
+    }
+    __syncthreads();
+    f32x4 acc = f32x4{};
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int sp = g + G * i;
+        const int sc = sp < a.splits ? sp : a.splits - 1;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(base + sc * pf + qi * D + 4 * cq);
+        acc += wsh[sp] * x;
+    }
+    part[tid] = acc;
+    __syncthreads();
+    if (tid < NQ) {
+        f32x4 y = part[tid];
+#pragma unroll
+        for (int j = 1; j < G; ++j) y += part[j * NQ + tid];
+        const uint32_t lo = static_cast<uint32_t>(bf16_bits(y[0])) | (static_cast<uint32_t>(bf16_bits(y[1])) << 16);
+        const uint32_t hi = static_cast<uint32_t>(bf16_bits(y[2])) | (static_cast<uint32_t>(bf16_bits(y[3])) << 16);
+        uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
+                         static_cast<int64_t>(h) * a.os.head + static_cast<int64_t>(qi) * a.os.tok + 4 * tid;
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2*>(orow) = u32x2{lo, hi};
     }
 }
 
@@ -312,17 +401,44 @@ __global__ __launch_bounds__(kGenThreads) void prefix_attn_generic_kernel(Prefix
     }
 }
 
+// Work-groups the split aims for (one per CU of 256: measured faster than two,
+// fewer and longer splits spend less on each work-group's first loads and its
+// final merge), and the fewest 32-key chunks a split should hold so that its
+// partial record (about 16 KiB) stays small beside the keys and values it
+// reads (16 chunks: 256 KiB).
+constexpr int64_t kSplitTargetWgs = 256;
+constexpr int64_t kSplitMinChunks = 16;
+
 }  // namespace
+
+int prefix_attention_splits(int R, int H, int d, int B, int io, int64_t total_tokens)
+{
+    if (io != BHA_BF16 || B > 32 || (d != 64 && d != 128) || R <= 0) return 1;
+    const int64_t pairs = static_cast<int64_t>(R) * H;
+    const int64_t avg_chunks = (total_tokens / R + B + 31) / 32;
+    int64_t sp = (kSplitTargetWgs + pairs - 1) / pairs;
+    sp = sp < avg_chunks / kSplitMinChunks ? sp : avg_chunks / kSplitMinChunks;
+    sp = sp < kSplitMax ? sp : static_cast<int64_t>(kSplitMax);
+    return sp < 2 ? 1 : static_cast<int>(sp);
+}
 
 hipError_t launch_prefix_attention_mfma(const PrefixArgs& a, hipStream_t s)
 {
     if (a.io != BHA_BF16 || a.B > 32) return hipErrorNotSupported;
     // per-lane offsets within a block and a chunk are 32-bit
     if (a.qs.tok >= (int64_t(1) << 25) || a.ps.tok >= (int64_t(1) << 25)) return hipErrorNotSupported;
-    const dim3 grid(static_cast<uint32_t>(a.R * a.H)), block(256);
+    if (a.splits < 1 || a.splits > kSplitMax || (a.splits > 1 && !a.part)) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * a.splits)), block(256);
     if (a.d == 128) hipLaunchKernelGGL(prefix_attn_mfma_kernel<128>, grid, block, 0, s, a);
     else if (a.d == 64) hipLaunchKernelGGL(prefix_attn_mfma_kernel<64>, grid, block, 0, s, a);
     else return hipErrorNotSupported;
+    if (a.splits > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const dim3 mgrid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * a.B));
+        if (a.d == 128) hipLaunchKernelGGL(prefix_attn_merge_kernel<128>, mgrid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(prefix_attn_merge_kernel<64>, mgrid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -242,14 +242,14 @@ def test_forward_commit_validation(lib):
 
 
 def prefix_attn(lib, dims, q=FAKE, k=FAKE, v=FAKE, kp=FAKE, vp=FAKE, kps=None, offs=FAKE, total=100,
-                out=FAKE + (1 << 24), qs=None, outs=None):
+                ws=0, ws_bytes=0, out=FAKE + (1 << 24), qs=None, outs=None):
     qs = qs or _st()
     outs = outs or _st()
     kps = kps or _st(req=0)
     P = ctypes.c_void_p
     return lib.bha_prefix_attention(ctypes.byref(dims) if dims is not None else None, P(q), P(k), P(v),
-                                    ctypes.byref(qs), P(kp), P(vp), ctypes.byref(kps), P(offs), total, P(out),
-                                    ctypes.byref(outs), P(0))
+                                    ctypes.byref(qs), P(kp), P(vp), ctypes.byref(kps), P(offs), total, P(ws),
+                                    ws_bytes, P(out), ctypes.byref(outs), P(0))
 
 
 def test_prefix_attention_validation(lib):
@@ -266,3 +266,22 @@ def test_prefix_attention_validation(lib):
     assert prefix_attn(lib, _dims(head_dim=96)) == UNSUP
     assert prefix_attn(lib, _dims(block_size=65)) == UNSUP
     assert prefix_attn(lib, _dims(io_dtype=3)) == DTYPE
+    assert prefix_attn(lib, _dims(), ws=FAKE + 8, ws_bytes=1 << 20) == ALIGN
+    assert prefix_attn(lib, _dims(), ws=FAKE, ws_bytes=-1) == DIMS
+
+
+def test_prefix_attention_workspace_size(lib):
+    ws = lib.bha_prefix_attention_workspace
+    # few pairs with long prefixes: split; many pairs: no split
+    part = (32 * 128 + 64) * 4
+    n = ws(ctypes.byref(_dims(num_requests=1, num_heads=16)), 32768)
+    assert n > 0 and n % (16 * part) == 0 and n // (16 * part) <= 64
+    assert ws(ctypes.byref(_dims(num_requests=256, num_heads=16)), 256 * 4096) == 0
+    # short prefixes are not split (fewer than 16 chunks of 32 keys per split)
+    assert ws(ctypes.byref(_dims(num_requests=1, num_heads=16)), 100) == 0
+    # the float32 path never splits
+    assert ws(ctypes.byref(_dims(num_requests=1, num_heads=16, io_dtype=0)), 32768) == 0
+    assert ws(ctypes.byref(_dims(num_requests=0)), 10) == 0
+    assert ws(ctypes.byref(_dims(head_dim=96)), 10) == UNSUP
+    assert ws(ctypes.byref(_dims()), -1) == DIMS
+    assert ws(None, 10) == NULL

@@ -451,3 +451,41 @@ def test_prefix_attention_offsets_are_clamped(dev):
                                    torch.tensor([a, b], dtype=torch.int32, device=dev))
         torch.cuda.synchronize()
         assert torch.equal(y[r], y_r[0]), r
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_prefix_attention_split_matches_oracle(dev, d):
+    # few pairs with long prefixes: the keys of each pair are split over several
+    # work-groups (the request with no prefix leaves some splits without keys);
+    # the same call with a workspace too small to split, and with one that
+    # allows half the splits, agree with the oracle too
+    b = 32
+    case = synth.make_case("tiny", R=3, H=2, d=d, FW=64, B=b, io="bf16", blocks=(625, 625), gamma="uniform")
+    lens = np.array([0, 20000, 40])
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    kp = np.concatenate([case.prefix_k[r][:lens[r]] for r in range(case.R)])
+    vp = np.concatenate([case.prefix_v[r][:lens[r]] for r in range(case.R)])
+    T = kp.shape[0]
+    q, k, v = (to_device(x, "bf16", dev) for x in (case.q, case.k, case.v))
+    kd, vd, od = to_device(kp, "bf16", dev), to_device(vp, "bf16", dev), torch.from_numpy(offs).to(dev)
+    full = bha.prefix_attention_workspace(case.R, case.H, d, b, T)
+    part = case.R * case.H * (32 * d + 64) * 4
+    assert full > 0 and full % part == 0
+    n_split = full // part
+    assert n_split >= 4
+    results = {}
+    for name, ws_bytes in (("full", full), ("half", (n_split // 2) * part), ("none", 16)):
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        results[name] = to_host(bha.prefix_attention(q, k, v, kd, vd, od, workspace=ws))
+    torch.cuda.synchronize()
+    for name, y in results.items():
+        assert np.all(np.isfinite(y)), name
+        worst = 0.0
+        for r in range(case.R):
+            for h in range(case.H):
+                ref = oracle.prefix_attention(case.q[r, :, h], case.k[r, :, h], case.v[r, :, h],
+                                              kp[offs[r]:offs[r + 1], h], vp[offs[r]:offs[r + 1], h])
+                worst = max(worst, normwise_err(y[r, :, h], ref, None))
+        _log(f"[prefix-attn split] d={d} workspace={name} ({n_split} splits in full) lens={lens.tolist()} "
+             f"err {worst:.2e}")
+        assert worst <= TOL["bf16"]
