@@ -74,6 +74,17 @@ __device__ __forceinline__ bf16x8 vt_frag_ps(const uint16_t* Xs, int c0, int kb,
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// Row-major tiles of 16-byte chunks read as MFMA fragments (16 rows at one
+// chunk index per 16-lane group): chunk ch of row t sits at position
+// k_chunk_pos<D>(t, ch), XOR-swizzled so that those 16 rows fall into 16
+// distinct 16-byte bank groups (rows of D bf16: 256 bytes at D = 128, 128 at
+// D = 64), and the 16 (or 2 x 8) chunks one 16-lane group writes do too.
+template <int D>
+__device__ __forceinline__ int k_chunk_pos(int t, int ch)
+{
+    return D == 128 ? (ch ^ (t & 15)) : (ch ^ ((t >> 1) & 7));
+}
+
 // v_mfma_f32_16x16x32_bf16: A lane l holds row l % 16, k = 8 (l / 16) .. + 7;
 // B lane l holds column l % 16, the same k; C lane l holds column l % 16,
 // rows 4 (l / 16) .. + 3.

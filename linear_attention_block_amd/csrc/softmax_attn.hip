@@ -78,15 +78,6 @@ __device__ __forceinline__ void sa_load_chunk(const KeySource& ks, int c, int la
     }
 }
 
-// Position of 16-byte chunk ch of row t in a wave's K tile: XOR-swizzled so
-// that the 16 rows one 16-lane group reads at one chunk index fall into 16
-// distinct 16-byte bank groups (rows are 256 bytes at d = 128, 128 at d = 64).
-template <int D>
-__device__ __forceinline__ int k_chunk_pos(int t, int ch)
-{
-    return D == 128 ? (ch ^ (t & 15)) : (ch ^ ((t >> 1) & 7));
-}
-
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefix_attn_mfma_kernel(PrefixArgs a)
 {
