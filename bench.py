@@ -227,6 +227,70 @@ def prefix_sweep(requests, prefixes, log) -> dict:
                           f"(B={B}, H={H}, d={d}, FW={FW}, bf16; per-launch medians)", "rows": rows}
 
 
+def shape_sweep(log) -> dict:
+    """Latency and bandwidth of one forward and one commit launch as the block
+    size B and the feature width FW vary: 256 requests x 16 heads, d = 128,
+    bf16, states built by one prefill over 1,024-token prefixes. Each launch is
+    timed with HIP events, cold (a 1 GiB buffer is read before it so the
+    Infinity Cache does not hold the state), median of 10."""
+    import numpy as np
+    import torch
+
+    import linear_attention_block_amd as bha
+    import synth
+
+    dev = torch.device("cuda:0")
+    R, H, d = 256, 16, 128
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def timed(fn, n=10):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for _ in range(2):
+            fn()
+        for e0, e1 in evs:
+            torch.sum(flush, dim=0, out=sink)
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+    rows = []
+    for FW in (32, 64, 128):
+        over = dict(H=H, d=d, FW=FW, B=32)
+        w, gamma = synth.device_layer_params("decode256", 0, dev, **over)
+        slots = torch.arange(R, dtype=torch.int32, device=dev)
+        state = bha.new_state(R, H, d, FW, dev)
+        pk, pv, offs = synth.device_packed_prefix("decode256", np.full(R, 32), dev, **over)
+        bha.state_prefill(pk, pv, offs, w, state, slots)
+        del pk, pv, offs
+        for B in (8, 16, 32, 48, 64):
+            q, k, v = synth.device_step_qkv("decode256", 0, R, dev, **dict(over, B=B))
+            out = torch.empty_like(q)
+            fwd = bha.prepare_forward(q, k, v, w, gamma, state, slots, out)
+            snap = state.clone()
+            com = bha.prepare_commit(k, v, w, state, slots)
+            tf, tc = timed(fwd), timed(com)
+            state.copy_(snap)
+            del snap
+            fb, cb = forward_bytes(R, H, d, FW, B), commit_bytes(R, H, d, FW, B)
+            row = {"B": B, "FW": FW, "F": 2 * FW, "state_MB": R * H * (d + 1) * 2 * FW * 4 / 1e6,
+                   "forward_us": tf, "forward_GBps": fb / tf / 1e3, "forward_tokens_per_s": R * B / tf * 1e6,
+                   "commit_us": tc, "commit_GBps": cb / tc / 1e3,
+                   "path": ("mfma, one query tile; commit kernel" if B <= 32 else
+                            "mfma, two query tiles; commit through the prefill kernel")}
+            log(f"shape B={B} FW={FW}: forward {tf:.1f} us ({row['forward_GBps']:.0f} GB/s, "
+                f"{row['forward_tokens_per_s'] / 1e6:.1f} M tok/s), commit {tc:.1f} us ({row['commit_GBps']:.0f} GB/s) "
+                f"[{row['path']}]")
+            rows.append(row)
+            del fwd, com, q, k, v, out
+        del state
+        torch.cuda.empty_cache()
+    return {"sweep": "forward and commit per launch vs block size B and feature width FW "
+                     f"(R={R}, H={H}, d={d}, bf16, cold)", "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +313,9 @@ def main() -> int:
                     help="instead of the block cycle: the kernel-level comparison of one block-hybrid forward "
                          "with softmax attention over prefixes of 1K..32K tokens (prints its own JSON line)")
     ap.add_argument("--sweep-requests", default="1,64")
+    ap.add_argument("--shape-sweep", action="store_true",
+                    help="instead of the block cycle: forward and commit latency over block sizes 8..64 and "
+                         "feature widths FW 32..128 (prints its own JSON line)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -276,6 +343,9 @@ def main() -> int:
     if args.prefix_sweep:
         reqs = [int(x) for x in args.sweep_requests.split(",")]
         print(json.dumps(prefix_sweep(reqs, [1024, 2048, 4096, 8192, 16384, 32768], log)), flush=True)
+        return 0
+    if args.shape_sweep:
+        print(json.dumps(shape_sweep(log)), flush=True)
         return 0
     case = synth.make_case(args.config, with_prefix=False, with_qkv=False)
     R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B

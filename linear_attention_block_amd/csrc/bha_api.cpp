@@ -61,6 +61,17 @@ extern "C" int bha_block_forward(const bha_dims* dims, const void* q, const void
     return launch_status(e);
 }
 
+// A commit of B tokens per request: the commit kernel (bf16, B <= 32), the
+// prefill kernel over each request's B rows (bf16, B <= 64), else the plain
+// kernel.
+static hipError_t launch_commit_any(const CommitArgs& a, hipStream_t stream)
+{
+    hipError_t e = launch_commit_mfma(a, stream);
+    if (e == hipErrorNotSupported) e = launch_prefill_mfma(a, stream);
+    if (e == hipErrorNotSupported) e = launch_commit_generic(a, stream);
+    return e;
+}
+
 extern "C" int bha_state_commit(const bha_dims* dims, const void* k, const void* v,
                                 const bha_strides* kv, const void* w, int64_t w_head_stride,
                                 float* state, int32_t num_slots, const int32_t* slot_ids,
@@ -79,9 +90,7 @@ extern "C" int bha_state_commit(const bha_dims* dims, const void* k, const void*
     a.k = k; a.v = v; a.ks = *kv; a.w = w; a.wh = w_head_stride;
     a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids;
     a.seq_offsets = nullptr; a.total_tokens = 0; a.commit_mask = nullptr;
-    hipError_t e = launch_commit_mfma(a, stream);
-    if (e == hipErrorNotSupported) e = launch_commit_generic(a, stream);
-    return launch_status(e);
+    return launch_status(launch_commit_any(a, stream));
 }
 
 extern "C" int bha_block_forward_commit(const bha_dims* dims, const void* q, const void* k, const void* v,
@@ -118,10 +127,7 @@ extern "C" int bha_block_forward_commit(const bha_dims* dims, const void* q, con
         // the commit changes it (both on the caller's stream)
         e = launch_forward_mfma(a, stream);
         if (e == hipErrorNotSupported) e = launch_forward_generic(a, stream);
-        if (e == hipSuccess) {
-            e = launch_commit_mfma(c, stream);
-            if (e == hipErrorNotSupported) e = launch_commit_generic(c, stream);
-        }
+        if (e == hipSuccess) e = launch_commit_any(c, stream);
     }
     return launch_status(e);
 }

@@ -1,5 +1,7 @@
 // Matrix-core (bf16 MFMA, fp32 accumulate) kernels of block-hybrid attention
-// for gfx950, used for bf16 I/O with blocks of at most 32 tokens.
+// for gfx950, used for bf16 I/O with blocks of at most 64 tokens (the forward
+// takes a block of 33 to 64 tokens as two 32-token query tiles over 64 keys;
+// commits of more than 32 tokens run through the prefill kernel).
 //
 // One work-group of d/32 waves owns one (request, head) pair; wave w owns the
 // 32 value columns [32w, 32w + 32). Every contraction is one
@@ -43,6 +45,16 @@ struct Cfg {
     // except with F = 256 whose state slice alone takes 128 registers
     static constexpr int WPE = FW >= 128 ? 1 : 2;
 };
+
+// Resident work-groups per CU of the forward with QT query tiles. With two
+// tiles and FW >= 64 the second tile's operands and softmax do not fit two
+// work-groups' registers (measured: one work-group per CU, no spills, is as
+// fast as two with spills); at FW = 32 two work-groups are faster.
+template <int D, int FW, int QT>
+constexpr int fwd_wpe()
+{
+    return QT > 1 && FW >= 64 ? 1 : Cfg<D, FW>::WPE;
+}
 
 // Issue the 128-bit loads of wave w's slice of the S tiles: load t gives lane
 // (n, g) = (lane % 32, lane / 32) the features 8t + 4g .. 8t + 4g + 3 of
@@ -168,22 +180,23 @@ __device__ __forceinline__ void logit_range(const f32x16 (&u)[FW / 32], float& m
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-template <int D, int FW>
+// QT 32-token tiles of the block (QT = 2 for 32 < B <= 64).
+template <int D, int FW, int QT = 1>
 struct alignas(16) FwdLds {
     using C = Cfg<D, FW>;
-    uint16_t Qs[32 * C::RS];
-    uint16_t Ks[32 * C::RS];
+    uint16_t Qs[32 * QT * C::RS];
+    uint16_t Ks[32 * QT * C::RS];
     uint16_t Ws[FW * C::RS];
-    uint16_t Vs[32 * C::RS];  // V rows, read transposed by ds_read_b64_tr_b16
+    uint16_t Vs[32 * QT * C::RS];  // V rows, read transposed by ds_read_b64_tr_b16
     float Zs[C::F];
 };
 
 // The per-pair operands a thread stages through LDS, held in registers from
 // their global loads to the LDS writes.
-template <int D, int FW>
+template <int D, int FW, int QT = 1>
 struct PairOperands {
     using C = Cfg<D, FW>;
-    RowChunks<D, C::NT> q, k, v;
+    RowChunks<D, C::NT, 32 * QT> q, k, v;
     f32x4 z;
     const float* rec;  // the state record the slice loads read (slot 0's for an out-of-range slot)
     bool valid;        // the slot id is in range
@@ -205,7 +218,7 @@ struct PairOperands {
         z = reinterpret_cast<const f32x4*>(rec + D * C::F)[(tid % (C::F / 4)) * live];
     }
 
-    __device__ __forceinline__ void store(FwdLds<D, FW>& sm, int tid) const
+    __device__ __forceinline__ void store(FwdLds<D, FW, QT>& sm, int tid) const
     {
         q.template store_rows<C::RS>(sm.Qs, tid);
         k.template store_rows<C::RS>(sm.Ks, tid);
@@ -220,13 +233,13 @@ struct PairOperands {
 // phi(q) for token ln as bf16 B operands of unnormalised exponentials
 // e+ = exp(u - max u) and e- = exp(min u - u); returns the two normalisers
 // sp, sn and den = phi(q)^T Z.
-template <int D, int FW>
-__device__ __forceinline__ void phi_operands(const FwdLds<D, FW>& sm, int ln, int g, bf16x8 (&pb)[Cfg<D, FW>::F / 16],
-                                             float& sp, float& sn, float& den)
+template <int D, int FW, int QT>
+__device__ __forceinline__ void phi_operands(const FwdLds<D, FW, QT>& sm, int q0, int ln, int g,
+                                             bf16x8 (&pb)[Cfg<D, FW>::F / 16], float& sp, float& sn, float& den)
 {
     using C = Cfg<D, FW>;
     f32x16 u[FW / 32];
-    feature_logits<D, FW, C::RS>(sm.Ws, sm.Qs, ln, g, u);
+    feature_logits<D, FW, C::RS>(sm.Ws, sm.Qs + q0 * C::RS, ln, g, u);
     constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
     for (int T = 0; T < FW / 32; ++T)
@@ -289,58 +302,68 @@ __device__ __forceinline__ f32x16 linear_read(const f32x4 (&sv)[Cfg<D, FW>::NSL]
     return lacc;
 }
 
-// Block logits s^T = K Q^T (masked beyond B), row maximum m, exponentials P
-// and row sum l for token ln, then this wave's 32 columns of P V.
-template <int D, int FW>
-__device__ __forceinline__ f32x16 block_softmax_pv(const ForwardArgs& a, const FwdLds<D, FW>& sm, int wv, int ln,
-                                                   int g, float& m, float& l)
+// Block logits s^T = K Q^T over the QT key tiles (masked beyond B), row
+// maximum m, exponentials P and row sum l for query q0 + ln, then this wave's
+// 32 columns of P V. Key 32 kt + 8(v/4) + 4g + v%4 of tile kt lands in P
+// operand 2 kt + v/8, element v%8: the k order vt_frag reads V rows in.
+template <int D, int FW, int QT>
+__device__ __forceinline__ f32x16 block_softmax_pv(const ForwardArgs& a, const FwdLds<D, FW, QT>& sm, int q0, int wv,
+                                                   int ln, int g, float& m, float& l)
 {
     using C = Cfg<D, FW>;
-    bf16x8 pp[2];
+    bf16x8 pp[2 * QT];
     {
-        f32x16 sacc = f32x16{};
+        f32x16 sacc[QT];
 #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-            sacc = mfma32(lds_frag(sm.Ks + ln * C::RS + 16 * kb + 8 * g),
-                          lds_frag(sm.Qs + ln * C::RS + 16 * kb + 8 * g), sacc);
+        for (int kt = 0; kt < QT; ++kt) {
+            sacc[kt] = f32x16{};
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb)
+                sacc[kt] = mfma32(lds_frag(sm.Ks + (32 * kt + ln) * C::RS + 16 * kb + 8 * g),
+                                  lds_frag(sm.Qs + (q0 + ln) * C::RS + 16 * kb + 8 * g), sacc[kt]);
+        }
         m = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int j = 8 * (v >> 2) + 4 * g + (v & 3);
-            const float s = j < a.B ? sacc[v] * a.scale : -INFINITY;
-            sacc[v] = s;
-            m = fmaxf(m, s);
-        }
+        for (int kt = 0; kt < QT; ++kt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int j = 32 * kt + 8 * (v >> 2) + 4 * g + (v & 3);
+                const float s = j < a.B ? sacc[kt][v] * a.scale : -INFINITY;
+                sacc[kt][v] = s;
+                m = fmaxf(m, s);
+            }
         m = fmaxf(m, __shfl_xor(m, 32, 64));
         l = 0.0f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float p = __expf(sacc[v] - m);
-            l += p;
-            pp[v >> 3][v & 7] = static_cast<__bf16>(p);
-        }
+        for (int kt = 0; kt < QT; ++kt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = __expf(sacc[kt][v] - m);
+                l += p;
+                pp[2 * kt + (v >> 3)][v & 7] = static_cast<__bf16>(p);
+            }
         l += __shfl_xor(l, 32, 64);
     }
     f32x16 vacc = f32x16{};
     const int lane = 32 * g + ln;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) vacc = mfma32(vt_frag<C::RS>(sm.Vs, 32 * wv, kb, lane), pp[kb], vacc);
+    for (int kb = 0; kb < 2 * QT; ++kb) vacc = mfma32(vt_frag<C::RS>(sm.Vs, 32 * wv, kb, lane), pp[kb], vacc);
     return vacc;
 }
 
 // Merge of the two branches for token ln and store of this wave's 32 columns.
 __device__ __forceinline__ void merge_store(const ForwardArgs& a, const f32x16& vacc, const f32x16& lacc, float gamma,
-                                            float m, float l, float den, float sn, int r, int h, int wv, int ln, int g,
+                                            float m, float l, float den, float sn, int r, int h, int wv, int qi, int g,
                                             bool valid)
 {
-    if (ln >= a.B) return;
+    if (qi >= a.B) return;
     float al, be;
     merge_weights(gamma, m, al, be);
     // an out-of-range slot stores NaN rows
     const float inv = valid ? __builtin_amdgcn_rcpf(al * l + be * den) : __builtin_nanf("");
     const float bl = be * __builtin_amdgcn_rcpf(sn);
     uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
-                     static_cast<int64_t>(h) * a.os.head + (ln * static_cast<int>(a.os.tok) + 32 * wv + 4 * g);
+                     static_cast<int64_t>(h) * a.os.head + (qi * static_cast<int>(a.os.tok) + 32 * wv + 4 * g);
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
         uint32_t pk[2];
@@ -364,9 +387,10 @@ __device__ __forceinline__ void merge_store(const ForwardArgs& a, const f32x16& 
 // follow. The next pair's Q, K, V, Z loads are issued right after the current
 // ones reach LDS. The vector memory counter retires in issue order, so every
 // wait only covers loads issued before the ones still streaming.
-template <int D, int FW>
+template <int D, int FW, int QT>
 __global__ __launch_bounds__(64 * (D / 32))
-__attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forward_mfma_kernel(ForwardArgs a, int npairs)
+__attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, QT>(), fwd_wpe<D, FW, QT>()))) void forward_mfma_kernel(ForwardArgs a,
+                                                                                                 int npairs)
 {
     using C = Cfg<D, FW>;
     constexpr int F = C::F;
@@ -378,7 +402,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
     const int h = p % a.H;
     const float gamma = a.gamma[h];
 
-    __shared__ FwdLds<D, FW> sm;
+    __shared__ FwdLds<D, FW, QT> sm;
     {
         WChunks<D, FW, C::NT> wc;
         wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
@@ -388,7 +412,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
     // slot ids run one pair ahead of the operand loads (index clamped in range)
     auto slot_of = [&](int pp) { return a.slot_ids[(pp < npairs ? pp : npairs - 1) / a.H]; };
     const int count = (npairs - p + G - 1) / G;  // pairs of this work-group
-    PairOperands<D, FW> op;
+    PairOperands<D, FW, QT> op;
     f32x4 sv[C::NSL];
     // issue order as in the loop (operands, then the slice, then the next
     // slot id), so the waits at the loop head are the same from either side
@@ -409,18 +433,32 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
         op.store(sm, tid);
         __syncthreads();
         op.load(a, pn, __builtin_amdgcn_readfirstlane(slot_next), tid, live);
+        // the first QT - 1 query tiles, then the last one, after whose linear
+        // read the state slice registers are free for the next pair's slice
+#pragma unroll
+        for (int qt = 0; qt + 1 < QT; ++qt) {
+            f32x16 lacc, vacc;
+            float sp, sn, den, m, l;
+            {
+                bf16x8 pb[F / 16];
+                phi_operands<D, FW, QT>(sm, 32 * qt, ln, g, pb, sp, sn, den);
+                vacc = block_softmax_pv<D, FW, QT>(a, sm, 32 * qt, wv, ln, g, m, l);
+                lacc = linear_read<D, FW>(sv, pb, sp, sn);
+            }
+            merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, 32 * qt + ln, g, valid);
+        }
         f32x16 lacc, vacc;
         float sp, sn, den, m, l;
         {
             bf16x8 pb[F / 16];
-            phi_operands<D, FW>(sm, ln, g, pb, sp, sn, den);
-            vacc = block_softmax_pv<D, FW>(a, sm, wv, ln, g, m, l);
+            phi_operands<D, FW, QT>(sm, 32 * (QT - 1), ln, g, pb, sp, sn, den);
+            vacc = block_softmax_pv<D, FW, QT>(a, sm, 32 * (QT - 1), wv, ln, g, m, l);
             lacc = linear_read<D, FW>(sv, pb, sp, sn);
         }
         __builtin_amdgcn_sched_barrier(0);
         load_state_slice(op.rec + wv * F * 32, lane, sv, live);
         __builtin_amdgcn_sched_barrier(0);
-        merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, ln, g, valid);
+        merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, 32 * (QT - 1) + ln, g, valid);
         // the slot id read at the top of this trip crosses the loop in a
         // vector register: its wait lands here, a whole trip after the load,
         // and covers no load issued since
@@ -579,8 +617,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
         f32x16 lacc, vacc;
         float sp, sn, den, m, l;
         bf16x8 pb[F / 16];
-        phi_operands<D, FW>(sm.f, ln, g, pb, sp, sn, den);
-        vacc = block_softmax_pv<D, FW>(a, sm.f, wv, ln, g, m, l);
+        phi_operands<D, FW, 1>(sm.f, 0, ln, g, pb, sp, sn, den);
+        vacc = block_softmax_pv<D, FW, 1>(a, sm.f, 0, wv, ln, g, m, l);
         lacc = linear_read<D, FW>(sv, pb, sp, sn);
         merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, ln, g, op.valid);
     }
@@ -930,7 +968,9 @@ void prefill_mfma_kernel(CommitArgs a)
     commit_rows(a, r, first_row, n);
     if (n == 0) return;
     float* rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * F;
-    const int64_t base = first_row * a.ks.tok + static_cast<int64_t>(h) * a.ks.head;
+    // a packed token range, or (a commit of B tokens) the request's block rows
+    const int64_t base = (first_row >= 0 ? first_row * a.ks.tok : static_cast<int64_t>(r) * a.ks.req) +
+                         static_cast<int64_t>(h) * a.ks.head;
     PrefillPair<D, FW> pp;
     pp.kbase = static_cast<const uint16_t*>(a.k) + base;
     pp.vbase = static_cast<const uint16_t*>(a.v) + base;
@@ -1045,12 +1085,16 @@ template <int D, int FW>
 static hipError_t launch_forward(const ForwardArgs& a, hipStream_t s)
 {
     const int npairs = a.R * a.H;
-    int64_t G = static_cast<int64_t>(compute_units()) * Cfg<D, FW>::WPE;
+    int64_t G = static_cast<int64_t>(compute_units()) * (a.B <= 32 ? fwd_wpe<D, FW, 1>() : fwd_wpe<D, FW, 2>());
     G = (G / a.H) * a.H;
     if (G < a.H) G = a.H;
     if (G > npairs) G = npairs;
-    hipLaunchKernelGGL((forward_mfma_kernel<D, FW>), dim3(static_cast<uint32_t>(G)), dim3(64 * (D / 32)), 0, s, a,
-                       npairs);
+    if (a.B <= 32)
+        hipLaunchKernelGGL((forward_mfma_kernel<D, FW, 1>), dim3(static_cast<uint32_t>(G)), dim3(64 * (D / 32)), 0, s,
+                           a, npairs);
+    else
+        hipLaunchKernelGGL((forward_mfma_kernel<D, FW, 2>), dim3(static_cast<uint32_t>(G)), dim3(64 * (D / 32)), 0, s,
+                           a, npairs);
     return hipGetLastError();
 }
 
@@ -1098,7 +1142,7 @@ static bool small_token_stride(int64_t tok) { return tok >= 0 && tok < (int64_t(
 
 hipError_t launch_forward_mfma(const ForwardArgs& a, hipStream_t s)
 {
-    if (a.io != BHA_BF16 || a.B > 32) return hipErrorNotSupported;
+    if (a.io != BHA_BF16 || a.B > 64) return hipErrorNotSupported;
     if (!small_token_stride(a.qs.tok) || !small_token_stride(a.os.tok)) return hipErrorNotSupported;
     if (a.d == 128) return forward_by_fw<128>(a, s);
     if (a.d == 64) return forward_by_fw<64>(a, s);
@@ -1107,7 +1151,8 @@ hipError_t launch_forward_mfma(const ForwardArgs& a, hipStream_t s)
 
 hipError_t launch_prefill_mfma(const CommitArgs& a, hipStream_t s)
 {
-    if (a.io != BHA_BF16 || a.seq_offsets == nullptr) return hipErrorNotSupported;
+    // packed ranges (seq_offsets), or blocks of B <= 64 rows per request
+    if (a.io != BHA_BF16 || (a.seq_offsets == nullptr && a.B > 64)) return hipErrorNotSupported;
     // in-chunk offsets (up to 128 rows) are 32-bit
     if (a.ks.tok >= (int64_t(1) << 23)) return hipErrorNotSupported;
     if (a.d == 128) return prefill_by_fw<128>(a, s);

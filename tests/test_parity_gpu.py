@@ -139,11 +139,14 @@ def test_b16_bf16_end_to_end(dev):
 
 
 SWEEP = [
-    # (io, d, FW, B): B <= 32 with bf16 takes the matrix-core kernels, the rest the fp32 kernels
+    # (io, d, FW, B): bf16 takes the matrix-core kernels (B <= 32: one query tile
+    # and the commit kernel; 33..64: two query tiles and commits through the
+    # prefill kernel), fp32 the plain kernels
     ("bf16", 128, 64, 32), ("bf16", 128, 64, 1), ("bf16", 128, 64, 17), ("bf16", 128, 32, 32),
     ("bf16", 128, 128, 32), ("bf16", 64, 32, 8), ("bf16", 64, 64, 31), ("bf16", 64, 128, 32),
-    ("bf16", 128, 64, 33), ("bf16", 64, 32, 64), ("f32", 128, 64, 32), ("f32", 64, 128, 5),
-    ("f32", 128, 32, 64), ("f32", 64, 64, 1),
+    ("bf16", 128, 64, 33), ("bf16", 64, 32, 64), ("bf16", 128, 64, 48), ("bf16", 128, 128, 64),
+    ("bf16", 128, 32, 63), ("bf16", 64, 64, 40), ("bf16", 64, 128, 57),
+    ("f32", 128, 64, 32), ("f32", 64, 128, 5), ("f32", 128, 32, 64), ("f32", 64, 64, 1),
 ]
 
 
@@ -189,7 +192,7 @@ def test_strided_views_and_shared_map(dev):
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("io,b", [("bf16", 32), ("f32", 8)])
+@pytest.mark.parametrize("io,b", [("bf16", 32), ("bf16", 48), ("f32", 8)])
 def test_out_of_range_slot_is_isolated(dev, io, b):
     case = synth.make_case("tiny", R=4, H=2, d=64, FW=32, B=b, io=io, blocks=(1, 2), gamma="uniform")
     run = Run(case, dev)
@@ -325,7 +328,8 @@ def test_prefill_long_prompts_fused_kv(dev):
 
 
 FUSED = [("bf16", 128, 64, 32), ("bf16", 128, 64, 17), ("bf16", 64, 32, 32), ("bf16", 128, 128, 32),
-         ("bf16", 64, 128, 8), ("bf16", 128, 64, 40), ("f32", 128, 64, 32), ("f32", 64, 32, 5)]
+         ("bf16", 64, 128, 8), ("bf16", 128, 64, 40), ("bf16", 128, 64, 64), ("f32", 128, 64, 32),
+         ("f32", 64, 32, 5)]
 
 
 @pytest.mark.parametrize("io,d,fw,b", FUSED)
@@ -489,3 +493,42 @@ def test_prefix_attention_split_matches_oracle(dev, d):
         _log(f"[prefix-attn split] d={d} workspace={name} ({n_split} splits in full) lens={lens.tolist()} "
              f"err {worst:.2e}")
         assert worst <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_state_is_consistent_across_block_sizes(dev, io):
+    # blocks of 32, 16, 8, 1, 64 and 5 tokens committed in turn into one state
+    # (each commit a separate call with its own B, both kernel families), then
+    # forwards with B = 16 and B = 48 from it: the state equals the oracle's
+    # build over all 126 tokens, and each forward the oracle's forward from
+    # that state -- the state does not depend on how the prefix was cut into
+    # blocks
+    R, H, d, FW = 3, 2, 128, 64
+    sizes = [32, 16, 8, 1, 64, 5]
+    n = sum(sizes)
+    case = synth.make_case("tiny", R=R, H=H, d=d, FW=FW, B=n, io=io, blocks=(1, 1), gamma="uniform")
+    w = to_device(case.w, io, dev)
+    slots = torch.from_numpy(case.slot_ids).to(dev)
+    state = bha.new_state(case.num_slots, H, d, FW, dev)
+    pk = np.stack([case.prefix_k[r][:n] for r in range(R)])  # [R][n][H][d]
+    pv = np.stack([case.prefix_v[r][:n] for r in range(R)])
+    t0 = 0
+    for b in sizes:
+        bha.state_commit(to_device(pk[:, t0:t0 + b], io, dev), to_device(pv[:, t0:t0 + b], io, dev), w, state, slots)
+        t0 += b
+    torch.cuda.synchronize()
+    S, Z = record_to_plain(state.cpu().numpy()[case.slot_ids], d, case.F)
+    worst_s = 0.0
+    for r in range(R):
+        for h in range(H):
+            S_ref, Z_ref = oracle.state_build(pk[r, :, h], pv[r, :, h], case.w[h])
+            worst_s = max(worst_s, normwise_err(S[r, h], S_ref, None), normwise_err(Z[r, h], Z_ref, None))
+    worst_f = 0.0
+    for b in (16, 48):
+        q, k, v = (case.q[:, :b], case.k[:, :b], case.v[:, :b])
+        y = to_host(bha.block_forward(*(to_device(np.ascontiguousarray(x), io, dev) for x in (q, k, v)), w,
+                                      torch.from_numpy(case.gamma).to(dev), state, slots))
+        ref = oracle.block_forward_batch(pairs(q), pairs(k), pairs(v), case.w, case.gamma, S, Z, nthreads=NTHREADS)
+        worst_f = max(worst_f, normwise_err(pairs(y), ref, (2, 3)))
+    _log(f"[block sizes] io={io} commits of {sizes}: state err {worst_s:.2e}; forwards B=16, 48 err {worst_f:.2e}")
+    assert worst_s <= TOL[io] and worst_f <= TOL[io]
