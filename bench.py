@@ -72,6 +72,14 @@ def prefill_bytes(T, R, H, d, FW, es=2):
     return T * H * 2 * d * es + R * H * 2 * (d * F * 4 + F * 4) + H * FW * d * es + (2 * R + 1) * 4
 
 
+def forward_gqa_bytes(R, H, HK, d, FW, B, es=2):
+    """Algorithmic HBM bytes of one bha_block_forward_gqa launch: per
+    (request, K/V head) the state record (S, Z) and K, V read; per (request,
+    query head) Q read and O written; W once per K/V head."""
+    F = 2 * FW
+    return R * HK * (d * F * 4 + F * 4 + 2 * B * d * es) + R * H * 2 * B * d * es + HK * FW * d * es
+
+
 def prefix_attention_bytes(T, R, H, d, B, es=2):
     """Algorithmic HBM bytes of one bha_prefix_attention launch: K and V of
     every packed prefix token and head read once, the block's Q, K, V read and
@@ -156,6 +164,103 @@ def cpu_baseline(layer, case, denoise, n_req, log):
         "sample": (f"one block cycle ({denoise} forwards + 1 commit, one layer) of the first {n_req} "
                    f"of {R} requests, all {H} heads, same workload and state; fp64 C oracle, "
                    f"{dt:.2f} s wall"),
+    }
+
+
+def gqa_cycle(args, log) -> dict:
+    """The block cycle of the default workload with grouped K/V heads: the H
+    query heads share args.kv_heads K/V heads (states, W, K and V per K/V
+    head). Per layer: states built by one prefill over the K/V heads, then per
+    step 32 bha_block_forward_gqa launches and one bha_state_commit per layer
+    (the fused last step exists for one K/V head per query head only)."""
+    import numpy as np
+    import torch
+
+    import linear_attention_block_amd as bha
+    import synth
+
+    dev = torch.device("cuda:0")
+    case = synth.make_case(args.config, with_prefix=False, with_qkv=False)
+    R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B
+    HK = args.kv_heads
+    if HK < 1 or H % HK:
+        raise SystemExit(f"--kv-heads {HK} must divide the {H} query heads")
+    G = H // HK
+    nl, nd = args.layers, args.denoise
+    slots = torch.from_numpy(case.slot_ids).to(dev)
+    layers = []
+    for L in range(nl):
+        w, _ = synth.device_layer_params(args.config, L, dev, H=HK)
+        _, gamma = synth.device_layer_params(args.config, L, dev)
+        state = bha.new_state(case.num_slots, HK, d, FW, dev)
+        pk, pv, offs = synth.device_packed_prefix(args.config, case.n_blocks, dev, layer=L, H=HK)
+        bha.state_prefill(pk, pv, offs, w, state, slots)
+        del pk, pv, offs
+        q = synth.device_step_qkv(args.config, 0, R, dev, layer=L)[0]
+        _, k, v = synth.device_step_qkv(args.config, 0, R, dev, layer=L, H=HK)
+        out = torch.empty_like(q)
+        layers.append(dict(fwd=bha.prepare_forward_gqa(q, k, v, w, gamma, state, slots, out),
+                           com=bha.prepare_commit(k, v, w, state, slots), keep=(q, k, v, w, gamma, state, out)))
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps * (nd + 1) * nl)]
+
+    def step(it):
+        for _ in range(nd):
+            for lay in layers:
+                if it is not None:
+                    e0, e1 = next(it)
+                    e0.record()
+                lay["fwd"]()
+                if it is not None:
+                    e1.record()
+        for lay in layers:
+            if it is not None:
+                e0, e1 = next(it)
+                e0.record()
+            lay["com"]()
+            if it is not None:
+                e1.record()
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    it = iter(ev)
+    for _ in range(args.steps):
+        step(it)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per = (nd + 1) * nl
+    fwd_ms, com_ms = [], []
+    for st in range(args.steps):
+        blk = ev[st * per:(st + 1) * per]
+        fwd_ms += [a.elapsed_time(b) for a, b in blk[:nd * nl]]
+        com_ms += [a.elapsed_time(b) for a, b in blk[nd * nl:]]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms) * 1e-3
+    com_avg = sum(com_ms) / len(com_ms) * 1e-3
+    fb = forward_gqa_bytes(R, H, HK, d, FW, B)
+    cb = commit_bytes(R, HK, d, FW, B)
+    value = args.steps * nd * nl * R * B / elapsed
+    log(f"gqa forward (H={H}, {HK} K/V heads): avg {fwd_avg * 1e6:.1f} us/launch, {fb / fwd_avg / 1e9:.0f} GB/s "
+        f"algorithmic ({fb / 1e6:.1f} MB/launch); commit: avg {com_avg * 1e6:.1f} us, {cb / com_avg / 1e9:.0f} GB/s")
+    log(f"step: {elapsed / args.steps * 1e3:.2f} ms; {value / 1e6:.1f} M tokens/s")
+    return {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": (f"{args.config} with grouped K/V heads: {R} requests x {H} query heads over {HK} "
+                                f"K/V heads (G={G}), d={d}, FW={FW}, B={B}; per step {nd} forwards in each of {nl} "
+                                f"layers, then a commit per layer"),
+                   "requests": R, "heads": H, "kv_heads": HK, "head_dim": d, "feat_half": FW, "block": B,
+                   "denoise_steps": nd, "layers": nl},
+        "roofline": {"bound": "hbm", "achieved": fb / fwd_avg / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": fb / fwd_avg / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": f"bha_block_forward_gqa: forward_mfma_kernel<{d},{FW},1,{G}>",
+                     "bytes_per_launch": fb, "avg_launch_us": fwd_avg * 1e6},
+        "commit": {"kernel": "bha_state_commit over the K/V heads", "avg_launch_us": com_avg * 1e6,
+                   "bytes_per_launch": cb, "achieved_GBps": cb / com_avg / 1e9},
+        "cpu_baseline": None,
     }
 
 
@@ -313,6 +418,9 @@ def main() -> int:
                     help="instead of the block cycle: the kernel-level comparison of one block-hybrid forward "
                          "with softmax attention over prefixes of 1K..32K tokens (prints its own JSON line)")
     ap.add_argument("--sweep-requests", default="1,64")
+    ap.add_argument("--kv-heads", type=int, default=0,
+                    help="grouped K/V heads: the query heads share this many K/V heads (states, W, K, V per "
+                         "K/V head); runs the block cycle with bha_block_forward_gqa (prints its own JSON line)")
     ap.add_argument("--shape-sweep", action="store_true",
                     help="instead of the block cycle: forward and commit latency over block sizes 8..64 and "
                          "feature widths FW 32..128 (prints its own JSON line)")
@@ -346,6 +454,9 @@ def main() -> int:
         return 0
     if args.shape_sweep:
         print(json.dumps(shape_sweep(log)), flush=True)
+        return 0
+    if args.kv_heads:
+        print(json.dumps(gqa_cycle(args, log)), flush=True)
         return 0
     case = synth.make_case(args.config, with_prefix=False, with_qkv=False)
     R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B

@@ -135,6 +135,31 @@ int bha_block_forward(const bha_dims* dims, const void* q, const void* k, const 
                       hipStream_t stream);
 
 /*
+ * bha_block_forward_gqa -- bha_block_forward with H query heads sharing
+ * num_kv_heads K/V heads (grouped queries, G = H / num_kv_heads query heads
+ * per K/V head): query head h attends, within the block, to the keys and
+ * values of K/V head h / G and reads that head's state with that head's W,
+ * so S and Z are kept once per K/V head. Not on the pages, whose model has
+ * one K/V head per query head: a variant for models with grouped K/V heads.
+ * The feature map stays one W applied to queries and keys alike; the K/V
+ * head's W serves its G query heads.
+ *   dims->num_heads : H, query heads; must be a multiple of num_kv_heads.
+ *   q, out          : [R][B][H][d] with strides *qs, *outs.
+ *   k, v            : [R][B][num_kv_heads][d] with strides *kvs.
+ *   w               : num_kv_heads maps (w_head_stride apart, 0 = shared).
+ *   gamma           : [H] float32, one gate per query head.
+ *   state, slot_ids : as for bha_block_forward with num_kv_heads heads per
+ *                     slot; built by bha_state_commit / bha_state_prefill
+ *                     called with dims->num_heads = num_kv_heads.
+ * num_kv_heads == H is bha_block_forward. Errors as for bha_block_forward;
+ * num_kv_heads < 1 or not dividing H: BHA_ERR_DIMS.
+ */
+int bha_block_forward_gqa(const bha_dims* dims, int32_t num_kv_heads, const void* q, const bha_strides* qs,
+                          const void* k, const void* v, const bha_strides* kvs, const void* w,
+                          int64_t w_head_stride, const float* gamma, const float* state, int32_t num_slots,
+                          const int32_t* slot_ids, void* out, const bha_strides* outs, hipStream_t stream);
+
+/*
  * bha_state_commit -- fold a finished block into the state of every
  * (request, head): S += sum_t phi(k_t) v_t^T and Z += sum_t phi(k_t) over the
  * B tokens (gist.science "Architecture Design", state-compression bullet: the

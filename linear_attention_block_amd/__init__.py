@@ -41,7 +41,7 @@ BHA_BF16 = 1
 
 # Every symbol include/bha.h declares.
 EXPORTED_SYMBOLS = (
-    "bha_feature_map", "bha_block_forward", "bha_block_forward_commit", "bha_state_commit", "bha_state_prefill",
+    "bha_feature_map", "bha_block_forward", "bha_block_forward_gqa", "bha_block_forward_commit", "bha_state_commit", "bha_state_prefill",
     "bha_prefix_attention", "bha_prefix_attention_workspace",
     "bha_state_record_floats", "bha_status_string", "bha_version",
 )
@@ -91,6 +91,8 @@ def load_library():
     lib.bha_block_forward.argtypes = [PD, P, P, P, PS, P, I64, P, P, I32, P, P, PS, P]
     lib.bha_state_commit.argtypes = [PD, P, P, PS, P, I64, P, I32, P, P]
     lib.bha_block_forward_commit.argtypes = [PD, P, P, P, PS, P, I64, P, P, I32, P, P, P, PS, P]
+    lib.bha_block_forward_gqa.argtypes = [PD, I32, P, PS, P, P, PS, P, I64, P, P, I32, P, P, PS, P]
+    lib.bha_block_forward_gqa.restype = ctypes.c_int
     lib.bha_block_forward_commit.restype = ctypes.c_int
     lib.bha_state_prefill.argtypes = [PD, P, P, PS, P, I64, P, I64, P, I32, P, P]
     lib.bha_state_prefill.restype = ctypes.c_int
@@ -274,6 +276,49 @@ def block_forward(q, k, v, w, gamma, state, slot_ids, *, out=None, scale: float 
     return out
 
 
+def _forward_gqa_args(q, k, v, w, gamma, state, slot_ids, out, scale, stream):
+    qs = _tok_strides(q, "q")
+    R, B, H, d = q.shape
+    ks = _tok_strides(k, "k")
+    Rk, Bk, HK, dk = k.shape
+    if (Rk, Bk, dk) != (R, B, d) or HK < 1 or H % HK != 0:
+        raise ValueError("k must be [R][B][Hkv][d] with Hkv dividing the query heads of q")
+    if v.shape != k.shape or (v.stride(0), v.stride(1), v.stride(2)) != (ks.req, ks.tok, ks.head) or \
+            v.stride(3) != 1:
+        raise ValueError("v must match k in shape and strides")
+    if k.dtype != q.dtype or v.dtype != q.dtype or w.dtype != q.dtype:
+        raise TypeError("q, k, v and w must share one dtype")
+    fw, wh = _w_stride(w, HK, d)
+    if gamma.dtype != torch.float32 or gamma.numel() != H or not gamma.is_contiguous():
+        raise ValueError("gamma must be a contiguous float32 [H] tensor (one gate per query head)")
+    num_slots = _num_slots(state, HK, d, fw)
+    if slot_ids.dtype != torch.int32 or slot_ids.numel() != R or not slot_ids.is_contiguous():
+        raise ValueError("slot_ids must be a contiguous int32 [R] tensor")
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q in shape and dtype")
+    os_ = _tok_strides(out, "out")
+    _check_device(q.device, k, v, w, gamma, state, slot_ids, out)
+    dims = bha_dims(R, H, d, fw, B, _io_dtype(q), float(scale))
+    return (ctypes.byref(dims), HK, _ptr(q), ctypes.byref(qs), _ptr(k), _ptr(v), ctypes.byref(ks), _ptr(w), wh,
+            _ptr(gamma), _ptr(state), num_slots, _ptr(slot_ids), _ptr(out), ctypes.byref(os_),
+            _stream(q.device, stream)), (dims, qs, ks, os_)
+
+
+def block_forward_gqa(q, k, v, w, gamma, state, slot_ids, *, out=None, scale: float = 0.0,
+                      stream=None) -> torch.Tensor:
+    """block_forward with grouped K/V heads: q [R][B][H][d], k, v
+    [R][B][Hkv][d] (Hkv dividing H), w and the state per K/V head, gamma per
+    query head; query head h uses K/V head h // (H // Hkv). Returns ``out``."""
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    args, _keep = _forward_gqa_args(q, k, v, w, gamma, state, slot_ids, out, scale, stream)
+    st = lib.bha_block_forward_gqa(*args)
+    if st != 0:
+        raise BhaError("bha_block_forward_gqa", st)
+    return out
+
+
 def block_forward_commit(q, k, v, w, gamma, state, slot_ids, *, commit_mask=None, out=None,
                          scale: float = 0.0, stream=None) -> torch.Tensor:
     """The last denoising step of a block: the forward from the state as it
@@ -411,6 +456,13 @@ def prepare_forward(q, k, v, w, gamma, state, slot_ids, out, *, scale: float = 0
     args, keep = _forward_args(q, k, v, w, gamma, state, slot_ids, out, scale, stream)
     keep = keep + (q, k, v, w, gamma, state, slot_ids, out)
     return _Prepared(load_library().bha_block_forward, "bha_block_forward", args, keep)
+
+
+def prepare_forward_gqa(q, k, v, w, gamma, state, slot_ids, out, *, scale: float = 0.0, stream=None):
+    """Marshal a bha_block_forward_gqa call once, for launch-rate-bound loops."""
+    args, keep = _forward_gqa_args(q, k, v, w, gamma, state, slot_ids, out, scale, stream)
+    keep = keep + (q, k, v, w, gamma, state, slot_ids, out)
+    return _Prepared(load_library().bha_block_forward_gqa, "bha_block_forward_gqa", args, keep)
 
 
 def prepare_forward_commit(q, k, v, w, gamma, state, slot_ids, out, *, commit_mask=None, scale: float = 0.0,

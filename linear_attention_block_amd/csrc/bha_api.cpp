@@ -54,7 +54,41 @@ extern "C" int bha_block_forward(const bha_dims* dims, const void* q, const void
     a.R = dims->num_requests; a.H = dims->num_heads; a.d = dims->head_dim;
     a.FW = dims->feat_half; a.B = dims->block_size; a.io = dims->io_dtype;
     a.scale = dims->scale > 0.0f ? dims->scale : 1.0f / sqrtf((float)dims->head_dim);
-    a.q = q; a.k = k; a.v = v; a.qs = *qkv; a.w = w; a.wh = w_head_stride; a.gamma = gamma;
+    a.q = q; a.k = k; a.v = v; a.qs = *qkv; a.ks = *qkv; a.G = 1;
+    a.w = w; a.wh = w_head_stride; a.gamma = gamma;
+    a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids; a.out = out; a.os = *outs;
+    hipError_t e = launch_forward_mfma(a, stream);
+    if (e == hipErrorNotSupported) e = launch_forward_generic(a, stream);
+    return launch_status(e);
+}
+
+extern "C" int bha_block_forward_gqa(const bha_dims* dims, int32_t num_kv_heads, const void* q,
+                                     const bha_strides* qs, const void* k, const void* v, const bha_strides* kvs,
+                                     const void* w, int64_t w_head_stride, const float* gamma, const float* state,
+                                     int32_t num_slots, const int32_t* slot_ids, void* out,
+                                     const bha_strides* outs, hipStream_t stream)
+{
+    int st = validate_dims(dims);
+    if (st != BHA_OK) return st;
+    if (num_kv_heads < 1 || dims->num_heads % num_kv_heads != 0) return BHA_ERR_DIMS;
+    if (dims->num_requests == 0) return BHA_OK;
+    // K, V, W and the state have num_kv_heads heads
+    bha_dims kvd = *dims;
+    kvd.num_heads = num_kv_heads;
+    if ((st = validate_tokens(q, qs, dims, false)) != BHA_OK) return st;
+    if ((st = validate_tokens(k, kvs, &kvd, false)) != BHA_OK) return st;
+    if ((st = validate_tokens(v, kvs, &kvd, false)) != BHA_OK) return st;
+    if ((st = validate_w(w, w_head_stride, &kvd)) != BHA_OK) return st;
+    if (!gamma) return BHA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(gamma) % 4 != 0) return BHA_ERR_ALIGN;
+    if ((st = validate_state(state, num_slots, slot_ids, &kvd)) != BHA_OK) return st;
+    if ((st = validate_tokens(out, outs, dims, true)) != BHA_OK) return st;
+    ForwardArgs a;
+    a.R = dims->num_requests; a.H = dims->num_heads; a.d = dims->head_dim;
+    a.FW = dims->feat_half; a.B = dims->block_size; a.io = dims->io_dtype;
+    a.scale = dims->scale > 0.0f ? dims->scale : 1.0f / sqrtf((float)dims->head_dim);
+    a.q = q; a.k = k; a.v = v; a.qs = *qs; a.ks = *kvs; a.G = dims->num_heads / num_kv_heads;
+    a.w = w; a.wh = w_head_stride; a.gamma = gamma;
     a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids; a.out = out; a.os = *outs;
     hipError_t e = launch_forward_mfma(a, stream);
     if (e == hipErrorNotSupported) e = launch_forward_generic(a, stream);
@@ -114,7 +148,8 @@ extern "C" int bha_block_forward_commit(const bha_dims* dims, const void* q, con
     a.R = dims->num_requests; a.H = dims->num_heads; a.d = dims->head_dim;
     a.FW = dims->feat_half; a.B = dims->block_size; a.io = dims->io_dtype;
     a.scale = dims->scale > 0.0f ? dims->scale : 1.0f / sqrtf((float)dims->head_dim);
-    a.q = q; a.k = k; a.v = v; a.qs = *qkv; a.w = w; a.wh = w_head_stride; a.gamma = gamma;
+    a.q = q; a.k = k; a.v = v; a.qs = *qkv; a.ks = *qkv; a.G = 1;
+    a.w = w; a.wh = w_head_stride; a.gamma = gamma;
     a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids; a.out = out; a.os = *outs;
     CommitArgs c;
     c.R = a.R; c.H = a.H; c.d = a.d; c.FW = a.FW; c.B = a.B; c.io = a.io;

@@ -11,14 +11,16 @@ namespace bha {
 
 // Everything a launch needs, already validated on the host.
 struct ForwardArgs {
-    int R, H, d, FW, B, io;
+    int R, H, d, FW, B, io;  // H: query heads
     float scale;  // resolved: never 0
     const void *q, *k, *v;
-    bha_strides qs;
+    bha_strides qs;  // q (and out's layout is os)
+    bha_strides ks;  // k and v
+    int G;           // query heads per K/V head (1: one K/V head per query head)
     const void* w;
     int64_t wh;
-    const float* gamma;
-    const float* state;
+    const float* gamma;  // [H]
+    const float* state;  // [num_slots][H / G][record]; W: one per K/V head
     int num_slots;
     const int32_t* slot_ids;
     void* out;

@@ -45,12 +45,15 @@ __global__ __launch_bounds__(kThreads) void forward_generic_kernel(ForwardArgs a
         for (int c = tid; c < a.d; c += kThreads) st_elem(out, c, __builtin_nanf(""));
         return;
     }
-    const float* rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(a.d + 1) * F;
-    const int64_t base = r * a.qs.req + static_cast<int64_t>(h) * a.qs.head;
-    const T* q = static_cast<const T*>(a.q) + base + static_cast<int64_t>(i) * a.qs.tok;
-    const T* kb = static_cast<const T*>(a.k) + base;
-    const T* vb = static_cast<const T*>(a.v) + base;
-    const T* W = static_cast<const T*>(a.w) + static_cast<int64_t>(h) * a.wh;
+    // query head h reads K/V head h / G: its keys, values, W and state
+    const int hk = h / a.G, Hk = a.H / a.G;
+    const float* rec = a.state + (static_cast<int64_t>(slot) * Hk + hk) * static_cast<int64_t>(a.d + 1) * F;
+    const int64_t kbase = r * a.ks.req + static_cast<int64_t>(hk) * a.ks.head;
+    const T* q = static_cast<const T*>(a.q) + r * a.qs.req + static_cast<int64_t>(h) * a.qs.head +
+                 static_cast<int64_t>(i) * a.qs.tok;
+    const T* kb = static_cast<const T*>(a.k) + kbase;
+    const T* vb = static_cast<const T*>(a.v) + kbase;
+    const T* W = static_cast<const T*>(a.w) + static_cast<int64_t>(hk) * a.wh;
 
     for (int c = tid; c < a.d; c += kThreads) xq[c] = ld_elem(q, c);
     __syncthreads();
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void forward_generic_kernel(ForwardArgs a
     }
     for (int j = tid; j < a.B; j += kThreads) {
         float acc = 0.0f;
-        for (int c = 0; c < a.d; ++c) acc = fmaf(xq[c], ld_elem(kb, static_cast<int64_t>(j) * a.qs.tok + c), acc);
+        for (int c = 0; c < a.d; ++c) acc = fmaf(xq[c], ld_elem(kb, static_cast<int64_t>(j) * a.ks.tok + c), acc);
         pl[j] = acc * a.scale;
     }
     __syncthreads();
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void forward_generic_kernel(ForwardArgs a
     const float inv = 1.0f / (al * scal[1] + be * scal[2]);
     for (int c = tid; c < a.d; c += kThreads) {
         float num = 0.0f;
-        for (int j = 0; j < a.B; ++j) num = fmaf(pl[j], ld_elem(vb, static_cast<int64_t>(j) * a.qs.tok + c), num);
+        for (int j = 0; j < a.B; ++j) num = fmaf(pl[j], ld_elem(vb, static_cast<int64_t>(j) * a.ks.tok + c), num);
         float lin = 0.0f;
         for (int f = 0; f < F; ++f) lin = fmaf(ph[f], rec[s_offset(f, c, F)], lin);
         st_elem(out, c, (al * num + be * lin) * inv);

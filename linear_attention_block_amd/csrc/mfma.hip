@@ -46,14 +46,16 @@ struct Cfg {
     static constexpr int WPE = FW >= 128 ? 1 : 2;
 };
 
-// Resident work-groups per CU of the forward with QT query tiles. With two
-// tiles and FW >= 64 the second tile's operands and softmax do not fit two
-// work-groups' registers (measured: one work-group per CU, no spills, is as
-// fast as two with spills); at FW = 32 two work-groups are faster.
-template <int D, int FW, int QT>
+// Resident work-groups per CU of the forward with KT key tiles and G query
+// heads per K/V head (KT * G query tiles per pair). At two work-groups the
+// query tiles are kept apart by a scheduling barrier, so a tile's working set
+// does not overlap the next one's and G query heads fit the registers; the
+// second key tile's scores and operands do not at FW >= 64 (measured: one
+// work-group per CU, no spills, is as fast as two with spills).
+template <int D, int FW, int KT, int G>
 constexpr int fwd_wpe()
 {
-    return QT > 1 && FW >= 64 ? 1 : Cfg<D, FW>::WPE;
+    return KT > 1 && FW >= 64 ? 1 : Cfg<D, FW>::WPE;
 }
 
 // Issue the 128-bit loads of wave w's slice of the S tiles: load t gives lane
@@ -89,6 +91,18 @@ struct RowChunks {
             const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
             const int tr = t < nrows ? t : nrows - 1;
             v[i] = *reinterpret_cast<const u32x4*>(src + (tr * tok + ch * 8) * live);
+        }
+    }
+    // ROWS / RPH heads of RPH rows each, head j at src + j * head
+    template <int RPH>
+    __device__ __forceinline__ void load_heads(const uint16_t* src, int tok, int64_t head, int nrows, int tid,
+                                               int live = 1)
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
+            const int j = t / RPH, tr = t % RPH < nrows ? t % RPH : nrows - 1;
+            v[i] = *reinterpret_cast<const u32x4*>(src + j * head * live + (tr * tok + ch * 8) * live);
         }
     }
     // row-major copy, row stride RS
@@ -180,45 +194,54 @@ __device__ __forceinline__ void logit_range(const f32x16 (&u)[FW / 32], float& m
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
-// QT 32-token tiles of the block (QT = 2 for 32 < B <= 64).
-template <int D, int FW, int QT = 1>
+// KT 32-token tiles of the block (KT = 2 for 32 < B <= 64); the queries of
+// G query heads (head j at rows 32 KT j ..) that share one K/V head.
+template <int D, int FW, int KT = 1, int G = 1>
 struct alignas(16) FwdLds {
     using C = Cfg<D, FW>;
-    uint16_t Qs[32 * QT * C::RS];
-    uint16_t Ks[32 * QT * C::RS];
+    uint16_t Qs[32 * KT * G * C::RS];
+    uint16_t Ks[32 * KT * C::RS];
     uint16_t Ws[FW * C::RS];
-    uint16_t Vs[32 * QT * C::RS];  // V rows, read transposed by ds_read_b64_tr_b16
+    uint16_t Vs[32 * KT * C::RS];  // V rows, read transposed by ds_read_b64_tr_b16
     float Zs[C::F];
 };
 
 // The per-pair operands a thread stages through LDS, held in registers from
 // their global loads to the LDS writes.
-template <int D, int FW, int QT = 1>
+template <int D, int FW, int KT = 1, int G = 1>
 struct PairOperands {
     using C = Cfg<D, FW>;
-    RowChunks<D, C::NT, 32 * QT> q, k, v;
+    RowChunks<D, C::NT, 32 * KT * G> q;
+    RowChunks<D, C::NT, 32 * KT> k, v;
     f32x4 z;
     const float* rec;  // the state record the slice loads read (slot 0's for an out-of-range slot)
     bool valid;        // the slot id is in range
 
     // Issues the same loads whatever the pair: the loop's memory operations
     // are then a fixed sequence and every wait covers exactly the loads it
-    // needs. slot: the pair's slot id, read one pair ahead by the caller;
-    // live = 0 collapses the loads onto one location (no next pair).
+    // needs. p: the pair (request, K/V head); slot: its slot id, read one pair
+    // ahead by the caller; live = 0 collapses the loads onto one location (no
+    // next pair).
     __device__ __forceinline__ void load(const ForwardArgs& a, int p, int slot, int tid, int live = 1)
     {
-        const int r = p / a.H, h = p % a.H;
-        const int64_t base = static_cast<int64_t>(r) * a.qs.req + static_cast<int64_t>(h) * a.qs.head;
-        const int tok = static_cast<int>(a.qs.tok);
-        q.load(static_cast<const uint16_t*>(a.q) + base, tok, a.B, tid, live);
-        k.load(static_cast<const uint16_t*>(a.k) + base, tok, a.B, tid, live);
-        v.load(static_cast<const uint16_t*>(a.v) + base, tok, a.B, tid, live);
+        const int HK = a.H / G;
+        const int r = p / HK, hk = p % HK;
+        const int64_t qbase = static_cast<int64_t>(r) * a.qs.req + static_cast<int64_t>(hk) * G * a.qs.head;
+        const int64_t kbase = static_cast<int64_t>(r) * a.ks.req + static_cast<int64_t>(hk) * a.ks.head;
+        if constexpr (G == 1)
+            q.load(static_cast<const uint16_t*>(a.q) + qbase, static_cast<int>(a.qs.tok), a.B, tid, live);
+        else
+            q.template load_heads<32 * KT>(static_cast<const uint16_t*>(a.q) + qbase, static_cast<int>(a.qs.tok),
+                                           a.qs.head, a.B, tid, live);
+        const int ktok = static_cast<int>(a.ks.tok);
+        k.load(static_cast<const uint16_t*>(a.k) + kbase, ktok, a.B, tid, live);
+        v.load(static_cast<const uint16_t*>(a.v) + kbase, ktok, a.B, tid, live);
         valid = slot >= 0 && slot < a.num_slots;
-        rec = a.state + (static_cast<int64_t>(valid ? slot : 0) * a.H + h) * static_cast<int64_t>(D + 1) * C::F;
+        rec = a.state + (static_cast<int64_t>(valid ? slot : 0) * HK + hk) * static_cast<int64_t>(D + 1) * C::F;
         z = reinterpret_cast<const f32x4*>(rec + D * C::F)[(tid % (C::F / 4)) * live];
     }
 
-    __device__ __forceinline__ void store(FwdLds<D, FW, QT>& sm, int tid) const
+    __device__ __forceinline__ void store(FwdLds<D, FW, KT, G>& sm, int tid) const
     {
         q.template store_rows<C::RS>(sm.Qs, tid);
         k.template store_rows<C::RS>(sm.Ks, tid);
@@ -233,8 +256,8 @@ struct PairOperands {
 // phi(q) for token ln as bf16 B operands of unnormalised exponentials
 // e+ = exp(u - max u) and e- = exp(min u - u); returns the two normalisers
 // sp, sn and den = phi(q)^T Z.
-template <int D, int FW, int QT>
-__device__ __forceinline__ void phi_operands(const FwdLds<D, FW, QT>& sm, int q0, int ln, int g,
+template <int D, int FW, int KT, int G>
+__device__ __forceinline__ void phi_operands(const FwdLds<D, FW, KT, G>& sm, int q0, int ln, int g,
                                              bf16x8 (&pb)[Cfg<D, FW>::F / 16], float& sp, float& sn, float& den)
 {
     using C = Cfg<D, FW>;
@@ -302,15 +325,17 @@ __device__ __forceinline__ f32x16 linear_read(const f32x4 (&sv)[Cfg<D, FW>::NSL]
     return lacc;
 }
 
-// Block logits s^T = K Q^T over the QT key tiles (masked beyond B), row
-// maximum m, exponentials P and row sum l for query q0 + ln, then this wave's
-// 32 columns of P V. Key 32 kt + 8(v/4) + 4g + v%4 of tile kt lands in P
-// operand 2 kt + v/8, element v%8: the k order vt_frag reads V rows in.
-template <int D, int FW, int QT>
-__device__ __forceinline__ f32x16 block_softmax_pv(const ForwardArgs& a, const FwdLds<D, FW, QT>& sm, int q0, int wv,
-                                                   int ln, int g, float& m, float& l)
+// Block logits s^T = K Q^T over the KT key tiles (masked beyond B), row
+// maximum m, exponentials P and row sum l for the query in LDS row q0 + ln,
+// then this wave's 32 columns of P V. Key 32 kt + 8(v/4) + 4g + v%4 of tile kt
+// lands in P operand 2 kt + v/8, element v%8: the k order vt_frag reads V
+// rows in.
+template <int D, int FW, int KT, int G>
+__device__ __forceinline__ f32x16 block_softmax_pv(const ForwardArgs& a, const FwdLds<D, FW, KT, G>& sm, int q0,
+                                                   int wv, int ln, int g, float& m, float& l)
 {
     using C = Cfg<D, FW>;
+    constexpr int QT = KT;
     bf16x8 pp[2 * QT];
     {
         f32x16 sacc[QT];
@@ -379,40 +404,46 @@ __device__ __forceinline__ void merge_store(const ForwardArgs& a, const f32x16& 
 }
 
 // Persistent forward: WPE work-groups per compute unit, and work-group b
-// takes pairs b, b + G, b + 2G, ... (G = gridDim.x, a multiple of H, so every
-// pair of a work-group has the same head: W_h and the gate are loaded once).
-// Per pair: the operands arrive in LDS, then phi(q), the block softmax and P V
-// run while this wave's state slice streams in; the linear read consumes the
-// slice, the next pair's slice is issued at once, and the merge and stores
-// follow. The next pair's Q, K, V, Z loads are issued right after the current
-// ones reach LDS. The vector memory counter retires in issue order, so every
-// wait only covers loads issued before the ones still streaming.
-template <int D, int FW, int QT>
+// takes pairs b, b + NG, b + 2 NG, ... (NG = gridDim.x, a multiple of the
+// number of K/V heads, so every pair of a work-group has the same K/V head:
+// W and the gates are loaded once). A pair is (request, K/V head); with
+// G > 1 its G query heads share the K/V head's keys, values and state, and
+// run as G query tiles over the one state slice. Per pair: the operands
+// arrive in LDS, then per query tile phi(q), the block softmax and P V run
+// while this wave's state slice streams in and the linear read reads it;
+// after the last tile the next pair's slice is issued at once, and the merge
+// and stores follow. The next pair's Q, K, V, Z loads are issued right after
+// the current ones reach LDS. The vector memory counter retires in issue
+// order, so every wait only covers loads issued before the ones still
+// streaming.
+template <int D, int FW, int KT, int G>
 __global__ __launch_bounds__(64 * (D / 32))
-__attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, QT>(), fwd_wpe<D, FW, QT>()))) void forward_mfma_kernel(ForwardArgs a,
-                                                                                                 int npairs)
+__attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, KT, G>(), fwd_wpe<D, FW, KT, G>()))) void forward_mfma_kernel(
+    ForwardArgs a, int npairs)
 {
     using C = Cfg<D, FW>;
-    constexpr int F = C::F;
+    constexpr int F = C::F, NQT = KT * G;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int ln = lane & 31, g = lane >> 5;
-    const int G = gridDim.x;
+    const int NG = gridDim.x, HK = a.H / G;
     int p = blockIdx.x;
     if (p >= npairs) return;
-    const int h = p % a.H;
-    const float gamma = a.gamma[h];
+    const int hk = p % HK;
+    float gamma[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) gamma[j] = a.gamma[hk * G + j];
 
-    __shared__ FwdLds<D, FW, QT> sm;
+    __shared__ FwdLds<D, FW, KT, G> sm;
     {
         WChunks<D, FW, C::NT> wc;
-        wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
+        wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(hk) * a.wh, tid);
         wc.template store_rows<C::RS>(sm.Ws, tid);
     }
 
     // slot ids run one pair ahead of the operand loads (index clamped in range)
-    auto slot_of = [&](int pp) { return a.slot_ids[(pp < npairs ? pp : npairs - 1) / a.H]; };
-    const int count = (npairs - p + G - 1) / G;  // pairs of this work-group
-    PairOperands<D, FW, QT> op;
+    auto slot_of = [&](int pp) { return a.slot_ids[(pp < npairs ? pp : npairs - 1) / HK]; };
+    const int count = (npairs - p + NG - 1) / NG;  // pairs of this work-group
+    PairOperands<D, FW, KT, G> op;
     f32x4 sv[C::NSL];
     // issue order as in the loop (operands, then the slice, then the next
     // slot id), so the waits at the loop head are the same from either side
@@ -420,45 +451,52 @@ __attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, QT>(), fwd_wpe<D, FW, QT>())))
     __builtin_amdgcn_sched_barrier(0);
     load_state_slice(op.rec + wv * F * 32, lane, sv);
     __builtin_amdgcn_sched_barrier(0);
-    int slot_next = slot_of(p + G);
+    int slot_next = slot_of(p + NG);
     for (int k = 0; k < count; ++k) {
         // the last pair issues placeholder loads, so every trip runs the same
         // memory operations
         const int live = k + 1 < count ? 1 : 0;
-        const int pn = live ? p + G : p;
+        const int pn = live ? p + NG : p;
         const bool valid = op.valid;
-        const int r = p / a.H;
-        int slot_after = slot_of(pn + G);
+        const int r = p / HK;
+        int slot_after = slot_of(pn + NG);
         __syncthreads();  // every wave is done with the previous pair's LDS operands
         op.store(sm, tid);
         __syncthreads();
         op.load(a, pn, __builtin_amdgcn_readfirstlane(slot_next), tid, live);
-        // the first QT - 1 query tiles, then the last one, after whose linear
-        // read the state slice registers are free for the next pair's slice
+        // query tile qt: head hk G + qt / KT, rows 32 (qt % KT) ..; all but the
+        // last tile, then the last, after whose linear read the state slice
+        // registers are free for the next pair's slice
 #pragma unroll
-        for (int qt = 0; qt + 1 < QT; ++qt) {
+        for (int qt = 0; qt + 1 < NQT; ++qt) {
             f32x16 lacc, vacc;
             float sp, sn, den, m, l;
             {
                 bf16x8 pb[F / 16];
-                phi_operands<D, FW, QT>(sm, 32 * qt, ln, g, pb, sp, sn, den);
-                vacc = block_softmax_pv<D, FW, QT>(a, sm, 32 * qt, wv, ln, g, m, l);
+                phi_operands<D, FW, KT, G>(sm, 32 * qt, ln, g, pb, sp, sn, den);
+                vacc = block_softmax_pv<D, FW, KT, G>(a, sm, 32 * qt, wv, ln, g, m, l);
                 lacc = linear_read<D, FW>(sv, pb, sp, sn);
             }
-            merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, 32 * qt + ln, g, valid);
+            merge_store(a, vacc, lacc, gamma[qt / KT], m, l, den, sn, r, hk * G + qt / KT, wv, 32 * (qt % KT) + ln, g,
+                        valid);
+            // at two work-groups per CU the tiles must not overlap (registers);
+            // at one, letting them overlap is faster
+            if constexpr (fwd_wpe<D, FW, KT, G>() > 1) __builtin_amdgcn_sched_barrier(0);
         }
+        constexpr int QL = NQT - 1;
         f32x16 lacc, vacc;
         float sp, sn, den, m, l;
         {
             bf16x8 pb[F / 16];
-            phi_operands<D, FW, QT>(sm, 32 * (QT - 1), ln, g, pb, sp, sn, den);
-            vacc = block_softmax_pv<D, FW, QT>(a, sm, 32 * (QT - 1), wv, ln, g, m, l);
+            phi_operands<D, FW, KT, G>(sm, 32 * QL, ln, g, pb, sp, sn, den);
+            vacc = block_softmax_pv<D, FW, KT, G>(a, sm, 32 * QL, wv, ln, g, m, l);
             lacc = linear_read<D, FW>(sv, pb, sp, sn);
         }
         __builtin_amdgcn_sched_barrier(0);
         load_state_slice(op.rec + wv * F * 32, lane, sv, live);
         __builtin_amdgcn_sched_barrier(0);
-        merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, 32 * (QT - 1) + ln, g, valid);
+        merge_store(a, vacc, lacc, gamma[QL / KT], m, l, den, sn, r, hk * G + QL / KT, wv, 32 * (QL % KT) + ln, g,
+                    valid);
         // the slot id read at the top of this trip crosses the loop in a
         // vector register: its wait lands here, a whole trip after the load,
         // and covers no load issued since
@@ -617,8 +655,8 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
         f32x16 lacc, vacc;
         float sp, sn, den, m, l;
         bf16x8 pb[F / 16];
-        phi_operands<D, FW, 1>(sm.f, 0, ln, g, pb, sp, sn, den);
-        vacc = block_softmax_pv<D, FW, 1>(a, sm.f, 0, wv, ln, g, m, l);
+        phi_operands<D, FW, 1, 1>(sm.f, 0, ln, g, pb, sp, sn, den);
+        vacc = block_softmax_pv<D, FW, 1, 1>(a, sm.f, 0, wv, ln, g, m, l);
         lacc = linear_read<D, FW>(sv, pb, sp, sn);
         merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, ln, g, op.valid);
     }
@@ -1081,21 +1119,32 @@ static int compute_units()
 // Persistent grid: as many work-groups as can be resident (WPE per CU),
 // rounded down to a multiple of H so that each keeps one head, and no more
 // than there are pairs.
+template <int D, int FW, int KT, int G>
+static hipError_t launch_forward_kg(const ForwardArgs& a, hipStream_t s)
+{
+    const int hk = a.H / G, npairs = a.R * hk;
+    int64_t NG = static_cast<int64_t>(compute_units()) * fwd_wpe<D, FW, KT, G>();
+    NG = (NG / hk) * hk;
+    if (NG < hk) NG = hk;
+    if (NG > npairs) NG = npairs;
+    hipLaunchKernelGGL((forward_mfma_kernel<D, FW, KT, G>), dim3(static_cast<uint32_t>(NG)), dim3(64 * (D / 32)), 0, s,
+                       a, npairs);
+    return hipGetLastError();
+}
+
+// Blocks of up to 64 tokens with one query head per K/V head; up to 32 tokens
+// with 2 query heads per K/V head, or 4 at FW <= 64 (at FW = 128 four query
+// tiles and the 128-register state slice do not fit a wave's registers).
 template <int D, int FW>
 static hipError_t launch_forward(const ForwardArgs& a, hipStream_t s)
 {
-    const int npairs = a.R * a.H;
-    int64_t G = static_cast<int64_t>(compute_units()) * (a.B <= 32 ? fwd_wpe<D, FW, 1>() : fwd_wpe<D, FW, 2>());
-    G = (G / a.H) * a.H;
-    if (G < a.H) G = a.H;
-    if (G > npairs) G = npairs;
-    if (a.B <= 32)
-        hipLaunchKernelGGL((forward_mfma_kernel<D, FW, 1>), dim3(static_cast<uint32_t>(G)), dim3(64 * (D / 32)), 0, s,
-                           a, npairs);
-    else
-        hipLaunchKernelGGL((forward_mfma_kernel<D, FW, 2>), dim3(static_cast<uint32_t>(G)), dim3(64 * (D / 32)), 0, s,
-                           a, npairs);
-    return hipGetLastError();
+    if (a.G == 1) return a.B <= 32 ? launch_forward_kg<D, FW, 1, 1>(a, s) : launch_forward_kg<D, FW, 2, 1>(a, s);
+    if (a.B > 32) return hipErrorNotSupported;
+    if (a.G == 2) return launch_forward_kg<D, FW, 1, 2>(a, s);
+    if constexpr (FW <= 64) {
+        if (a.G == 4) return launch_forward_kg<D, FW, 1, 4>(a, s);
+    }
+    return hipErrorNotSupported;
 }
 
 template <int D>
@@ -1143,7 +1192,8 @@ static bool small_token_stride(int64_t tok) { return tok >= 0 && tok < (int64_t(
 hipError_t launch_forward_mfma(const ForwardArgs& a, hipStream_t s)
 {
     if (a.io != BHA_BF16 || a.B > 64) return hipErrorNotSupported;
-    if (!small_token_stride(a.qs.tok) || !small_token_stride(a.os.tok)) return hipErrorNotSupported;
+    if (!small_token_stride(a.qs.tok) || !small_token_stride(a.ks.tok) || !small_token_stride(a.os.tok))
+        return hipErrorNotSupported;
     if (a.d == 128) return forward_by_fw<128>(a, s);
     if (a.d == 64) return forward_by_fw<64>(a, s);
     return hipErrorNotSupported;
@@ -1175,8 +1225,9 @@ static hipError_t forward_commit_by_fw(const ForwardArgs& a, const CommitArgs& c
 
 hipError_t launch_forward_commit_mfma(const ForwardArgs& a, const CommitArgs& c, hipStream_t s)
 {
-    if (a.io != BHA_BF16 || a.B > 32) return hipErrorNotSupported;
-    if (!small_token_stride(a.qs.tok) || !small_token_stride(a.os.tok)) return hipErrorNotSupported;
+    if (a.io != BHA_BF16 || a.B > 32 || a.G != 1) return hipErrorNotSupported;
+    if (!small_token_stride(a.qs.tok) || !small_token_stride(a.ks.tok) || !small_token_stride(a.os.tok))
+        return hipErrorNotSupported;
     if (a.d == 128) return forward_commit_by_fw<128>(a, c, s);
     if (a.d == 64) return forward_commit_by_fw<64>(a, c, s);
     return hipErrorNotSupported;

@@ -285,3 +285,30 @@ def test_prefix_attention_workspace_size(lib):
     assert ws(ctypes.byref(_dims(head_dim=96)), 10) == UNSUP
     assert ws(ctypes.byref(_dims()), -1) == DIMS
     assert ws(None, 10) == NULL
+
+
+def fwd_gqa(lib, dims, hk=1, q=FAKE, k=FAKE, v=FAKE, w=FAKE, gamma=FAKE, state=FAKE, num_slots=8, slots=FAKE,
+            out=FAKE + (1 << 24), qs=None, kvs=None, outs=None):
+    qs = qs or _st()
+    kvs = kvs or _st(req=32 * hk * 128, tok=hk * 128)
+    outs = outs or _st()
+    P = ctypes.c_void_p
+    return lib.bha_block_forward_gqa(ctypes.byref(dims) if dims is not None else None, hk, P(q), ctypes.byref(qs),
+                                     P(k), P(v), ctypes.byref(kvs), P(w), 64 * 128, P(gamma), P(state), num_slots,
+                                     P(slots), P(out), ctypes.byref(outs), P(0))
+
+
+def test_forward_gqa_validation(lib):
+    # _dims() has 2 query heads
+    assert fwd_gqa(lib, None) == NULL
+    assert fwd_gqa(lib, _dims(num_requests=0), q=0, k=0, v=0, w=0, gamma=0, state=0, slots=0, out=0) == OK
+    for hk in (0, -1, 3, 4):
+        assert fwd_gqa(lib, _dims(), hk=hk) == DIMS, hk
+    for name in ("q", "k", "v", "w", "gamma", "state", "slots", "out"):
+        assert fwd_gqa(lib, _dims(), **{name: 0}) == NULL, name
+    assert fwd_gqa(lib, _dims(), gamma=FAKE + 2) == ALIGN
+    assert fwd_gqa(lib, _dims(), k=FAKE + 4) == ALIGN
+    assert fwd_gqa(lib, _dims(), kvs=_st(tok=128 + 4)) == STRIDE
+    assert fwd_gqa(lib, _dims(), num_slots=0) == DIMS
+    assert fwd_gqa(lib, _dims(head_dim=96)) == UNSUP
+    assert fwd_gqa(lib, _dims(), outs=bha_strides(0, 256, 128)) == STRIDE
