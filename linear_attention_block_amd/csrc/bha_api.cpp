@@ -204,7 +204,8 @@ extern "C" int bha_state_prefill(const bha_dims* dims, const void* k, const void
 static int64_t prefix_workspace_bytes(const bha_dims* d, int splits)
 {
     if (splits < 2) return 0;
-    return static_cast<int64_t>(d->num_requests) * d->num_heads * splits * prefix_part_floats(d->head_dim) * 4;
+    return static_cast<int64_t>(d->num_requests) * d->num_heads * prefix_query_tiles(d->block_size) * splits *
+           prefix_part_floats(d->head_dim) * 4;
 }
 
 extern "C" int64_t bha_prefix_attention_workspace(const bha_dims* dims, int64_t total_tokens)

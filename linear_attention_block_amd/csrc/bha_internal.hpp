@@ -93,6 +93,9 @@ __host__ __device__ inline int64_t prefix_part_floats(int d) { return 32 * stati
 // Key-sequence splits the matrix-core prefix attention uses for these sizes
 // (1 when the pairs alone fill the GPU or the path does not apply).
 int prefix_attention_splits(int R, int H, int d, int B, int io, int64_t total_tokens);
+// 32-query tiles of a block of B tokens in the matrix-core prefix attention
+// (one work-group per pair, query tile and key range).
+int prefix_query_tiles(int B);
 
 struct PhiArgs {
     int R, H, d, FW, B, io;

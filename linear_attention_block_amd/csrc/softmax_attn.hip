@@ -7,7 +7,8 @@
 //   s_it = c q_i . k_t over the prefix rows t and the block's B tokens,
 //   out_i = sum_t e^{s_it - m_i} v_t / sum_t e^{s_it - m_i},  m_i = max_t s_it.
 //
-// bf16 path (B <= 32): one work-group of four waves per (request, head). Wave
+// bf16 path (B <= 64): one work-group of four waves per (request, head,
+// 32-query tile of the block; every tile attends to all keys). Wave
 // w takes the 32-key chunks w, w + 4, ... of the prefix-then-block key
 // sequence and keeps its own running maximum, normaliser and 32 x d output
 // accumulator per query (online softmax); the four partial results are merged
@@ -83,7 +84,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 {
     using C = SaCfg<D>;
     constexpr int CH = D / 8;
-    const int pair = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
+    // work-group -> (pair, query tile qt: the block's queries 32 qt .. 32 qt + 31, key range sp)
+    const int nqt = (a.B + 31) >> 5;
+    const int sp = blockIdx.x % a.splits, pq = blockIdx.x / a.splits;
+    const int qt = pq % nqt, pair = pq / nqt;
     const int r = pair / a.H, h = pair % a.H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int ln = lane & 31, g = lane >> 5;
@@ -114,7 +118,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // Q fragments: query ln (rows past B read row B - 1; never stored)
     bf16x8 qf[C::NKB];
     {
-        const int qi = ln < a.B ? ln : a.B - 1;
+        const int qi = 32 * qt + ln < a.B ? 32 * qt + ln : a.B - 1;
         const uint16_t* qr = static_cast<const uint16_t*>(a.q) + boff + qi * a.qs.tok + g * (D / 2);
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) qf[kb] = *reinterpret_cast<const bf16x8*>(qr + 8 * kb);
@@ -197,8 +201,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
     // thread -> (query, 8 columns), 16-byte row stores
     for (int idx = tid; idx < 32 * CH; idx += 256) {
-        const int qi = idx / CH, c8 = (idx % CH) * 8;
-        if (qi >= a.B) continue;
+        const int qi = idx / CH, c8 = (idx % CH) * 8;  // row qi of the query tile
+        if (32 * qt + qi >= a.B) continue;
         float mw[4], M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             den += sc[w] * Ml[w * 32 + qi];
         }
         if (a.splits > 1) {
-            float* rec = a.part + (static_cast<int64_t>(pair) * a.splits + sp) * prefix_part_floats(D);
+            float* rec = a.part + (static_cast<int64_t>(pq) * a.splits + sp) * prefix_part_floats(D);
             f32x4 nv[2];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             pk[e] = static_cast<uint32_t>(bf16_bits(y[0])) | (static_cast<uint32_t>(bf16_bits(y[1])) << 16);
         }
         uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
-                         static_cast<int64_t>(h) * a.os.head + static_cast<int64_t>(qi) * a.os.tok + c8;
+                         static_cast<int64_t>(h) * a.os.head + static_cast<int64_t>(32 * qt + qi) * a.os.tok + c8;
         *reinterpret_cast<u32x4*>(orow) = u32x4{pk[0], pk[1], pk[2], pk[3]};
     }
 }
@@ -262,11 +266,12 @@ template <int D>
 __global__ __launch_bounds__(256) void prefix_attn_merge_kernel(PrefixArgs a)
 {
     constexpr int NQ = D / 4, G = 256 / NQ, PER = kSplitMax / G;
-    const int pair = blockIdx.x / a.B, qi = blockIdx.x % a.B;
+    const int pair = blockIdx.x / a.B, q = blockIdx.x % a.B;
+    const int qi = q & 31, pq = pair * ((a.B + 31) >> 5) + (q >> 5);  // row in its query tile; (pair, tile)
     const int r = pair / a.H, h = pair % a.H;
     const int tid = threadIdx.x, cq = tid % NQ, g = tid / NQ;
     constexpr int64_t pf = 32 * D + 64;
-    const float* base = a.part + static_cast<int64_t>(pair) * a.splits * pf;
+    const float* base = a.part + static_cast<int64_t>(pq) * a.splits * pf;
     __shared__ float wsh[kSplitMax];
     __shared__ f32x4 part[256];
     if (tid < 64) {
@@ -296,7 +301,7 @@ __global__ __launch_bounds__(256) void prefix_attn_merge_kernel(PrefixArgs a)
         const uint32_t lo = static_cast<uint32_t>(bf16_bits(y[0])) | (static_cast<uint32_t>(bf16_bits(y[1])) << 16);
         const uint32_t hi = static_cast<uint32_t>(bf16_bits(y[2])) | (static_cast<uint32_t>(bf16_bits(y[3])) << 16);
         uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
-                         static_cast<int64_t>(h) * a.os.head + static_cast<int64_t>(qi) * a.os.tok + 4 * tid;
+                         static_cast<int64_t>(h) * a.os.head + static_cast<int64_t>(q) * a.os.tok + 4 * tid;
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         *reinterpret_cast<u32x2*>(orow) = u32x2{lo, hi};
     }
@@ -402,10 +407,12 @@ constexpr int64_t kSplitMinChunks = 16;
 
 }  // namespace
 
+int prefix_query_tiles(int B) { return (B + 31) / 32; }
+
 int prefix_attention_splits(int R, int H, int d, int B, int io, int64_t total_tokens)
 {
-    if (io != BHA_BF16 || B > 32 || (d != 64 && d != 128) || R <= 0) return 1;
-    const int64_t pairs = static_cast<int64_t>(R) * H;
+    if (io != BHA_BF16 || B > 64 || (d != 64 && d != 128) || R <= 0) return 1;
+    const int64_t pairs = static_cast<int64_t>(R) * H * prefix_query_tiles(B);
     const int64_t avg_chunks = (total_tokens / R + B + 31) / 32;
     int64_t sp = (kSplitTargetWgs + pairs - 1) / pairs;
     sp = sp < avg_chunks / kSplitMinChunks ? sp : avg_chunks / kSplitMinChunks;
@@ -415,11 +422,12 @@ int prefix_attention_splits(int R, int H, int d, int B, int io, int64_t total_to
 
 hipError_t launch_prefix_attention_mfma(const PrefixArgs& a, hipStream_t s)
 {
-    if (a.io != BHA_BF16 || a.B > 32) return hipErrorNotSupported;
+    if (a.io != BHA_BF16 || a.B > 64) return hipErrorNotSupported;
     // per-lane offsets within a block and a chunk are 32-bit
     if (a.qs.tok >= (int64_t(1) << 25) || a.ps.tok >= (int64_t(1) << 25)) return hipErrorNotSupported;
     if (a.splits < 1 || a.splits > kSplitMax || (a.splits > 1 && !a.part)) return hipErrorInvalidValue;
-    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * a.splits)), block(256);
+    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * prefix_query_tiles(a.B) * a.splits)),
+        block(256);
     if (a.d == 128) hipLaunchKernelGGL(prefix_attn_mfma_kernel<128>, grid, block, 0, s, a);
     else if (a.d == 64) hipLaunchKernelGGL(prefix_attn_mfma_kernel<64>, grid, block, 0, s, a);
     else return hipErrorNotSupported;

@@ -390,7 +390,7 @@ def test_forward_commit_equals_forward_then_commit(dev, io, b):
 
 
 PREFIX = [("bf16", 128, 32), ("bf16", 128, 17), ("bf16", 64, 32), ("bf16", 64, 5), ("bf16", 128, 40),
-          ("f32", 128, 32), ("f32", 64, 9)]
+          ("bf16", 64, 64), ("f32", 128, 32), ("f32", 64, 9)]
 
 
 @pytest.mark.parametrize("io,d,b", PREFIX)
@@ -457,14 +457,14 @@ def test_prefix_attention_offsets_are_clamped(dev):
         assert torch.equal(y[r], y_r[0]), r
 
 
-@pytest.mark.parametrize("d", [128, 64])
-def test_prefix_attention_split_matches_oracle(dev, d):
+@pytest.mark.parametrize("d,b", [(128, 32), (64, 32), (128, 48)])
+def test_prefix_attention_split_matches_oracle(dev, d, b):
     # few pairs with long prefixes: the keys of each pair are split over several
     # work-groups (the request with no prefix leaves some splits without keys);
     # the same call with a workspace too small to split, and with one that
     # allows half the splits, agree with the oracle too
-    b = 32
-    case = synth.make_case("tiny", R=3, H=2, d=d, FW=64, B=b, io="bf16", blocks=(625, 625), gamma="uniform")
+    case = synth.make_case("tiny", R=3, H=2, d=d, FW=64, B=b, io="bf16", blocks=(20000 // b + 1, 20000 // b + 1),
+                           gamma="uniform")
     lens = np.array([0, 20000, 40])
     offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     kp = np.concatenate([case.prefix_k[r][:lens[r]] for r in range(case.R)])
@@ -473,7 +473,7 @@ def test_prefix_attention_split_matches_oracle(dev, d):
     q, k, v = (to_device(x, "bf16", dev) for x in (case.q, case.k, case.v))
     kd, vd, od = to_device(kp, "bf16", dev), to_device(vp, "bf16", dev), torch.from_numpy(offs).to(dev)
     full = bha.prefix_attention_workspace(case.R, case.H, d, b, T)
-    part = case.R * case.H * (32 * d + 64) * 4
+    part = case.R * case.H * ((b + 31) // 32) * (32 * d + 64) * 4
     assert full > 0 and full % part == 0
     n_split = full // part
     assert n_split >= 4
