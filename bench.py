@@ -659,7 +659,7 @@ def main() -> int:
             "traffic": None if args.staggered else read_traffic(args.config),
             "kernel": (f"bha_block_forward_commit: forward_commit_mfma_kernel<{d},{FW}> (1/{nd} of requests "
                        f"commit per launch)" if args.staggered else
-                       f"bha_block_forward: forward_mfma_kernel<{d},{FW}> (persistent, bf16 MFMA)"),
+                       f"bha_block_forward: forward_mfma_kernel<{d},{FW},1,1> (persistent, bf16 MFMA)"),
             "bytes_per_launch": fb,
             "avg_launch_us": fwd_avg * 1e6,
         },
