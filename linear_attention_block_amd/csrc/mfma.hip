@@ -84,13 +84,15 @@ struct RowChunks {
     // are stored, so the loads stay in flight until then.
     // live = 0 points every lane at src itself (a placeholder load of one
     // 16-byte location, for loops that keep their load sequence fixed).
+    // The rows are read once per launch: non-temporal loads (measured: the
+    // forward 84.0 -> 80.7 us at decode256).
     __device__ __forceinline__ void load(const uint16_t* src, int tok, int nrows, int tid, int live = 1)
     {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
             const int tr = t < nrows ? t : nrows - 1;
-            v[i] = *reinterpret_cast<const u32x4*>(src + (tr * tok + ch * 8) * live);
+            v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (tr * tok + ch * 8) * live));
         }
     }
     // ROWS / RPH heads of RPH rows each, head j at src + j * head
@@ -102,7 +104,8 @@ struct RowChunks {
         for (int i = 0; i < N; ++i) {
             const int idx = tid + i * NT, t = idx / CH, ch = idx % CH;
             const int j = t / RPH, tr = t % RPH < nrows ? t % RPH : nrows - 1;
-            v[i] = *reinterpret_cast<const u32x4*>(src + j * head * live + (tr * tok + ch * 8) * live);
+            v[i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(src + j * head * live + (tr * tok + ch * 8) * live));
         }
     }
     // row-major copy, row stride RS

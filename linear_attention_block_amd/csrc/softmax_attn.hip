@@ -74,8 +74,10 @@ __device__ __forceinline__ void sa_load_chunk(const KeySource& ks, int c, int la
         int tt = 32 * c + t;
         tt = tt < ks.nk ? tt : ks.nk - 1;  // past the end: the last key (masked)
         const int64_t off = tt < ks.np ? tt * ks.ptok : (tt - ks.np) * ks.btok;
-        kr[i] = *reinterpret_cast<const u32x4*>((tt < ks.np ? ks.prefix : ks.block) + off + ch * 8);
-        vr[i] = *reinterpret_cast<const u32x4*>((tt < ks.np ? vprefix : vblock) + off + ch * 8);
+        // read once per launch: non-temporal (measured 5.4 -> 5.7 TB/s at decode256)
+        kr[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>((tt < ks.np ? ks.prefix : ks.block) + off + ch * 8));
+        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>((tt < ks.np ? vprefix : vblock) + off + ch * 8));
     }
 }
 
