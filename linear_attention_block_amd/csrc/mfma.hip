@@ -392,17 +392,36 @@ __device__ __forceinline__ void merge_store(const ForwardArgs& a, const f32x16& 
     const float bl = be * __builtin_amdgcn_rcpf(sn);
     uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
                      static_cast<int64_t>(h) * a.os.head + (qi * static_cast<int>(a.os.tok) + 32 * wv + 4 * g);
+    uint32_t pk[4][2];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-        uint32_t pk[2];
+    for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int v0 = 4 * q4 + 2 * e;
             const float y0 = (al * vacc[v0] + bl * lacc[v0]) * inv;
             const float y1 = (al * vacc[v0 + 1] + bl * lacc[v0 + 1]) * inv;
-            pk[e] = static_cast<uint32_t>(bf16_bits(y0)) | (static_cast<uint32_t>(bf16_bits(y1)) << 16);
+            pk[q4][e] = static_cast<uint32_t>(bf16_bits(y0)) | (static_cast<uint32_t>(bf16_bits(y1)) << 16);
         }
-        *reinterpret_cast<uint2*>(orow + 8 * q4) = make_uint2(pk[0], pk[1]);
+    // Lanes n and n + 32 hold the two 8-byte halves of each 16-byte piece q4
+    // of row qi (columns 32 wv + 8 q4 ..): one row swap (v_permlane32_swap)
+    // per dword gives lane n pieces 0 and 2 and lane n + 32 pieces 1 and 3,
+    // so each store instruction writes 32 contiguous bytes per row with
+    // 16-byte lane stores (measured: 81.4 -> 78.3 us per forward at decode256
+    // against four 8-byte stores per lane). The partner lane has the same row,
+    // so both are active together.
+    uint16_t* const rbase = orow - 4 * g;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const uint32_t send = g ? pk[2 * j][e] : pk[2 * j + 1][e];
+            const auto sw = __builtin_amdgcn_permlane32_swap(send, send, false, false);
+            const uint32_t recv = g ? sw[0] : sw[1];  // the partner lane's send
+            w[e] = g ? recv : pk[2 * j][e];
+            w[2 + e] = g ? pk[2 * j + 1][e] : recv;
+        }
+        *reinterpret_cast<u32x4*>(rbase + 8 * (2 * j + g)) = u32x4{w[0], w[1], w[2], w[3]};
     }
 }
 
