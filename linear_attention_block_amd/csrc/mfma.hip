@@ -1220,12 +1220,19 @@ void prefill_mfma_kernel(CommitArgs a)
             __syncthreads();
         }
     } else {
-        // one buffer: phi and dS of a chunk between barriers
+        // one buffer: phi and dS of a chunk between barriers. The thread index
+        // is made opaque each trip, so the swizzled LDS addresses derived from
+        // it are computed in the loop rather than hoisted out of it: hoisted,
+        // they do not fit the registers beside the F = 256 state tiles, and
+        // their scratch reloads (each waiting for every load in flight) drain
+        // the K/V prefetch
         for (int c = 0; c < pp.nchunks; ++c) {
+            int tl = tid;
+            asm volatile("" : "+v"(tl));
             __syncthreads();  // W rows staged; every wave is done with the previous chunk
-            prefill_phi(pp, c, tid, Vs, Ps, Ws, vr, kf, zl);
+            prefill_phi(pp, c, tl, Vs, Ps, Ws, vr, kf, zl);
             __syncthreads();
-            prefill_ds<D, FW>(c, tid, Vs, Ps, st);
+            prefill_ds<D, FW>(c, tl, Vs, Ps, st);
         }
         __syncthreads();
     }
