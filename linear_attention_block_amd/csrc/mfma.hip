@@ -680,6 +680,12 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_tiles_mfma_kernel(Commit
 #pragma unroll 1
     for (int tt = 0; tt < KT; ++tt) {
         const int nt = B - 32 * tt;  // tokens of this tile (rows past it are clamped copies)
+        // LDS addresses derived from the thread index are computed per tile,
+        // not hoisted out of the loop into registers the tile needs
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, wv = tid >> 6;
+        const int ln = lane & 31, g = lane >> 5;
         if (tt > 0) {
             __syncthreads();  // every wave is done with the previous tile's K, V^T and phi(K)^T
             kc.load(static_cast<const uint16_t*>(a.k) + base + 32 * tt * tok, tok, nt, tid);
