@@ -244,12 +244,16 @@ struct PairOperands {
         z = reinterpret_cast<const f32x4*>(rec + D * C::F)[(tid % (C::F / 4)) * live];
     }
 
+    __device__ __forceinline__ void store_to(uint16_t* Qs, uint16_t* Ks, uint16_t* Vs, float* Zs, int tid) const
+    {
+        q.template store_rows<C::RS>(Qs, tid);
+        k.template store_rows<C::RS>(Ks, tid);
+        v.template store_rows<C::RS>(Vs, tid);
+        if (tid < C::F / 4) reinterpret_cast<f32x4*>(Zs)[tid] = z;
+    }
     __device__ __forceinline__ void store(FwdLds<D, FW, KT, G>& sm, int tid) const
     {
-        q.template store_rows<C::RS>(sm.Qs, tid);
-        k.template store_rows<C::RS>(sm.Ks, tid);
-        v.template store_rows<C::RS>(sm.Vs, tid);
-        if (tid < C::F / 4) reinterpret_cast<f32x4*>(sm.Zs)[tid] = z;
+        store_to(sm.Qs, sm.Ks, sm.Vs, sm.Zs, tid);
     }
 };
 
@@ -259,13 +263,14 @@ struct PairOperands {
 // phi(q) for token ln as bf16 B operands of unnormalised exponentials
 // e+ = exp(u - max u) and e- = exp(min u - u); returns the two normalisers
 // sp, sn and den = phi(q)^T Z.
-template <int D, int FW, int KT, int G>
-__device__ __forceinline__ void phi_operands(const FwdLds<D, FW, KT, G>& sm, int q0, int ln, int g,
-                                             bf16x8 (&pb)[Cfg<D, FW>::F / 16], float& sp, float& sn, float& den)
+template <int D, int FW>
+__device__ __forceinline__ void phi_operands_at(const uint16_t* Ws, const uint16_t* Qrows, const float* Zs, int ln,
+                                                int g, bf16x8 (&pb)[Cfg<D, FW>::F / 16], float& sp, float& sn,
+                                                float& den)
 {
     using C = Cfg<D, FW>;
     f32x16 u[FW / 32];
-    feature_logits<D, FW, C::RS>(sm.Ws, sm.Qs + q0 * C::RS, ln, g, u);
+    feature_logits<D, FW, C::RS>(Ws, Qrows, ln, g, u);
     constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
     for (int T = 0; T < FW / 32; ++T)
@@ -281,8 +286,8 @@ __device__ __forceinline__ void phi_operands(const FwdLds<D, FW, KT, G>& sm, int
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const int fw0 = 32 * T + 8 * q4 + 4 * g;
-            const f32x4 zp = *reinterpret_cast<const f32x4*>(sm.Zs + fw0);
-            const f32x4 zn = *reinterpret_cast<const f32x4*>(sm.Zs + FW + fw0);
+            const f32x4 zp = *reinterpret_cast<const f32x4*>(Zs + fw0);
+            const f32x4 zn = *reinterpret_cast<const f32x4*>(Zs + FW + fw0);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int v = 4 * q4 + e;
@@ -301,6 +306,13 @@ __device__ __forceinline__ void phi_operands(const FwdLds<D, FW, KT, G>& sm, int
     dp += __shfl_xor(dp, 32, 64);
     dn += __shfl_xor(dn, 32, 64);
     den = dp / sp + dn / sn;
+}
+
+template <int D, int FW, int KT, int G>
+__device__ __forceinline__ void phi_operands(const FwdLds<D, FW, KT, G>& sm, int q0, int ln, int g,
+                                             bf16x8 (&pb)[Cfg<D, FW>::F / 16], float& sp, float& sn, float& den)
+{
+    phi_operands_at<D, FW>(sm.Ws, sm.Qs + q0 * Cfg<D, FW>::RS, sm.Zs, ln, g, pb, sp, sn, den);
 }
 
 // Linear read of this wave's 32 columns: sum_f e_f S_f with the + half
@@ -522,6 +534,193 @@ __attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, KT, G>(), fwd_wpe<D, FW, KT, G
         // the slot id read at the top of this trip crosses the loop in a
         // vector register: its wait lands here, a whole trip after the load,
         // and covers no load issued since
+        asm volatile("" : "+v"(slot_after));
+        slot_next = slot_after;
+        p = pn;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Grouped forward with shared per-head operands (G query heads per K/V head,
+// blocks of up to 32 tokens). Every wave needs every query head's phi(q) and
+// P for its own 32 output columns; instead of each wave computing all of them
+// (the grouped form of forward_mfma_kernel), wave w computes phi(q) and the
+// block softmax of query heads w, w + NW, ... only, and the results go to LDS
+// as the B operands of the linear read and of P V (bf16, in lane order) plus
+// the per-query scalars; after a barrier every wave reads each head's operands
+// and does its own columns' linear read, P V and merge. The operands reuse the
+// LDS of Q and K, which phase one has finished with.
+// ---------------------------------------------------------------------------
+template <int D, int FW, int G>
+struct alignas(16) GqaLds {
+    using C = Cfg<D, FW>;
+    static constexpr int F = C::F;
+    static constexpr int QK_BYTES = (32 * G + 32) * C::RS * 2;  // Q of the G heads, then K
+    static constexpr int PB_BYTES = G * (F / 16) * 64 * 16;     // phi(q) operands
+    static constexpr int PP_BYTES = G * 2 * 64 * 16;            // P operands
+    static constexpr int SC_BYTES = G * 5 * 32 * 4;             // sp, sn, den, m, l per query
+    static constexpr int SH_BYTES = PB_BYTES + PP_BYTES + SC_BYTES;
+    static constexpr int U_BYTES = QK_BYTES > SH_BYTES ? QK_BYTES : SH_BYTES;
+    uint8_t u[U_BYTES];
+    uint16_t Ws[FW * C::RS];
+    uint16_t Vs[32 * C::RS];
+    float Zs[F];
+    __device__ uint16_t* qs() { return reinterpret_cast<uint16_t*>(u); }
+    __device__ uint16_t* ks() { return reinterpret_cast<uint16_t*>(u) + 32 * G * C::RS; }
+    __device__ bf16x8* pb() { return reinterpret_cast<bf16x8*>(u); }
+    __device__ bf16x8* pp() { return reinterpret_cast<bf16x8*>(u + PB_BYTES); }
+    __device__ float* sc() { return reinterpret_cast<float*>(u + PB_BYTES + PP_BYTES); }
+};
+
+// Resident work-groups per CU: two, unless the F = 256 state slice (128
+// registers) leaves room for one, or four heads' next-pair Q prefetch would
+// spill at FW = 64 (measured: one work-group without spills, 42.3 us against
+// 48.9 us with them, at 256 requests x 16 query heads over 4 K/V heads).
+template <int D, int FW, int G>
+constexpr int gqa_wpe()
+{
+    return FW >= 128 || (G >= 4 && FW >= 64) ? 1 : 2;
+}
+
+// Block logits s^T = K Q^T for the 32 staged queries at Qrows (masked beyond
+// B), row maximum m, exponentials P as bf16 B operands and row sum l.
+template <int D>
+__device__ __forceinline__ void block_softmax_at(const ForwardArgs& a, const uint16_t* Ks, const uint16_t* Qrows,
+                                                 int ln, int g, float& m, float& l, bf16x8 (&pp)[2])
+{
+    constexpr int RS = D + 8;
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < D / 16; ++kb)
+        sacc = mfma32(lds_frag(Ks + ln * RS + 16 * kb + 8 * g), lds_frag(Qrows + ln * RS + 16 * kb + 8 * g), sacc);
+    m = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int j = 8 * (v >> 2) + 4 * g + (v & 3);
+        const float s = j < a.B ? sacc[v] * a.scale : -INFINITY;
+        sacc[v] = s;
+        m = fmaxf(m, s);
+    }
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    l = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const float pe = __expf(sacc[v] - m);
+        l += pe;
+        pp[v >> 3][v & 7] = static_cast<__bf16>(pe);
+    }
+    l += __shfl_xor(l, 32, 64);
+}
+
+template <int D, int FW, int G>
+__global__ __launch_bounds__(64 * (D / 32))
+__attribute__((amdgpu_waves_per_eu(gqa_wpe<D, FW, G>(), gqa_wpe<D, FW, G>()))) void forward_gqa_mfma_kernel(
+    ForwardArgs a, int npairs)
+{
+    using C = Cfg<D, FW>;
+    constexpr int F = C::F, NW = C::NW, HPW = (G + NW - 1) / NW;  // phase-one heads per wave
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int ln = lane & 31, g = lane >> 5;
+    const int NG = gridDim.x, HK = a.H / G;
+    int p = blockIdx.x;
+    if (p >= npairs) return;
+    const int hk = p % HK;
+    float gamma[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) gamma[j] = a.gamma[hk * G + j];
+
+    __shared__ GqaLds<D, FW, G> sm;
+    uint16_t* const Qs = sm.qs();
+    uint16_t* const Ks = sm.ks();
+    bf16x8* const PB = sm.pb();
+    bf16x8* const PP = sm.pp();
+    float* const SC = sm.sc();
+    {
+        WChunks<D, FW, C::NT> wc;
+        wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(hk) * a.wh, tid);
+        wc.template store_rows<C::RS>(sm.Ws, tid);
+    }
+
+    // slot ids run one pair ahead of the operand loads (index clamped in range)
+    auto slot_of = [&](int pp) { return a.slot_ids[(pp < npairs ? pp : npairs - 1) / HK]; };
+    const int count = (npairs - p + NG - 1) / NG;
+    PairOperands<D, FW, 1, G> op;
+    f32x4 sv[C::NSL];
+    op.load(a, p, slot_of(p), tid);
+    __builtin_amdgcn_sched_barrier(0);
+    load_state_slice(op.rec + wv * F * 32, lane, sv);
+    __builtin_amdgcn_sched_barrier(0);
+    int slot_next = slot_of(p + NG);
+    for (int k = 0; k < count; ++k) {
+        const int live = k + 1 < count ? 1 : 0;
+        const int pn = live ? p + NG : p;
+        const bool valid = op.valid;
+        const int r = p / HK;
+        int slot_after = slot_of(pn + NG);
+        __syncthreads();  // every wave is done with the previous pair's LDS operands
+        op.store_to(Qs, Ks, sm.Vs, sm.Zs, tid);
+        __syncthreads();
+        op.load(a, pn, __builtin_amdgcn_readfirstlane(slot_next), tid, live);
+
+        // lane indices made opaque each trip: the LDS addresses derived from
+        // them are computed in the loop, not kept in registers across it
+        int tlane = lane;
+        asm volatile("" : "+v"(tlane));
+        const int tln = tlane & 31, tg = tlane >> 5;
+        // phase one: phi(q) and the block softmax of this wave's query heads
+        bf16x8 pbo[HPW][F / 16], ppo[HPW][2];
+        float sco[HPW][5];
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) {
+            const int j = wv + NW * i;
+            if (j < G) {
+                const uint16_t* const Qj = Qs + 32 * j * C::RS;
+                phi_operands_at<D, FW>(sm.Ws, Qj, sm.Zs, tln, tg, pbo[i], sco[i][0], sco[i][1], sco[i][2]);
+                block_softmax_at<D>(a, Ks, Qj, tln, tg, sco[i][3], sco[i][4], ppo[i]);
+            }
+        }
+        __syncthreads();  // Q and K are no longer read: their LDS takes the shared operands
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) {
+            const int j = wv + NW * i;
+            if (j < G) {
+#pragma unroll
+                for (int kb = 0; kb < F / 16; ++kb) PB[(j * (F / 16) + kb) * 64 + tlane] = pbo[i][kb];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) PP[(j * 2 + kb) * 64 + tlane] = ppo[i][kb];
+                if (tg == 0) {
+#pragma unroll
+                    for (int e = 0; e < 5; ++e) SC[(j * 5 + e) * 32 + tln] = sco[i][e];
+                }
+            }
+        }
+        __syncthreads();
+
+        // phase two: every query head's linear read, P V and merge for this
+        // wave's 32 columns; after the last head's linear read the state slice
+        // registers take the next pair's slice
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            bf16x8 pb[F / 16], pp[2];
+#pragma unroll
+            for (int kb = 0; kb < F / 16; ++kb) pb[kb] = PB[(j * (F / 16) + kb) * 64 + tlane];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) pp[kb] = PP[(j * 2 + kb) * 64 + tlane];
+            const float sp = SC[(j * 5 + 0) * 32 + tln], sn = SC[(j * 5 + 1) * 32 + tln];
+            const float den = SC[(j * 5 + 2) * 32 + tln], m = SC[(j * 5 + 3) * 32 + tln];
+            const float l = SC[(j * 5 + 4) * 32 + tln];
+            const f32x16 lacc = linear_read<D, FW>(sv, pb, sp, sn);
+            if (j == G - 1) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_state_slice(op.rec + wv * F * 32, lane, sv, live);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            f32x16 vacc = f32x16{};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) vacc = mfma32(vt_frag<C::RS>(sm.Vs, 32 * wv, kb, tlane), pp[kb], vacc);
+            merge_store(a, vacc, lacc, gamma[j], m, l, den, sn, r, hk * G + j, wv, tln, tg, valid);
+            __builtin_amdgcn_sched_barrier(0);  // one head's operands in registers at a time
+        }
         asm volatile("" : "+v"(slot_after));
         slot_next = slot_after;
         p = pn;
@@ -1298,18 +1497,28 @@ static hipError_t launch_forward_kg(const ForwardArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int D, int FW, int G>
+static hipError_t launch_forward_gqa(const ForwardArgs& a, hipStream_t s)
+{
+    const int hk = a.H / G, npairs = a.R * hk;
+    int64_t NG = static_cast<int64_t>(compute_units()) * gqa_wpe<D, FW, G>();
+    NG = (NG / hk) * hk;
+    if (NG < hk) NG = hk;
+    if (NG > npairs) NG = npairs;
+    hipLaunchKernelGGL((forward_gqa_mfma_kernel<D, FW, G>), dim3(static_cast<uint32_t>(NG)), dim3(64 * (D / 32)), 0,
+                       s, a, npairs);
+    return hipGetLastError();
+}
+
 // Blocks of up to 64 tokens with one query head per K/V head; up to 32 tokens
-// with 2 query heads per K/V head, or 4 at FW <= 64 (at FW = 128 four query
-// tiles and the 128-register state slice do not fit a wave's registers).
+// with 2 or 4 query heads per K/V head.
 template <int D, int FW>
 static hipError_t launch_forward(const ForwardArgs& a, hipStream_t s)
 {
     if (a.G == 1) return a.B <= 32 ? launch_forward_kg<D, FW, 1, 1>(a, s) : launch_forward_kg<D, FW, 2, 1>(a, s);
     if (a.B > 32) return hipErrorNotSupported;
-    if (a.G == 2) return launch_forward_kg<D, FW, 1, 2>(a, s);
-    if constexpr (FW <= 64) {
-        if (a.G == 4) return launch_forward_kg<D, FW, 1, 4>(a, s);
-    }
+    if (a.G == 2) return launch_forward_gqa<D, FW, 2>(a, s);
+    if (a.G == 4) return launch_forward_gqa<D, FW, 4>(a, s);
     return hipErrorNotSupported;
 }
 
