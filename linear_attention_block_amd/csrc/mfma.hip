@@ -441,8 +441,9 @@ __device__ __forceinline__ void merge_store(const ForwardArgs& a, const f32x16& 
 // takes pairs b, b + NG, b + 2 NG, ... (NG = gridDim.x, a multiple of the
 // number of K/V heads, so every pair of a work-group has the same K/V head:
 // W and the gates are loaded once). A pair is (request, K/V head); with
-// G > 1 its G query heads share the K/V head's keys, values and state, and
-// run as G query tiles over the one state slice. Per pair: the operands
+// G > 1 (not launched: grouped heads use forward_gqa_mfma_kernel, which
+// shares each head's phi(q) and P between the waves) its G query heads run as
+// G query tiles over the one state slice. Per pair: the operands
 // arrive in LDS, then per query tile phi(q), the block softmax and P V run
 // while this wave's state slice streams in and the linear read reads it;
 // after the last tile the next pair's slice is issued at once, and the merge
