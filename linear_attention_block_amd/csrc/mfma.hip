@@ -46,13 +46,13 @@ struct Cfg {
     static constexpr int WPE = FW >= 128 ? 1 : 2;
 };
 
-// Resident work-groups per CU of the forward with KT key tiles and G query
-// heads per K/V head (KT * G query tiles per pair). At two work-groups the
-// query tiles are kept apart by a scheduling barrier, so a tile's working set
-// does not overlap the next one's and G query heads fit the registers; the
-// second key tile's scores and operands do not at FW >= 64 (measured: one
-// work-group per CU, no spills, is as fast as two with spills).
-template <int D, int FW, int KT, int G>
+// Resident work-groups per CU of the forward with KT key (and query) tiles.
+// At two work-groups the query tiles are kept apart by a scheduling barrier,
+// so a tile's working set does not overlap the next one's; the second key
+// tile's scores and operands do not fit two work-groups' registers at
+// FW >= 64 (measured: one work-group per CU, no spills, is as fast as two
+// with spills).
+template <int D, int FW, int KT>
 constexpr int fwd_wpe()
 {
     return KT > 1 && FW >= 64 ? 1 : Cfg<D, FW>::WPE;
@@ -438,47 +438,42 @@ __device__ __forceinline__ void merge_store(const ForwardArgs& a, const f32x16& 
 }
 
 // Persistent forward: WPE work-groups per compute unit, and work-group b
-// takes pairs b, b + NG, b + 2 NG, ... (NG = gridDim.x, a multiple of the
-// number of K/V heads, so every pair of a work-group has the same K/V head:
-// W and the gates are loaded once). A pair is (request, K/V head); with
-// G > 1 (not launched: grouped heads use forward_gqa_mfma_kernel, which
-// shares each head's phi(q) and P between the waves) its G query heads run as
-// G query tiles over the one state slice. Per pair: the operands
-// arrive in LDS, then per query tile phi(q), the block softmax and P V run
-// while this wave's state slice streams in and the linear read reads it;
-// after the last tile the next pair's slice is issued at once, and the merge
-// and stores follow. The next pair's Q, K, V, Z loads are issued right after
-// the current ones reach LDS. The vector memory counter retires in issue
-// order, so every wait only covers loads issued before the ones still
+// takes pairs b, b + NG, b + 2 NG, ... (NG = gridDim.x, a multiple of H, so
+// every pair of a work-group has the same head: W_h and the gate are loaded
+// once). Per pair: the operands arrive in LDS, then per 32-query tile (KT of
+// them: two for 32 < B <= 64) phi(q), the block softmax over all KT key
+// tiles and P V run while this wave's state slice streams in and the linear
+// read reads it; after the last tile the next pair's slice is issued at once,
+// and the merge and stores follow. The next pair's Q, K, V, Z loads are issued
+// right after the current ones reach LDS. The vector memory counter retires in
+// issue order, so every wait only covers loads issued before the ones still
 // streaming.
-template <int D, int FW, int KT, int G>
+template <int D, int FW, int KT>
 __global__ __launch_bounds__(64 * (D / 32))
-__attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, KT, G>(), fwd_wpe<D, FW, KT, G>()))) void forward_mfma_kernel(
+__attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, KT>(), fwd_wpe<D, FW, KT>()))) void forward_mfma_kernel(
     ForwardArgs a, int npairs)
 {
     using C = Cfg<D, FW>;
-    constexpr int F = C::F, NQT = KT * G;
+    constexpr int F = C::F;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int ln = lane & 31, g = lane >> 5;
-    const int NG = gridDim.x, HK = a.H / G;
+    const int NG = gridDim.x;
     int p = blockIdx.x;
     if (p >= npairs) return;
-    const int hk = p % HK;
-    float gamma[G];
-#pragma unroll
-    for (int j = 0; j < G; ++j) gamma[j] = a.gamma[hk * G + j];
+    const int h = p % a.H;
+    const float gamma = a.gamma[h];
 
-    __shared__ FwdLds<D, FW, KT, G> sm;
+    __shared__ FwdLds<D, FW, KT> sm;
     {
         WChunks<D, FW, C::NT> wc;
-        wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(hk) * a.wh, tid);
+        wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
         wc.template store_rows<C::RS>(sm.Ws, tid);
     }
 
     // slot ids run one pair ahead of the operand loads (index clamped in range)
-    auto slot_of = [&](int pp) { return a.slot_ids[(pp < npairs ? pp : npairs - 1) / HK]; };
+    auto slot_of = [&](int pp) { return a.slot_ids[(pp < npairs ? pp : npairs - 1) / a.H]; };
     const int count = (npairs - p + NG - 1) / NG;  // pairs of this work-group
-    PairOperands<D, FW, KT, G> op;
+    PairOperands<D, FW, KT> op;
     f32x4 sv[C::NSL];
     // issue order as in the loop (operands, then the slice, then the next
     // slot id), so the waits at the loop head are the same from either side
@@ -493,45 +488,43 @@ __attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, KT, G>(), fwd_wpe<D, FW, KT, G
         const int live = k + 1 < count ? 1 : 0;
         const int pn = live ? p + NG : p;
         const bool valid = op.valid;
-        const int r = p / HK;
+        const int r = p / a.H;
         int slot_after = slot_of(pn + NG);
         __syncthreads();  // every wave is done with the previous pair's LDS operands
         op.store(sm, tid);
         __syncthreads();
         op.load(a, pn, __builtin_amdgcn_readfirstlane(slot_next), tid, live);
-        // query tile qt: head hk G + qt / KT, rows 32 (qt % KT) ..; all but the
-        // last tile, then the last, after whose linear read the state slice
-        // registers are free for the next pair's slice
+        // query tile qt: the block's rows 32 qt ..; all but the last tile, then
+        // the last, after whose linear read the state slice registers are free
+        // for the next pair's slice
 #pragma unroll
-        for (int qt = 0; qt + 1 < NQT; ++qt) {
+        for (int qt = 0; qt + 1 < KT; ++qt) {
             f32x16 lacc, vacc;
             float sp, sn, den, m, l;
             {
                 bf16x8 pb[F / 16];
-                phi_operands<D, FW, KT, G>(sm, 32 * qt, ln, g, pb, sp, sn, den);
-                vacc = block_softmax_pv<D, FW, KT, G>(a, sm, 32 * qt, wv, ln, g, m, l);
+                phi_operands<D, FW, KT, 1>(sm, 32 * qt, ln, g, pb, sp, sn, den);
+                vacc = block_softmax_pv<D, FW, KT, 1>(a, sm, 32 * qt, wv, ln, g, m, l);
                 lacc = linear_read<D, FW>(sv, pb, sp, sn);
             }
-            merge_store(a, vacc, lacc, gamma[qt / KT], m, l, den, sn, r, hk * G + qt / KT, wv, 32 * (qt % KT) + ln, g,
-                        valid);
+            merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, 32 * qt + ln, g, valid);
             // at two work-groups per CU the tiles must not overlap (registers);
             // at one, letting them overlap is faster
-            if constexpr (fwd_wpe<D, FW, KT, G>() > 1) __builtin_amdgcn_sched_barrier(0);
+            if constexpr (fwd_wpe<D, FW, KT>() > 1) __builtin_amdgcn_sched_barrier(0);
         }
-        constexpr int QL = NQT - 1;
+        constexpr int QL = KT - 1;
         f32x16 lacc, vacc;
         float sp, sn, den, m, l;
         {
             bf16x8 pb[F / 16];
-            phi_operands<D, FW, KT, G>(sm, 32 * QL, ln, g, pb, sp, sn, den);
-            vacc = block_softmax_pv<D, FW, KT, G>(a, sm, 32 * QL, wv, ln, g, m, l);
+            phi_operands<D, FW, KT, 1>(sm, 32 * QL, ln, g, pb, sp, sn, den);
+            vacc = block_softmax_pv<D, FW, KT, 1>(a, sm, 32 * QL, wv, ln, g, m, l);
             lacc = linear_read<D, FW>(sv, pb, sp, sn);
         }
         __builtin_amdgcn_sched_barrier(0);
         load_state_slice(op.rec + wv * F * 32, lane, sv, live);
         __builtin_amdgcn_sched_barrier(0);
-        merge_store(a, vacc, lacc, gamma[QL / KT], m, l, den, sn, r, hk * G + QL / KT, wv, 32 * (QL % KT) + ln, g,
-                    valid);
+        merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, 32 * QL + ln, g, valid);
         // the slot id read at the top of this trip crosses the loop in a
         // vector register: its wait lands here, a whole trip after the load,
         // and covers no load issued since
@@ -545,7 +538,7 @@ __attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, KT, G>(), fwd_wpe<D, FW, KT, G
 // Grouped forward with shared per-head operands (G query heads per K/V head,
 // blocks of up to 32 tokens). Every wave needs every query head's phi(q) and
 // P for its own 32 output columns; instead of each wave computing all of them
-// (the grouped form of forward_mfma_kernel), wave w computes phi(q) and the
+// (as the one-head kernel run over G query tiles would), wave w computes phi(q) and the
 // block softmax of query heads w, w + NW, ... only, and the results go to LDS
 // as the B operands of the linear read and of P V (bf16, in lane order) plus
 // the per-query scalars; after a barrier every wave reads each head's operands
@@ -1485,15 +1478,15 @@ static int compute_units()
 // Persistent grid: as many work-groups as can be resident (WPE per CU),
 // rounded down to a multiple of H so that each keeps one head, and no more
 // than there are pairs.
-template <int D, int FW, int KT, int G>
-static hipError_t launch_forward_kg(const ForwardArgs& a, hipStream_t s)
+template <int D, int FW, int KT>
+static hipError_t launch_forward_kt(const ForwardArgs& a, hipStream_t s)
 {
-    const int hk = a.H / G, npairs = a.R * hk;
-    int64_t NG = static_cast<int64_t>(compute_units()) * fwd_wpe<D, FW, KT, G>();
-    NG = (NG / hk) * hk;
-    if (NG < hk) NG = hk;
+    const int npairs = a.R * a.H;
+    int64_t NG = static_cast<int64_t>(compute_units()) * fwd_wpe<D, FW, KT>();
+    NG = (NG / a.H) * a.H;
+    if (NG < a.H) NG = a.H;
     if (NG > npairs) NG = npairs;
-    hipLaunchKernelGGL((forward_mfma_kernel<D, FW, KT, G>), dim3(static_cast<uint32_t>(NG)), dim3(64 * (D / 32)), 0, s,
+    hipLaunchKernelGGL((forward_mfma_kernel<D, FW, KT>), dim3(static_cast<uint32_t>(NG)), dim3(64 * (D / 32)), 0, s,
                        a, npairs);
     return hipGetLastError();
 }
@@ -1516,7 +1509,7 @@ static hipError_t launch_forward_gqa(const ForwardArgs& a, hipStream_t s)
 template <int D, int FW>
 static hipError_t launch_forward(const ForwardArgs& a, hipStream_t s)
 {
-    if (a.G == 1) return a.B <= 32 ? launch_forward_kg<D, FW, 1, 1>(a, s) : launch_forward_kg<D, FW, 2, 1>(a, s);
+    if (a.G == 1) return a.B <= 32 ? launch_forward_kt<D, FW, 1>(a, s) : launch_forward_kt<D, FW, 2>(a, s);
     if (a.B > 32) return hipErrorNotSupported;
     if (a.G == 2) return launch_forward_gqa<D, FW, 2>(a, s);
     if (a.G == 4) return launch_forward_gqa<D, FW, 4>(a, s);
