@@ -117,43 +117,51 @@ __global__ __launch_bounds__(kThreads) void forward_generic_kernel(ForwardArgs a
 }
 
 // ---------------------------------------------------------------------------
-// Commit and prefill: one work-group per (request, head, 32-column slice cs of
-// S), over the request's B block tokens (commit) or its packed token range
-// (prefill). Tokens are taken 16 at a time: phi(k_t) for the chunk into LDS, then each thread
-// accumulates its (f, c) entries of sum_t phi(k_t) v_t^T. The slice cs == 0
-// work-group also folds sum_t phi(k_t) into Z. Finally a read-modify-write.
+// Commit and prefill: one work-group of 512 threads per (request, head), over
+// the request's B block tokens (commit) or its packed token range (prefill),
+// 16 tokens at a time. W is staged once in LDS (rows padded by one float, so
+// the 64 rows a wave reads at one column fall in distinct banks). Per chunk:
+// the K and V rows to LDS, the feature logits u = k W^T (a wave takes one
+// token's logits), phi(k) per token (a wave per token and half), then thread
+// (column c, feature group fg) adds phi(k_t)[f] v_t[c] for its contiguous run
+// of features f and, for f < F, the Z sums. Finally one read-modify-write of
+// the record.
 // ---------------------------------------------------------------------------
-template <typename T, int FW>
-__global__ __launch_bounds__(kThreads) void commit_generic_kernel(CommitArgs a)
+constexpr int kCommitThreads = 512;
+
+template <typename T, int D, int FW>
+__global__ __launch_bounds__(kCommitThreads) void commit_generic_kernel(CommitArgs a)
 {
     constexpr int F = 2 * FW;
-    constexpr int KPT = F / 8;  // accumulators per thread: f = fg + 8 k
-    constexpr int TC = 16;      // tokens per chunk
-    const int nslice = a.d / 32;
-    const int64_t blk = blockIdx.x;
-    const int cs = static_cast<int>(blk % nslice);
-    const int64_t pair = blk / nslice;
-    const int h = static_cast<int>(pair % a.H);
-    const int64_t r = pair / a.H;
+    constexpr int NT = kCommitThreads;
+    constexpr int TC = 16;        // tokens per chunk
+    constexpr int WS = D + 1;     // padded W row (floats)
+    constexpr int NG = NT / D;    // feature groups: 4 at d = 128, 8 at d = 64
+    constexpr int KPT = F / NG;   // accumulators per thread: f = fg KPT .. + KPT - 1
+    const int pair = blockIdx.x;
+    const int h = pair % a.H, r = pair / a.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = tid & 31, fg = tid >> 5;
+    const int c = tid % D, fg = tid / D;
 
-    __shared__ float xk[TC][128];
-    __shared__ float u[TC][FW];
-    __shared__ float ph[TC][F];
-    __shared__ float vv[TC][32];
+    __shared__ float Ws[FW * WS];
+    __shared__ float xk[TC * D];
+    __shared__ float xv[TC * D];
+    __shared__ float u[TC * FW];
+    __shared__ __attribute__((aligned(16))) float ph[TC * F];
 
     const int slot = a.slot_ids[r];
     if (slot < 0 || slot >= a.num_slots) return;
-    float* rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(a.d + 1) * F;
     int64_t first_row;
     int n;
-    commit_rows(a, static_cast<int>(r), first_row, n);
+    commit_rows(a, r, first_row, n);
     if (n == 0) return;
-    const int64_t base = (first_row < 0 ? r * a.ks.req : first_row * a.ks.tok) + static_cast<int64_t>(h) * a.ks.head;
+    float* rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * F;
+    const int64_t base = (first_row < 0 ? static_cast<int64_t>(r) * a.ks.req : first_row * a.ks.tok) +
+                         static_cast<int64_t>(h) * a.ks.head;
     const T* kb = static_cast<const T*>(a.k) + base;
     const T* vb = static_cast<const T*>(a.v) + base;
     const T* W = static_cast<const T*>(a.w) + static_cast<int64_t>(h) * a.wh;
+    for (int idx = tid; idx < FW * D; idx += NT) Ws[(idx / D) * WS + idx % D] = ld_elem(W, idx);
 
     float acc[KPT];
 #pragma unroll
@@ -161,54 +169,55 @@ __global__ __launch_bounds__(kThreads) void commit_generic_kernel(CommitArgs a)
     float zacc = 0.0f;
 
     for (int t0 = 0; t0 < n; t0 += TC) {
-        const int nt = min(TC, n - t0);
-        for (int idx = tid; idx < nt * a.d; idx += kThreads) {
-            const int tt = idx / a.d, cc = idx % a.d;
-            xk[tt][cc] = ld_elem(kb, static_cast<int64_t>(t0 + tt) * a.ks.tok + cc);
-        }
-        for (int idx = tid; idx < nt * 32; idx += kThreads) {
-            const int tt = idx >> 5, cc = idx & 31;
-            vv[tt][cc] = ld_elem(vb, static_cast<int64_t>(t0 + tt) * a.ks.tok + cs * 32 + cc);
+        const int nt = n - t0 < TC ? n - t0 : TC;
+        __syncthreads();  // W staged; every thread is done with the previous chunk
+        for (int idx = tid; idx < nt * D; idx += NT) {
+            const int tt = idx / D, cc = idx % D;
+            const int64_t o = static_cast<int64_t>(t0 + tt) * a.ks.tok + cc;
+            xk[idx] = ld_elem(kb, o);
+            xv[idx] = ld_elem(vb, o);
         }
         __syncthreads();
-        for (int idx = tid; idx < nt * FW; idx += kThreads) {
+        for (int idx = tid; idx < nt * FW; idx += NT) {
             const int tt = idx / FW, j = idx % FW;
-            float s = 0.0f;
-            for (int cc = 0; cc < a.d; ++cc) s = fmaf(xk[tt][cc], ld_elem(W, static_cast<int64_t>(j) * a.d + cc), s);
-            u[tt][j] = s;
+            const float* kr = xk + tt * D;
+            const float* wr = Ws + j * WS;
+            float sdot = 0.0f;
+#pragma unroll 8
+            for (int cc = 0; cc < D; ++cc) sdot = fmaf(kr[cc], wr[cc], sdot);
+            u[idx] = sdot;
         }
         __syncthreads();
-        for (int tt = wave; tt < nt; tt += kThreads / 64) {
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const float sg = half == 0 ? 1.0f : -1.0f;
-                float mx = -INFINITY;
-                for (int j = lane; j < FW; j += 64) mx = fmaxf(mx, sg * u[tt][j]);
-                mx = wave_max(mx);
-                float sum = 0.0f;
-                for (int j = lane; j < FW; j += 64) sum += expf(sg * u[tt][j] - mx);
-                sum = wave_sum(sum);
-                for (int j = lane; j < FW; j += 64) ph[tt][half * FW + j] = expf(sg * u[tt][j] - mx) / sum;
-            }
+        for (int th = wave; th < 2 * nt; th += NT / 64) {
+            const int tt = th >> 1, half = th & 1;
+            const float sg = half == 0 ? 1.0f : -1.0f;
+            float mx = -INFINITY;
+            for (int j = lane; j < FW; j += 64) mx = fmaxf(mx, sg * u[tt * FW + j]);
+            mx = wave_max(mx);
+            float sum = 0.0f;
+            for (int j = lane; j < FW; j += 64) sum += expf(sg * u[tt * FW + j] - mx);
+            sum = wave_sum(sum);
+            for (int j = lane; j < FW; j += 64) ph[tt * F + half * FW + j] = expf(sg * u[tt * FW + j] - mx) / sum;
         }
         __syncthreads();
         for (int tt = 0; tt < nt; ++tt) {
-            const float vc = vv[tt][c];
+            const float vc = xv[tt * D + c];
+            const float4* pr = reinterpret_cast<const float4*>(ph + tt * F + fg * KPT);
 #pragma unroll
-            for (int k = 0; k < KPT; ++k) acc[k] = fmaf(ph[tt][fg + 8 * k], vc, acc[k]);
+            for (int k4 = 0; k4 < KPT / 4; ++k4) {
+                const float4 p4 = pr[k4];
+                acc[4 * k4] = fmaf(p4.x, vc, acc[4 * k4]);
+                acc[4 * k4 + 1] = fmaf(p4.y, vc, acc[4 * k4 + 1]);
+                acc[4 * k4 + 2] = fmaf(p4.z, vc, acc[4 * k4 + 2]);
+                acc[4 * k4 + 3] = fmaf(p4.w, vc, acc[4 * k4 + 3]);
+            }
         }
-        if (cs == 0) {
-            for (int f = tid; f < F; f += kThreads)
-                for (int tt = 0; tt < nt; ++tt) zacc += ph[tt][f];
-        }
-        __syncthreads();
+        if (tid < F)
+            for (int tt = 0; tt < nt; ++tt) zacc += ph[tt * F + tid];
     }
 #pragma unroll
-    for (int k = 0; k < KPT; ++k) {
-        const int64_t o = s_offset(fg + 8 * k, cs * 32 + c, F);
-        rec[o] += acc[k];
-    }
-    if (cs == 0 && tid < F) rec[static_cast<int64_t>(a.d) * F + tid] += zacc;
+    for (int k = 0; k < KPT; ++k) rec[s_offset(fg * KPT + k, c, F)] += acc[k];
+    if (tid < F) rec[static_cast<int64_t>(D) * F + tid] += zacc;
 }
 
 // ---------------------------------------------------------------------------
@@ -264,24 +273,26 @@ hipError_t launch_forward_generic(const ForwardArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int D>
 static void commit_dispatch(const CommitArgs& a, hipStream_t s, dim3 grid)
 {
     switch (a.FW) {
-        case 32: hipLaunchKernelGGL((commit_generic_kernel<T, 32>), grid, dim3(kThreads), 0, s, a); break;
-        case 64: hipLaunchKernelGGL((commit_generic_kernel<T, 64>), grid, dim3(kThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL((commit_generic_kernel<T, 128>), grid, dim3(kThreads), 0, s, a); break;
+        case 32: hipLaunchKernelGGL((commit_generic_kernel<T, D, 32>), grid, dim3(kCommitThreads), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((commit_generic_kernel<T, D, 64>), grid, dim3(kCommitThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((commit_generic_kernel<T, D, 128>), grid, dim3(kCommitThreads), 0, s, a); break;
     }
 }
 
 hipError_t launch_commit_generic(const CommitArgs& a, hipStream_t s)
 {
-    const int64_t nblk = static_cast<int64_t>(a.R) * a.H * (a.d / 32);
-    const dim3 grid(static_cast<uint32_t>(nblk));
-    if (a.io == BHA_BF16)
-        commit_dispatch<uint16_t>(a, s, grid);
-    else
-        commit_dispatch<float>(a, s, grid);
+    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H));
+    if (a.io == BHA_BF16) {
+        if (a.d == 128) commit_dispatch<uint16_t, 128>(a, s, grid);
+        else commit_dispatch<uint16_t, 64>(a, s, grid);
+    } else {
+        if (a.d == 128) commit_dispatch<float, 128>(a, s, grid);
+        else commit_dispatch<float, 64>(a, s, grid);
+    }
     return hipGetLastError();
 }
 
