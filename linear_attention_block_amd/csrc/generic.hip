@@ -1,11 +1,12 @@
-// Plain fp32-arithmetic kernels of block-hybrid attention for gfx950.
+// fp32-arithmetic kernels of block-hybrid attention for gfx950.
 //
 // They cover every supported size (d in {64,128}, FW in {32,64,128}, B <= 64)
-// and both I/O dtypes, with float32 loads, FMAs and accurate expf. They serve
-// float32 I/O (where bf16 matrix-core inputs would lose the precision the
-// caller asked for) and the block sizes the MFMA kernels do not tile. Each
-// work-group handles one token (forward, feature map) or one 32-column slice
-// of one state record (commit), staging its operands in LDS.
+// and both I/O dtypes, with fp32 products and sums throughout (the forward's
+// contractions on the fp32 matrix cores, everything else in fp32 vector code
+// with accurate expf). They serve float32 I/O (where bf16 matrix-core inputs
+// would lose the precision the caller asked for) and the shapes the bf16
+// kernels do not tile. The forward and the commit run one work-group per
+// (request, head); the feature map one wave per token and head.
 #include "bha_device.hpp"
 #include "bha_internal.hpp"
 
@@ -15,104 +16,215 @@ namespace {
 
 constexpr int kThreads = 256;
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 32x32 fp32 matrix-core product with two k values per step: lane l gives
+// A[l % 32][k = l / 32] and B[k = l / 32][l % 32], and holds D[i][l % 32] for
+// i = 8 (v / 4) + 4 (l / 32) + v % 4 in element v. Products and sums are fp32.
+__device__ __forceinline__ f32x16 mfma32f(float x, float y, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, c, 0, 0, 0);
+}
+
+// Four consecutive elements as floats (16- or 8-byte aligned).
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld4(const uint16_t* p)
+{
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+}
+
 // ---------------------------------------------------------------------------
-// Forward: one work-group per (request, head, token i). Computes
-//   s_j = scale q_i.k_j, m = max_j s_j, p_j = e^{s_j - m}, l = sum_j p_j,
-//   phi(q_i), lin = phi(q_i)^T S, den = phi(q_i)^T Z,
-//   y = (al sum_j p_j v_j + be lin) / (al l + be den)  (merge_weights).
+// Forward: one work-group of four waves per (request, query head), over query
+// tiles of 32 rows. With s_ij = scale q_i.k_j, m_i = max_j s_ij,
+// p_ij = e^{s_ij - m_i}, l_i = sum_j p_ij and den_i = phi(q_i)^T Z,
+//   y_i = (al_i sum_j p_ij v_j + be_i phi(q_i)^T S) / (al_i l_i + be_i den_i)
+// (merge_weights), computed as one product Y = P' V + Phi' S with the rows of
+// P and phi(Q) scaled by al_i / denominator and be_i / denominator. The three
+// products (feature logits U = Q W^T, block logits, Y) run on the fp32 matrix
+// cores; the row softmaxes go through LDS, eight threads per row. Operand k
+// indices are taken in runs of four per lane (one 16-byte load feeds four
+// steps); the state's 32-column panels make its operand loads whole 1 KB rows.
+// The record is read once per work-group.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int D, int FW>
 __global__ __launch_bounds__(kThreads) void forward_generic_kernel(ForwardArgs a)
 {
-    const int F = 2 * a.FW;
-    const int64_t blk = blockIdx.x;
-    const int i = static_cast<int>(blk % a.B);
-    const int64_t pair = blk / a.B;
-    const int h = static_cast<int>(pair % a.H);
-    const int64_t r = pair / a.H;
+    constexpr int F = 2 * FW;
+    constexpr int US = FW + 4;  // LDS row strides (floats)
+    constexpr int PS = 64 + 4;
+    constexpr int FS = F + 4;
+    constexpr int NU = FW / 32;  // feature-logit column tiles
+    constexpr int NQ = FW / 4;   // features per thread in the softmax
+    const int pair = blockIdx.x;
+    const int h = pair % a.H, r = pair / a.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int B = a.B, NK = (B + 31) >> 5;
 
-    __shared__ float xq[128];
-    __shared__ float u[128];
-    __shared__ float ph[256];
-    __shared__ float pl[64];
-    __shared__ float scal[4];
+    __shared__ __attribute__((aligned(16))) float Us[32 * US];
+    __shared__ __attribute__((aligned(16))) float Ps[32 * PS];
+    __shared__ __attribute__((aligned(16))) float Phs[32 * FS];
 
-    T* out = static_cast<T*>(a.out) + r * a.os.req + static_cast<int64_t>(i) * a.os.tok +
-             static_cast<int64_t>(h) * a.os.head;
+    T* const ob = static_cast<T*>(a.out) + static_cast<int64_t>(r) * a.os.req + static_cast<int64_t>(h) * a.os.head;
     const int slot = a.slot_ids[r];
     if (slot < 0 || slot >= a.num_slots) {
-        for (int c = tid; c < a.d; c += kThreads) st_elem(out, c, __builtin_nanf(""));
+        for (int idx = tid; idx < B * D; idx += kThreads)
+            st_elem(ob, static_cast<int64_t>(idx / D) * a.os.tok + idx % D, __builtin_nanf(""));
         return;
     }
     // query head h reads K/V head h / G: its keys, values, W and state
     const int hk = h / a.G, Hk = a.H / a.G;
-    const float* rec = a.state + (static_cast<int64_t>(slot) * Hk + hk) * static_cast<int64_t>(a.d + 1) * F;
-    const int64_t kbase = r * a.ks.req + static_cast<int64_t>(hk) * a.ks.head;
-    const T* q = static_cast<const T*>(a.q) + r * a.qs.req + static_cast<int64_t>(h) * a.qs.head +
-                 static_cast<int64_t>(i) * a.qs.tok;
-    const T* kb = static_cast<const T*>(a.k) + kbase;
-    const T* vb = static_cast<const T*>(a.v) + kbase;
+    const float* rec = a.state + (static_cast<int64_t>(slot) * Hk + hk) * static_cast<int64_t>(D + 1) * F;
+    const T* qb = static_cast<const T*>(a.q) + static_cast<int64_t>(r) * a.qs.req + static_cast<int64_t>(h) * a.qs.head;
+    const int64_t kvo = static_cast<int64_t>(r) * a.ks.req + static_cast<int64_t>(hk) * a.ks.head;
+    const T* kb = static_cast<const T*>(a.k) + kvo;
+    const T* vb = static_cast<const T*>(a.v) + kvo;
     const T* W = static_cast<const T*>(a.w) + static_cast<int64_t>(hk) * a.wh;
+    const float gam = a.gamma[h];
 
-    for (int c = tid; c < a.d; c += kThreads) xq[c] = ld_elem(q, c);
-    __syncthreads();
-
-    // xW (one column j per thread) and the block logits (one key j per thread)
-    for (int j = tid; j < a.FW; j += kThreads) {
-        float acc = 0.0f;
-        for (int c = 0; c < a.d; ++c) acc = fmaf(xq[c], ld_elem(W, static_cast<int64_t>(j) * a.d + c), acc);
-        u[j] = acc;
-    }
-    for (int j = tid; j < a.B; j += kThreads) {
-        float acc = 0.0f;
-        for (int c = 0; c < a.d; ++c) acc = fmaf(xq[c], ld_elem(kb, static_cast<int64_t>(j) * a.ks.tok + c), acc);
-        pl[j] = acc * a.scale;
-    }
-    __syncthreads();
-
-    if (wave < 2) {
-        // wave 0: softmax(u) into ph[0, FW); wave 1: softmax(-u) into ph[FW, F)
-        const float sg = wave == 0 ? 1.0f : -1.0f;
-        float mx = -INFINITY;
-        for (int j = lane; j < a.FW; j += 64) mx = fmaxf(mx, sg * u[j]);
-        mx = wave_max(mx);
-        float sum = 0.0f;
-        for (int j = lane; j < a.FW; j += 64) sum += expf(sg * u[j] - mx);
-        sum = wave_sum(sum);
-        for (int j = lane; j < a.FW; j += 64) ph[wave * a.FW + j] = expf(sg * u[j] - mx) / sum;
-    } else if (wave == 2) {
-        // row maximum, exponentials and their sum for the block logits
-        float m = -INFINITY;
-        for (int j = lane; j < a.B; j += 64) m = fmaxf(m, pl[j]);
-        m = wave_max(m);
-        float l = 0.0f;
-        for (int j = lane; j < a.B; j += 64) {
-            const float p = expf(pl[j] - m);
-            pl[j] = p;
-            l += p;
+    for (int i0 = 0; i0 < B; i0 += 32) {
+        // U and the block logits, one 32-column tile per wave. Rows past the
+        // block are clamped to its last row: computed, never used.
+        for (int job = wave; job < NU + NK; job += 4) {
+            const bool isu = job < NU;
+            const int j0 = 32 * (isu ? job : job - NU);
+            const T* arow = qb + static_cast<int64_t>(min(i0 + l32, B - 1)) * a.qs.tok;
+            const T* brow = isu ? W + static_cast<int64_t>(j0 + l32) * D
+                                : kb + static_cast<int64_t>(min(j0 + l32, B - 1)) * a.ks.tok;
+            f32x16 acc = {};
+#pragma unroll 4
+            for (int g = 0; g < D / 8; ++g) {
+                const int k0 = 8 * g + 4 * hf;
+                const f32x4 x = ld4(arow + k0), y = ld4(brow + k0);
+                acc = mfma32f(x[0], y[0], acc);
+                acc = mfma32f(x[1], y[1], acc);
+                acc = mfma32f(x[2], y[2], acc);
+                acc = mfma32f(x[3], y[3], acc);
+            }
+            float* dst = isu ? Us + j0 + l32 : Ps + j0 + l32;
+            const int ds = isu ? US : PS;
+            const float sc = isu ? 1.0f : a.scale;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) dst[(8 * (v >> 2) + 4 * hf + (v & 3)) * ds] = acc[v] * sc;
         }
-        l = wave_sum(l);
-        if (lane == 0) { scal[0] = m; scal[1] = l; }
-    }
-    __syncthreads();
-    if (wave == 0) {
-        float den = 0.0f;
-        for (int f = lane; f < F; f += 64) den = fmaf(ph[f], rec[static_cast<int64_t>(a.d) * F + f], den);
-        den = wave_sum(den);
-        if (lane == 0) scal[2] = den;
-    }
-    __syncthreads();
+        __syncthreads();
 
-    float al, be;
-    merge_weights(a.gamma[h], scal[0], al, be);
-    const float inv = 1.0f / (al * scal[1] + be * scal[2]);
-    for (int c = tid; c < a.d; c += kThreads) {
-        float num = 0.0f;
-        for (int j = 0; j < a.B; ++j) num = fmaf(pl[j], ld_elem(vb, static_cast<int64_t>(j) * a.ks.tok + c), num);
-        float lin = 0.0f;
-        for (int f = 0; f < F; ++f) lin = fmaf(ph[f], rec[s_offset(f, c, F)], lin);
-        st_elem(out, c, (al * num + be * lin) * inv);
+        // Row softmaxes: row i = tid / 8; thread p = tid % 8 takes keys p + 8t,
+        // and features (sign p / 4, quarter p % 4) of phi.
+        {
+            const int i = tid >> 3, p = tid & 7, q4 = p & 3, sgn = p >> 2;
+            float s[8];
+            float m = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int j = p + 8 * t;
+                s[t] = j < B ? Ps[i * PS + j] : -INFINITY;
+                m = fmaxf(m, s[t]);
+            }
+            m = fmaxf(m, __shfl_xor(m, 1, 64));
+            m = fmaxf(m, __shfl_xor(m, 2, 64));
+            m = fmaxf(m, __shfl_xor(m, 4, 64));
+            float l = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                s[t] = p + 8 * t < B ? expf(s[t] - m) : 0.0f;
+                l += s[t];
+            }
+            l += __shfl_xor(l, 1, 64);
+            l += __shfl_xor(l, 2, 64);
+            l += __shfl_xor(l, 4, 64);
+
+            const float sg = sgn ? -1.0f : 1.0f;
+            float e[NQ];
+            float mu = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < NQ; t += 4) {
+                const f32x4 u4 = *reinterpret_cast<const f32x4*>(Us + i * US + q4 * NQ + t);
+#pragma unroll
+                for (int z = 0; z < 4; ++z) {
+                    e[t + z] = sg * u4[z];
+                    mu = fmaxf(mu, e[t + z]);
+                }
+            }
+            mu = fmaxf(mu, __shfl_xor(mu, 1, 64));
+            mu = fmaxf(mu, __shfl_xor(mu, 2, 64));
+            float su = 0.0f;
+#pragma unroll
+            for (int t = 0; t < NQ; ++t) {
+                e[t] = expf(e[t] - mu);
+                su += e[t];
+            }
+            su += __shfl_xor(su, 1, 64);
+            su += __shfl_xor(su, 2, 64);
+            const float* Z = rec + static_cast<int64_t>(D) * F + sgn * FW + q4 * NQ;
+            float dz = 0.0f;
+#pragma unroll
+            for (int t = 0; t < NQ; t += 4) {
+                const f32x4 z4 = ld4(Z + t);
+                dz = fmaf(e[t], z4[0], dz);
+                dz = fmaf(e[t + 1], z4[1], dz);
+                dz = fmaf(e[t + 2], z4[2], dz);
+                dz = fmaf(e[t + 3], z4[3], dz);
+            }
+            dz /= su;
+            dz += __shfl_xor(dz, 1, 64);
+            dz += __shfl_xor(dz, 2, 64);
+            dz += __shfl_xor(dz, 4, 64);
+
+            float al, be;
+            merge_weights(gam, m, al, be);
+            const float inv = 1.0f / (al * l + be * dz);
+            const float ca = al * inv, cb = be * inv / su;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int j = p + 8 * t;
+                if (j < 32 * NK) Ps[i * PS + j] = s[t] * ca;
+            }
+#pragma unroll
+            for (int t = 0; t < NQ; t += 4)
+                *reinterpret_cast<f32x4*>(Phs + i * FS + sgn * FW + q4 * NQ + t) =
+                    f32x4{e[t] * cb, e[t + 1] * cb, e[t + 2] * cb, e[t + 3] * cb};
+        }
+        __syncthreads();
+
+        // Y = P' V + Phi' S, one 32-column tile per wave.
+        for (int ct = wave; ct < D / 32; ct += 4) {
+            const int c = 32 * ct + l32;
+            f32x16 acc = {};
+            for (int g = 0; g < 4 * NK; ++g) {
+                const int k0 = 8 * g + 4 * hf;
+                const f32x4 x = *reinterpret_cast<const f32x4*>(Ps + l32 * PS + k0);
+                float y[4];
+#pragma unroll
+                for (int z = 0; z < 4; ++z)
+                    y[z] = k0 + z < B ? ld_elem(vb, static_cast<int64_t>(k0 + z) * a.ks.tok + c) : 0.0f;
+                acc = mfma32f(x[0], y[0], acc);
+                acc = mfma32f(x[1], y[1], acc);
+                acc = mfma32f(x[2], y[2], acc);
+                acc = mfma32f(x[3], y[3], acc);
+            }
+            // S[f][c] for f = k0 .. k0 + 3 of this column are 16 contiguous bytes
+            const float* sp = rec + static_cast<int64_t>(ct) * (F / 4) * 128 + l32 * 4;
+#pragma unroll 4
+            for (int g = 0; g < F / 8; ++g) {
+                const int k0 = 8 * g + 4 * hf;
+                const f32x4 x = *reinterpret_cast<const f32x4*>(Phs + l32 * FS + k0);
+                const f32x4 y = ld4(sp + (k0 >> 2) * 128);
+                acc = mfma32f(x[0], y[0], acc);
+                acc = mfma32f(x[1], y[1], acc);
+                acc = mfma32f(x[2], y[2], acc);
+                acc = mfma32f(x[3], y[3], acc);
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int i = i0 + 8 * (v >> 2) + 4 * hf + (v & 3);
+                if (i < B) st_elem(ob, static_cast<int64_t>(i) * a.os.tok + c, acc[v]);
+            }
+        }
+        __syncthreads();  // the next tile rewrites Us, Ps and Phs
     }
 }
 
@@ -263,13 +375,26 @@ __global__ __launch_bounds__(64) void feature_map_generic_kernel(PhiArgs a)
 
 }  // namespace
 
+template <typename T, int D>
+static void forward_dispatch(const ForwardArgs& a, hipStream_t s, dim3 grid)
+{
+    switch (a.FW) {
+        case 32: hipLaunchKernelGGL((forward_generic_kernel<T, D, 32>), grid, dim3(kThreads), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((forward_generic_kernel<T, D, 64>), grid, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((forward_generic_kernel<T, D, 128>), grid, dim3(kThreads), 0, s, a); break;
+    }
+}
+
 hipError_t launch_forward_generic(const ForwardArgs& a, hipStream_t s)
 {
-    const int64_t nblk = static_cast<int64_t>(a.R) * a.H * a.B;
-    if (a.io == BHA_BF16)
-        hipLaunchKernelGGL(forward_generic_kernel<uint16_t>, dim3(static_cast<uint32_t>(nblk)), dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(forward_generic_kernel<float>, dim3(static_cast<uint32_t>(nblk)), dim3(kThreads), 0, s, a);
+    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H));
+    if (a.io == BHA_BF16) {
+        if (a.d == 128) forward_dispatch<uint16_t, 128>(a, s, grid);
+        else forward_dispatch<uint16_t, 64>(a, s, grid);
+    } else {
+        if (a.d == 128) forward_dispatch<float, 128>(a, s, grid);
+        else forward_dispatch<float, 64>(a, s, grid);
+    }
     return hipGetLastError();
 }
 

@@ -146,7 +146,7 @@ SWEEP = [
     ("bf16", 128, 128, 32), ("bf16", 64, 32, 8), ("bf16", 64, 64, 31), ("bf16", 64, 128, 32),
     ("bf16", 128, 64, 33), ("bf16", 64, 32, 64), ("bf16", 128, 64, 48), ("bf16", 128, 128, 64),
     ("bf16", 128, 32, 63), ("bf16", 64, 64, 40), ("bf16", 64, 128, 57),
-    ("f32", 128, 64, 32), ("f32", 64, 128, 5), ("f32", 128, 32, 64), ("f32", 64, 64, 1),
+    ("f32", 128, 64, 32), ("f32", 64, 128, 5), ("f32", 128, 32, 64), ("f32", 64, 64, 1), ("f32", 128, 128, 40),
 ]
 
 
