@@ -65,6 +65,44 @@ __device__ __forceinline__ void commit_rows(const CommitArgs& a, int r, int64_t&
     n = len > 0x7fffffff ? 0x7fffffff : static_cast<int>(len);
 }
 
+// Work-group order of a ragged prefill (one work-group per request and head,
+// each running over its request's whole token range). Work-groups are handed
+// out in blockIdx order, so in request order a long request dispatched late
+// runs on with the rest of the device idle. Longest first instead: position s
+// of the grid takes the request whose token count (as commit_rows clamps it)
+// has rank s in decreasing order, ties by request index; the ranks are a
+// permutation, so exactly one thread finds it. Up to kPrefillOrderMax
+// requests, their counts staged in `lens` (LDS, kPrefillOrderMax + 1 ints,
+// free again on return); commits of B rows per request and larger batches
+// keep request order. Every thread of the work-group calls it.
+constexpr int kPrefillOrderMax = 1024;
+
+template <int NT>
+__device__ int prefill_request(const CommitArgs& a, int s, int tid, int* lens)
+{
+    if (a.seq_offsets == nullptr || a.R > kPrefillOrderMax) return s;
+    for (int r = tid; r < a.R; r += NT) {
+        int64_t f;
+        int n;
+        commit_rows(a, r, f, n);
+        lens[r] = n;
+    }
+    __syncthreads();
+    for (int r = tid; r < a.R; r += NT) {
+        const int nr = lens[r];
+        int rank = 0;
+        for (int j = 0; j < a.R; ++j) {
+            const int nj = lens[j];
+            rank += nj > nr || (nj == nr && j < r);
+        }
+        if (rank == s) lens[a.R] = r;
+    }
+    __syncthreads();
+    const int pick = lens[a.R];
+    __syncthreads();  // every thread has its pick before the caller reuses lens
+    return pick;
+}
+
 // Softmax attention of the block's queries over the request's prefix and the
 // block: prefix rows seq_offsets[r] .. seq_offsets[r+1]-1 of kp, vp (clamped).
 struct PrefixArgs {

@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_generic_kernel(CommitAr
     constexpr int NG = NT / D;    // feature groups: 4 at d = 128, 8 at d = 64
     constexpr int KPT = F / NG;   // accumulators per thread: f = fg KPT .. + KPT - 1
     const int pair = blockIdx.x;
-    const int h = pair % a.H, r = pair / a.H;
+    const int h = pair % a.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = tid % D, fg = tid / D;
 
@@ -260,6 +260,8 @@ __global__ __launch_bounds__(kCommitThreads) void commit_generic_kernel(CommitAr
     __shared__ float xv[TC * D];
     __shared__ float u[TC * FW];
     __shared__ __attribute__((aligned(16))) float ph[TC * F];
+    static_assert(FW * WS >= kPrefillOrderMax + 1, "request counts fit the W buffer");
+    const int r = prefill_request<NT>(a, pair / a.H, tid, reinterpret_cast<int*>(Ws));
 
     const int slot = a.slot_ids[r];
     if (slot < 0 || slot >= a.num_slots) return;

@@ -1340,12 +1340,14 @@ void prefill_mfma_kernel(CommitArgs a)
     using P = PCfg<D, FW>;
     constexpr int F = P::F, NC = P::NC, NT = P::NT, CT = P::CT, RW = P::RW, KS = P::KS, VQ = P::VQ;
     const int pair = blockIdx.x;
-    const int r = pair / a.H, h = pair % a.H;
+    const int h = pair % a.H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int cs = wv % NC, r0 = (wv / NC) * RW;
     const int n16 = lane & 15, q = lane >> 4;
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[P::LDS];
+    static_assert(P::LDS >= 4 * (kPrefillOrderMax + 1), "request counts fit the LDS");
+    const int r = prefill_request<NT>(a, pair / a.H, tid, reinterpret_cast<int*>(smem));
     uint16_t* const Vs = reinterpret_cast<uint16_t*>(smem);
     uint16_t* const Ps = Vs + P::NBUF * CT * D;
     uint16_t* const Ws = Ps + P::NBUF * CT * F;

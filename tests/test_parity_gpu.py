@@ -295,6 +295,35 @@ def test_prefill_ragged_matches_oracle_build(dev, io, d, fw):
     assert worst <= TOL[io]
 
 
+@pytest.mark.parametrize("io,R", [("bf16", 1024), ("bf16", 1025), ("f32", 1024), ("f32", 1025)])
+def test_prefill_many_requests(dev, io, R):
+    # up to 1024 requests the work-groups take the requests longest first
+    # (ranked in the kernel), beyond that in request order; lengths 0..12
+    # give many ties and empty ranges. Each request's state against the
+    # oracle's build over its own tokens.
+    case = synth.make_case("tiny", R=R, H=1, d=64, FW=32, B=1, io=io, blocks=(0, 12), gamma="uniform")
+    lens = case.n_blocks.copy()
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    kp = np.concatenate([case.prefix_k[r][:lens[r]] for r in range(R)])
+    vp = np.concatenate([case.prefix_v[r][:lens[r]] for r in range(R)])
+    state = bha.new_state(case.num_slots, 1, case.d, case.FW, dev)
+    bha.state_prefill(to_device(kp, io, dev), to_device(vp, io, dev), torch.from_numpy(offs).to(dev),
+                      to_device(case.w, io, dev), state, torch.from_numpy(case.slot_ids).to(dev))
+    torch.cuda.synchronize()
+    S, Z = record_to_plain(state.cpu().numpy()[case.slot_ids], case.d, case.F)
+    worst = 0.0
+    for r in range(R):
+        n = int(lens[r])
+        if n == 0:
+            assert not S[r].any() and not Z[r].any()
+            continue
+        S_ref, Z_ref = oracle.state_build(case.prefix_k[r][:n, 0].astype(np.float64),
+                                          case.prefix_v[r][:n, 0].astype(np.float64), case.w[0])
+        worst = max(worst, normwise_err(S[r, 0], S_ref, None), normwise_err(Z[r, 0], Z_ref, None))
+    _log(f"[prefill-many] io={io} R={R} empty={(lens == 0).sum()} err {worst:.2e}")
+    assert worst <= TOL[io]
+
+
 def test_prefill_long_prompts_fused_kv(dev):
     # prompts of several thousand tokens (many 32-token chunks per work-group),
     # k and v as views of one fused [T][2][H][d] tensor, slots in shuffled order
