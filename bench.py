@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 METRIC = "active-block tokens/s through block-hybrid attn; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 KERNEL_SOURCES = ("linear_attention_block_amd/csrc/mfma.hip", "linear_attention_block_amd/csrc/bha_device.hpp",
+                  "linear_attention_block_amd/csrc/bha_internal.hpp",
                   "linear_attention_block_amd/csrc/bha_mfma.hpp")
 
 
@@ -256,7 +257,10 @@ def gqa_cycle(args, log) -> dict:
                    "denoise_steps": nd, "layers": nl},
         "roofline": {"bound": "hbm", "achieved": fb / fwd_avg / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": fb / fwd_avg / 1e9 / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": f"bha_block_forward_gqa: forward_mfma_kernel<{d},{FW},1,{G}>",
+                     "kernel": ("bha_block_forward_gqa: " +
+                                (f"forward_mfma_kernel<{d},{FW},{(B + 31) // 32}>" if G == 1 and B <= 64 else
+                                 f"forward_gqa_mfma_kernel<{d},{FW},{G}>" if G in (2, 4) and B <= 32 else
+                                 "forward_generic_kernel")),
                      "bytes_per_launch": fb, "avg_launch_us": fwd_avg * 1e6},
         "commit": {"kernel": "bha_state_commit over the K/V heads", "avg_launch_us": com_avg * 1e6,
                    "bytes_per_launch": cb, "achieved_GBps": cb / com_avg / 1e9},
@@ -659,7 +663,7 @@ def main() -> int:
             "traffic": None if args.staggered else read_traffic(args.config),
             "kernel": (f"bha_block_forward_commit: forward_commit_mfma_kernel<{d},{FW}> (1/{nd} of requests "
                        f"commit per launch)" if args.staggered else
-                       f"bha_block_forward: forward_mfma_kernel<{d},{FW},1,1> (persistent, bf16 MFMA)"),
+                       f"bha_block_forward: forward_mfma_kernel<{d},{FW},1> (persistent, bf16 MFMA)"),
             "bytes_per_launch": fb,
             "avg_launch_us": fwd_avg * 1e6,
         },
