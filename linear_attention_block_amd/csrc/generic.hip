@@ -228,16 +228,25 @@ __global__ __launch_bounds__(kThreads) void forward_generic_kernel(ForwardArgs a
     }
 }
 
+// 16x16 fp32 matrix-core product with four k values per step: lane l gives
+// A[l % 16][k = l / 16] and B[k = l / 16][l % 16], and holds
+// D[4 (l / 16) + v][l % 16] in element v.
+__device__ __forceinline__ f32x4 mfma16f(float x, float y, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
-// Commit and prefill: one work-group of 512 threads per (request, head), over
+// Commit and prefill: one work-group of eight waves per (request, head), over
 // the request's B block tokens (commit) or its packed token range (prefill),
-// 16 tokens at a time. W is staged once in LDS (rows padded by one float, so
-// the 64 rows a wave reads at one column fall in distinct banks). Per chunk:
-// the K and V rows to LDS, the feature logits u = k W^T (a wave takes one
-// token's logits), phi(k) per token (a wave per token and half), then thread
-// (column c, feature group fg) adds phi(k_t)[f] v_t[c] for its contiguous run
-// of features f and, for f < F, the Z sums. Finally one read-modify-write of
-// the record.
+// 32 tokens at a time. Each wave owns 32x32 tiles of the state (rows f,
+// columns c), held in matrix-core accumulators from the first load of the
+// record to its single write-back (the record's 32-column panels make both
+// whole 1 KB wave accesses). Per chunk: V rows to LDS; the feature logits
+// U = K W^T on 16x16 fp32 tiles (K and W rows straight from memory, k taken
+// in runs of four per lane); phi(k) per token, 16 threads per token (accurate
+// expf); the Z sums; then dS = phi(K)^T V on 32x32 fp32 tiles over the
+// chunk's tokens. Rows past the range have zero phi and zero V.
 // ---------------------------------------------------------------------------
 constexpr int kCommitThreads = 512;
 
@@ -245,23 +254,23 @@ template <typename T, int D, int FW>
 __global__ __launch_bounds__(kCommitThreads) void commit_generic_kernel(CommitArgs a)
 {
     constexpr int F = 2 * FW;
-    constexpr int NT = kCommitThreads;
-    constexpr int TC = 16;        // tokens per chunk
-    constexpr int WS = D + 1;     // padded W row (floats)
-    constexpr int NG = NT / D;    // feature groups: 4 at d = 128, 8 at d = 64
-    constexpr int KPT = F / NG;   // accumulators per thread: f = fg KPT .. + KPT - 1
+    constexpr int NT = kCommitThreads, NW = NT / 64;
+    constexpr int TC = 32;                               // tokens per chunk
+    constexpr int US = FW + 4, FS = F + 8, VS = D + 8;   // LDS row strides (floats)
+    constexpr int NTILE = (F / 32) * (D / 32);           // 32x32 state tiles
+    constexpr int TPW = (NTILE + NW - 1) / NW;           // state tiles per wave
+    constexpr int NUT = (TC / 16) * (FW / 16);           // 16x16 logit tiles per chunk
+    constexpr int PT = FW / 8;                           // features per thread in the softmax
     const int pair = blockIdx.x;
     const int h = pair % a.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = tid % D, fg = tid / D;
+    const int l32 = lane & 31, hf = lane >> 5, l16 = lane & 15, q = lane >> 4;
 
-    __shared__ float Ws[FW * WS];
-    __shared__ float xk[TC * D];
-    __shared__ float xv[TC * D];
-    __shared__ float u[TC * FW];
-    __shared__ __attribute__((aligned(16))) float ph[TC * F];
-    static_assert(FW * WS >= kPrefillOrderMax + 1, "request counts fit the W buffer");
-    const int r = prefill_request<NT>(a, pair / a.H, tid, reinterpret_cast<int*>(Ws));
+    __shared__ __attribute__((aligned(16))) float u[TC * US];
+    __shared__ __attribute__((aligned(16))) float ph[TC * FS];
+    __shared__ __attribute__((aligned(16))) float xv[TC * VS];
+    static_assert(TC * FS >= kPrefillOrderMax + 1, "request counts fit the phi buffer");
+    const int r = prefill_request<NT>(a, pair / a.H, tid, reinterpret_cast<int*>(ph));
 
     const int slot = a.slot_ids[r];
     if (slot < 0 || slot >= a.num_slots) return;
@@ -275,62 +284,121 @@ __global__ __launch_bounds__(kCommitThreads) void commit_generic_kernel(CommitAr
     const T* kb = static_cast<const T*>(a.k) + base;
     const T* vb = static_cast<const T*>(a.v) + base;
     const T* W = static_cast<const T*>(a.w) + static_cast<int64_t>(h) * a.wh;
-    for (int idx = tid; idx < FW * D; idx += NT) Ws[(idx / D) * WS + idx % D] = ld_elem(W, idx);
 
-    float acc[KPT];
+    // Element v of tile (ft, ct) is S[32 ft + 8 (v / 4) + 4 hf + v % 4][32 ct + l32]:
+    // four consecutive floats of the record per v / 4.
+    f32x16 acc[TPW];
 #pragma unroll
-    for (int k = 0; k < KPT; ++k) acc[k] = 0.0f;
+    for (int i = 0; i < TPW; ++i) {
+        const int ti = wave + NW * i;
+        if (ti < NTILE) {
+            const int ft = ti / (D / 32), ct = ti % (D / 32);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const f32x4 x = ld4(rec + (static_cast<int64_t>(ct) * (F / 4) + 8 * ft + 2 * b + hf) * 128 + l32 * 4);
+#pragma unroll
+                for (int z = 0; z < 4; ++z) acc[i][4 * b + z] = x[z];
+            }
+        } else {
+            acc[i] = f32x16{};
+        }
+    }
     float zacc = 0.0f;
 
     for (int t0 = 0; t0 < n; t0 += TC) {
         const int nt = n - t0 < TC ? n - t0 : TC;
-        __syncthreads();  // W staged; every thread is done with the previous chunk
-        for (int idx = tid; idx < nt * D; idx += NT) {
-            const int tt = idx / D, cc = idx % D;
-            const int64_t o = static_cast<int64_t>(t0 + tt) * a.ks.tok + cc;
-            xk[idx] = ld_elem(kb, o);
-            xv[idx] = ld_elem(vb, o);
+        __syncthreads();  // the previous chunk's phi and V reads are done
+        for (int idx = tid; idx < TC * D / 4; idx += NT) {
+            const int t = idx / (D / 4), c4 = idx % (D / 4);
+            const f32x4 x = t < nt ? ld4(vb + static_cast<int64_t>(t0 + t) * a.ks.tok + 4 * c4) : f32x4{};
+            *reinterpret_cast<f32x4*>(xv + t * VS + 4 * c4) = x;
         }
-        __syncthreads();
-        for (int idx = tid; idx < nt * FW; idx += NT) {
-            const int tt = idx / FW, j = idx % FW;
-            const float* kr = xk + tt * D;
-            const float* wr = Ws + j * WS;
-            float sdot = 0.0f;
-#pragma unroll 8
-            for (int cc = 0; cc < D; ++cc) sdot = fmaf(kr[cc], wr[cc], sdot);
-            u[idx] = sdot;
-        }
-        __syncthreads();
-        for (int th = wave; th < 2 * nt; th += NT / 64) {
-            const int tt = th >> 1, half = th & 1;
-            const float sg = half == 0 ? 1.0f : -1.0f;
-            float mx = -INFINITY;
-            for (int j = lane; j < FW; j += 64) mx = fmaxf(mx, sg * u[tt * FW + j]);
-            mx = wave_max(mx);
-            float sum = 0.0f;
-            for (int j = lane; j < FW; j += 64) sum += expf(sg * u[tt * FW + j] - mx);
-            sum = wave_sum(sum);
-            for (int j = lane; j < FW; j += 64) ph[tt * F + half * FW + j] = expf(sg * u[tt * FW + j] - mx) / sum;
-        }
-        __syncthreads();
-        for (int tt = 0; tt < nt; ++tt) {
-            const float vc = xv[tt * D + c];
-            const float4* pr = reinterpret_cast<const float4*>(ph + tt * F + fg * KPT);
+        for (int ut = wave; ut < NUT; ut += NW) {
+            const int mt = ut % (TC / 16), jt = ut / (TC / 16);
+            const int tr = 16 * mt + l16 < nt ? 16 * mt + l16 : nt - 1;  // past the range: a copy, phi zeroed
+            const T* krow = kb + static_cast<int64_t>(t0 + tr) * a.ks.tok;
+            const T* wrow = W + static_cast<int64_t>(16 * jt + l16) * D;
+            f32x4 c = {};
+#pragma unroll 4
+            for (int g = 0; g < D / 16; ++g) {
+                const int k0 = 16 * g + 4 * q;
+                const f32x4 x = ld4(krow + k0), y = ld4(wrow + k0);
+                c = mfma16f(x[0], y[0], c);
+                c = mfma16f(x[1], y[1], c);
+                c = mfma16f(x[2], y[2], c);
+                c = mfma16f(x[3], y[3], c);
+            }
 #pragma unroll
-            for (int k4 = 0; k4 < KPT / 4; ++k4) {
-                const float4 p4 = pr[k4];
-                acc[4 * k4] = fmaf(p4.x, vc, acc[4 * k4]);
-                acc[4 * k4 + 1] = fmaf(p4.y, vc, acc[4 * k4 + 1]);
-                acc[4 * k4 + 2] = fmaf(p4.z, vc, acc[4 * k4 + 2]);
-                acc[4 * k4 + 3] = fmaf(p4.w, vc, acc[4 * k4 + 3]);
+            for (int v = 0; v < 4; ++v) u[(16 * mt + 4 * q + v) * US + 16 * jt + l16] = c[v];
+        }
+        __syncthreads();
+        {
+            // token t = tid / 16; thread p = tid % 16 takes sign p / 8 and the
+            // features (p % 8) PT .. + PT - 1 of that half
+            const int t = tid >> 4, p = tid & 15, sgn = p >> 3, part = p & 7;
+            const float sg = sgn ? -1.0f : 1.0f;
+            float e[PT];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < PT; i += 4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(u + t * US + part * PT + i);
+#pragma unroll
+                for (int z = 0; z < 4; ++z) {
+                    e[i + z] = sg * x[z];
+                    mx = fmaxf(mx, e[i + z]);
+                }
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+            float sum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < PT; ++i) {
+                e[i] = expf(e[i] - mx);
+                sum += e[i];
+            }
+            sum += __shfl_xor(sum, 1, 64);
+            sum += __shfl_xor(sum, 2, 64);
+            sum += __shfl_xor(sum, 4, 64);
+            const float inv = t < nt ? 1.0f / sum : 0.0f;
+#pragma unroll
+            for (int i = 0; i < PT; i += 4)
+                *reinterpret_cast<f32x4*>(ph + t * FS + sgn * FW + part * PT + i) =
+                    f32x4{e[i] * inv, e[i + 1] * inv, e[i + 2] * inv, e[i + 3] * inv};
+        }
+        __syncthreads();
+        if (tid < F)
+            for (int t = 0; t < nt; ++t) zacc += ph[t * FS + tid];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int ti = wave + NW * i;
+            if (ti < NTILE) {
+                const int ft = ti / (D / 32), ct = ti % (D / 32);
+                const float* pa = ph + 32 * ft + l32;
+                const float* va = xv + 32 * ct + l32;
+#pragma unroll
+                for (int g = 0; g < TC / 8; ++g) {
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) {
+                        const int t = 8 * g + 4 * hf + z;
+                        acc[i] = mfma32f(pa[t * FS], va[t * VS], acc[i]);
+                    }
+                }
             }
         }
-        if (tid < F)
-            for (int tt = 0; tt < nt; ++tt) zacc += ph[tt * F + tid];
     }
 #pragma unroll
-    for (int k = 0; k < KPT; ++k) rec[s_offset(fg * KPT + k, c, F)] += acc[k];
+    for (int i = 0; i < TPW; ++i) {
+        const int ti = wave + NW * i;
+        if (ti < NTILE) {
+            const int ft = ti / (D / 32), ct = ti % (D / 32);
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                *reinterpret_cast<f32x4*>(rec + (static_cast<int64_t>(ct) * (F / 4) + 8 * ft + 2 * b + hf) * 128 +
+                                          l32 * 4) =
+                    f32x4{acc[i][4 * b], acc[i][4 * b + 1], acc[i][4 * b + 2], acc[i][4 * b + 3]};
+        }
+    }
     if (tid < F) rec[static_cast<int64_t>(D) * F + tid] += zacc;
 }
 
