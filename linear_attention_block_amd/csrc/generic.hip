@@ -236,17 +236,40 @@ __device__ __forceinline__ f32x4 mfma16f(float x, float y, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c, 0, 0, 0);
 }
 
+// Four consecutive elements as loaded (16 bytes of float, 8 of bf16), kept
+// raw while the load is in flight and widened when used.
+template <typename T>
+struct Raw4;
+template <>
+struct Raw4<float> {
+    f32x4 x;
+    __device__ __forceinline__ void load(const float* p) { x = *reinterpret_cast<const f32x4*>(p); }
+    __device__ __forceinline__ f32x4 f32() const { return x; }
+};
+template <>
+struct Raw4<uint16_t> {
+    uint2 x;
+    __device__ __forceinline__ void load(const uint16_t* p) { x = *reinterpret_cast<const uint2*>(p); }
+    __device__ __forceinline__ f32x4 f32() const
+    {
+        return f32x4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u), __uint_as_float(x.y << 16),
+                     __uint_as_float(x.y & 0xffff0000u)};
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Commit and prefill: one work-group of eight waves per (request, head), over
 // the request's B block tokens (commit) or its packed token range (prefill),
 // 32 tokens at a time. Each wave owns 32x32 tiles of the state (rows f,
 // columns c), held in matrix-core accumulators from the first load of the
 // record to its single write-back (the record's 32-column panels make both
-// whole 1 KB wave accesses). Per chunk: V rows to LDS; the feature logits
-// U = K W^T on 16x16 fp32 tiles (K and W rows straight from memory, k taken
-// in runs of four per lane); phi(k) per token, 16 threads per token (accurate
-// expf); the Z sums; then dS = phi(K)^T V on 32x32 fp32 tiles over the
-// chunk's tokens. Rows past the range have zero phi and zero V.
+// whole 1 KB wave accesses; the write-back is non-temporal). Per chunk: its K
+// and V rows, loaded into registers during the previous chunk, go to LDS and
+// the next chunk's loads are issued; the feature logits U = K W^T on 16x16
+// fp32 tiles (W rows from memory, k taken in runs of four per lane); phi(k)
+// per token, 16 threads per token (accurate expf); the Z sums; then
+// dS = phi(K)^T V on 32x32 fp32 tiles over the chunk's tokens. Rows past the
+// range hold copies of the last K row, zero phi and zero V.
 // ---------------------------------------------------------------------------
 constexpr int kCommitThreads = 512;
 
@@ -256,7 +279,8 @@ __global__ __launch_bounds__(kCommitThreads) void commit_generic_kernel(CommitAr
     constexpr int F = 2 * FW;
     constexpr int NT = kCommitThreads, NW = NT / 64;
     constexpr int TC = 32;                               // tokens per chunk
-    constexpr int US = FW + 4, FS = F + 8, VS = D + 8;   // LDS row strides (floats)
+    constexpr int US = FW + 4, FS = F + 8, VS = D + 8, KS = D + 4;  // LDS row strides (floats)
+    constexpr int LQ = TC * D / 4 / NT;                  // 4-element pieces of K (and V) per thread per chunk
     constexpr int NTILE = (F / 32) * (D / 32);           // 32x32 state tiles
     constexpr int TPW = (NTILE + NW - 1) / NW;           // state tiles per wave
     constexpr int NUT = (TC / 16) * (FW / 16);           // 16x16 logit tiles per chunk
@@ -269,6 +293,8 @@ __global__ __launch_bounds__(kCommitThreads) void commit_generic_kernel(CommitAr
     __shared__ __attribute__((aligned(16))) float u[TC * US];
     __shared__ __attribute__((aligned(16))) float ph[TC * FS];
     __shared__ __attribute__((aligned(16))) float xv[TC * VS];
+    __shared__ __attribute__((aligned(16))) float xk[TC * KS];
+    static_assert(LQ >= 1 && LQ * NT * 4 == TC * D, "whole pieces per thread");
     static_assert(TC * FS >= kPrefillOrderMax + 1, "request counts fit the phi buffer");
     const int r = prefill_request<NT>(a, pair / a.H, tid, reinterpret_cast<int*>(ph));
 
@@ -305,24 +331,41 @@ __global__ __launch_bounds__(kCommitThreads) void commit_generic_kernel(CommitAr
     }
     float zacc = 0.0f;
 
+    // piece j of thread tid: row (tid + NT j) / (D / 4), columns 4 ((tid + NT j) % (D / 4)) .. + 3;
+    // rows past the range load the last row
+    Raw4<T> kr[LQ], vr[LQ];
+    auto load_chunk = [&](int tc) {
+        const int ntc = n - tc < TC ? n - tc : TC;
+#pragma unroll
+        for (int j = 0; j < LQ; ++j) {
+            const int idx = tid + NT * j, t = idx / (D / 4), c4 = idx % (D / 4);
+            const int64_t o = static_cast<int64_t>(tc + (t < ntc ? t : ntc - 1)) * a.ks.tok + 4 * c4;
+            kr[j].load(kb + o);
+            vr[j].load(vb + o);
+        }
+    };
+    load_chunk(0);
+
     for (int t0 = 0; t0 < n; t0 += TC) {
         const int nt = n - t0 < TC ? n - t0 : TC;
-        __syncthreads();  // the previous chunk's phi and V reads are done
-        for (int idx = tid; idx < TC * D / 4; idx += NT) {
-            const int t = idx / (D / 4), c4 = idx % (D / 4);
-            const f32x4 x = t < nt ? ld4(vb + static_cast<int64_t>(t0 + t) * a.ks.tok + 4 * c4) : f32x4{};
-            *reinterpret_cast<f32x4*>(xv + t * VS + 4 * c4) = x;
+        __syncthreads();  // the previous chunk's K, phi and V reads are done
+#pragma unroll
+        for (int j = 0; j < LQ; ++j) {
+            const int idx = tid + NT * j, t = idx / (D / 4), c4 = idx % (D / 4);
+            *reinterpret_cast<f32x4*>(xk + t * KS + 4 * c4) = kr[j].f32();
+            *reinterpret_cast<f32x4*>(xv + t * VS + 4 * c4) = t < nt ? vr[j].f32() : f32x4{};
         }
+        if (t0 + TC < n) load_chunk(t0 + TC);
+        __syncthreads();
         for (int ut = wave; ut < NUT; ut += NW) {
             const int mt = ut % (TC / 16), jt = ut / (TC / 16);
-            const int tr = 16 * mt + l16 < nt ? 16 * mt + l16 : nt - 1;  // past the range: a copy, phi zeroed
-            const T* krow = kb + static_cast<int64_t>(t0 + tr) * a.ks.tok;
+            const float* krow = xk + (16 * mt + l16) * KS;
             const T* wrow = W + static_cast<int64_t>(16 * jt + l16) * D;
             f32x4 c = {};
 #pragma unroll 4
             for (int g = 0; g < D / 16; ++g) {
                 const int k0 = 16 * g + 4 * q;
-                const f32x4 x = ld4(krow + k0), y = ld4(wrow + k0);
+                const f32x4 x = *reinterpret_cast<const f32x4*>(krow + k0), y = ld4(wrow + k0);
                 c = mfma16f(x[0], y[0], c);
                 c = mfma16f(x[1], y[1], c);
                 c = mfma16f(x[2], y[2], c);
@@ -394,9 +437,10 @@ __global__ __launch_bounds__(kCommitThreads) void commit_generic_kernel(CommitAr
             const int ft = ti / (D / 32), ct = ti % (D / 32);
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                *reinterpret_cast<f32x4*>(rec + (static_cast<int64_t>(ct) * (F / 4) + 8 * ft + 2 * b + hf) * 128 +
-                                          l32 * 4) =
-                    f32x4{acc[i][4 * b], acc[i][4 * b + 1], acc[i][4 * b + 2], acc[i][4 * b + 3]};
+                __builtin_nontemporal_store(
+                    f32x4{acc[i][4 * b], acc[i][4 * b + 1], acc[i][4 * b + 2], acc[i][4 * b + 3]},
+                    reinterpret_cast<f32x4*>(rec + (static_cast<int64_t>(ct) * (F / 4) + 8 * ft + 2 * b + hf) * 128 +
+                                             l32 * 4));
         }
     }
     if (tid < F) rec[static_cast<int64_t>(D) * F + tid] += zacc;
