@@ -149,22 +149,30 @@ def cpu_baseline(layer, case, denoise, n_req, log):
     rec = layer["state"].cpu().numpy()[case.slot_ids[:n_req]]
     S, Z = record_to_plain(rec, d, 2 * FW)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(denoise):
-        oracle.block_forward_batch(q, k, v, w, g, S, Z, nthreads=nthreads)
-    oracle.state_commit_batch(S, Z, k, v, w, nthreads=nthreads)
-    dt = time.perf_counter() - t0
-    tokens = denoise * n_req * B
+
+    def cycle(n, threads):
+        S_, Z_ = S[:n].copy(), Z[:n].copy()
+        t0 = time.perf_counter()
+        for _ in range(denoise):
+            oracle.block_forward_batch(q[:n], k[:n], v[:n], w, g, S_, Z_, nthreads=threads)
+        oracle.state_commit_batch(S_, Z_, k[:n], v[:n], w, nthreads=threads)
+        return time.perf_counter() - t0
+
+    dt = cycle(n_req, nthreads)
+    n1 = max(1, n_req // 16)
+    dt1 = cycle(n1, 1)
     log(f"cpu oracle: {n_req} requests x {H} heads, {denoise} forwards + 1 commit in {dt:.2f} s "
-        f"on {nthreads} threads")
+        f"on {nthreads} threads; {n1} requests in {dt1:.2f} s on 1 thread")
     return {
-        "value": tokens / dt,
+        "value": denoise * n_req * B / dt,
         "unit": "tokens/s",
         "cores": nthreads,
         "kind": "oracle",
         "sample": (f"one block cycle ({denoise} forwards + 1 commit, one layer) of the first {n_req} "
                    f"of {R} requests, all {H} heads, same workload and state; fp64 C oracle, "
                    f"{dt:.2f} s wall"),
+        "value_1thread": denoise * n1 * B / dt1,
+        "sample_1thread": f"the same cycle for the first {n1} requests on one thread, {dt1:.2f} s wall",
     }
 
 
@@ -410,7 +418,7 @@ def main() -> int:
                     choices=["decode256", "b16", "longctx2k", "longctx16k", "longctx32k", "wide2048"])
     ap.add_argument("--layers", type=int, default=6, help="block-hybrid layer instances (default 6)")
     ap.add_argument("--denoise", type=int, default=32, help="denoising forwards per block")
-    ap.add_argument("--cpu-sample-requests", type=int, default=32)
+    ap.add_argument("--cpu-sample-requests", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate-commit", action="store_true",
                     help="run every denoising step as a plain forward and commit with bha_state_commit "
@@ -666,6 +674,8 @@ def main() -> int:
                        f"bha_block_forward: forward_mfma_kernel<{d},{FW},1> (persistent, bf16 MFMA)"),
             "bytes_per_launch": fb,
             "avg_launch_us": fwd_avg * 1e6,
+            "launches": len(fwd_ms),
+            "launch_us_p10_median_p90": [float(x) * 1e3 for x in np.percentile(fwd_ms, [10, 50, 90])],
         },
         "context": {"torch_copy_GBps": copy_gbps},
         "commit": None if args.staggered else {
