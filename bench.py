@@ -634,8 +634,18 @@ def main() -> int:
     c1.record()
     torch.cuda.synchronize()
     copy_gbps = 2 * ctx_src.numel() * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del ctx_src, ctx_dst
-    log(f"context: torch device copy of {fb / 1e6:.0f} MB runs at {copy_gbps:.0f} GB/s (read + write)")
+    # and a plain streaming read of the same bytes (a sum reduction)
+    ctx_sum = torch.empty((), dtype=torch.float32, device=dev)
+    torch.sum(ctx_src, dim=0, out=ctx_sum)
+    c0.record()
+    for _ in range(5):
+        torch.sum(ctx_src, dim=0, out=ctx_sum)
+    c1.record()
+    torch.cuda.synchronize()
+    read_gbps = ctx_src.numel() * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del ctx_src, ctx_dst, ctx_sum
+    log(f"context: torch device copy of {fb / 1e6:.0f} MB runs at {copy_gbps:.0f} GB/s (read + write); "
+        f"a sum over the same bytes reads at {read_gbps:.0f} GB/s")
 
     achieved = fb / fwd_avg / 1e9
     result = {
@@ -677,7 +687,7 @@ def main() -> int:
             "launches": len(fwd_ms),
             "launch_us_p10_median_p90": [float(x) * 1e3 for x in np.percentile(fwd_ms, [10, 50, 90])],
         },
-        "context": {"torch_copy_GBps": copy_gbps},
+        "context": {"torch_copy_GBps": copy_gbps, "torch_sum_read_GBps": read_gbps},
         "commit": None if args.staggered else {
             "kernel": ("bha_state_commit" if args.separate_commit
                        else "bha_block_forward_commit (last denoising step and commit, one pass)"),

@@ -27,6 +27,9 @@
 // contiguous ranges, one work-group each; a work-group then leaves its
 // unnormalised output, maximum and normaliser in fp32, and a second launch
 // rescales the partial results to their common maximum and sums them.
+//
+// fp32 path (float32 I/O, and bf16 with token strides too large for the
+// kernel above): the same layout and split on the fp32 matrix cores.
 #include "bha_device.hpp"
 #include "bha_internal.hpp"
 #include "bha_mfma.hpp"
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // issued together) and the G partial sums of each quad are added through LDS.
 constexpr int kSplitMax = 64;
 
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void prefix_attn_merge_kernel(PrefixArgs a)
 {
     constexpr int NQ = D / 4, G = 256 / NQ, PER = kSplitMax / G;
@@ -300,57 +303,80 @@ __global__ __launch_bounds__(256) void prefix_attn_merge_kernel(PrefixArgs a)
         f32x4 y = part[tid];
 #pragma unroll
         for (int j = 1; j < G; ++j) y += part[j * NQ + tid];
-        const uint32_t lo = static_cast<uint32_t>(bf16_bits(y[0])) | (static_cast<uint32_t>(bf16_bits(y[1])) << 16);
-        const uint32_t hi = static_cast<uint32_t>(bf16_bits(y[2])) | (static_cast<uint32_t>(bf16_bits(y[3])) << 16);
-        uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
-                         static_cast<int64_t>(h) * a.os.head + static_cast<int64_t>(q) * a.os.tok + 4 * tid;
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<u32x2*>(orow) = u32x2{lo, hi};
+        T* orow = static_cast<T*>(a.out) + static_cast<int64_t>(r) * a.os.req + static_cast<int64_t>(h) * a.os.head +
+                  static_cast<int64_t>(q) * a.os.tok + 4 * tid;
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t lo =
+                static_cast<uint32_t>(bf16_bits(y[0])) | (static_cast<uint32_t>(bf16_bits(y[1])) << 16);
+            const uint32_t hi =
+                static_cast<uint32_t>(bf16_bits(y[2])) | (static_cast<uint32_t>(bf16_bits(y[3])) << 16);
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<u32x2*>(orow) = u32x2{lo, hi};
+        } else {
+            *reinterpret_cast<f32x4*>(orow) = y;
+        }
     }
 }
 
-// Plain kernel for every size and both I/O dtypes, fp32 arithmetic with
-// accurate exponentials: one work-group per (request, head, query); 256 keys
-// per step, one thread per key for the scores and one per column for the
-// weighted sum of the values.
-constexpr int kGenThreads = 256;
-
-__device__ __forceinline__ float block_max(float x, float* red)
-{
-    x = wave_max(x);
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    if (lane == 0) red[wv] = x;
-    __syncthreads();
-    float y = red[0];
-    for (int w = 1; w < kGenThreads / 64; ++w) y = fmaxf(y, red[w]);
-    __syncthreads();
-    return y;
-}
-
-__device__ __forceinline__ float block_sum(float x, float* red)
-{
-    x = wave_sum(x);
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    if (lane == 0) red[wv] = x;
-    __syncthreads();
-    float y = 0.0f;
-    for (int w = 0; w < kGenThreads / 64; ++w) y += red[w];
-    __syncthreads();
-    return y;
-}
-
+// fp32 path, for float32 I/O and the bf16 shapes the kernel above does not
+// take: the same work-group layout (four waves per (request, head, query
+// tile, key range), each wave its own 32-key chunks, online softmax, merge at
+// the end), on the fp32 matrix cores (v_mfma_f32_32x32x2_f32: fp32 products
+// and sums) with accurate expf. Per chunk: s^T = K Q^T (lane = query; K rows
+// loaded straight from memory, Q from LDS; k taken in runs of four per lane),
+// then out^T += V^T P^T with P straight from the score accumulators (element v
+// of a lane is the key 8 (v/4) + 4 (lane/32) + v%4 of its k order). Output
+// column tile ct of lane j holds column CT j + ct, so each V row is one
+// contiguous CT-float load per lane. The four waves' results are scaled to a
+// common maximum and added into one LDS tile in a fixed order.
 template <typename T>
-__global__ __launch_bounds__(kGenThreads) void prefix_attn_generic_kernel(PrefixArgs a)
+__device__ __forceinline__ f32x4 sa_ld4(const T* p);
+template <>
+__device__ __forceinline__ f32x4 sa_ld4<float>(const float* p)
 {
-    const int64_t blk = blockIdx.x;
-    const int i = static_cast<int>(blk % a.B);
-    const int64_t pr = blk / a.B;
-    const int h = static_cast<int>(pr % a.H);
-    const int r = static_cast<int>(pr / a.H);
-    const int tid = threadIdx.x;
-    __shared__ float qs[128];
-    __shared__ float ps[kGenThreads];
-    __shared__ float red[kGenThreads / 64];
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+template <>
+__device__ __forceinline__ f32x4 sa_ld4<uint16_t>(const uint16_t* p)
+{
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 u = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+                 __uint_as_float(u[1] & 0xffff0000u)};
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void sa_ldn(const T* p, float (&x)[N])
+{
+    if constexpr (N == 4) {
+        const f32x4 y = sa_ld4<T>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = y[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] = ld_elem(p, i);
+    }
+}
+
+__device__ __forceinline__ f32x16 mfma32f(float x, float y, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(x, y, c, 0, 0, 0);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void prefix_attn_f32_kernel(PrefixArgs a)
+{
+    constexpr int CT = D / 32;   // output column tiles per wave
+    constexpr int QS = D + 4;    // LDS row stride of the query tile and the merged output (floats)
+    const int nqt = (a.B + 31) >> 5;
+    const int sp = blockIdx.x % a.splits, pq = blockIdx.x / a.splits;
+    const int qt = pq % nqt, pair = pq / nqt;
+    const int r = pair / a.H, h = pair % a.H;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int ln = lane & 31, g = lane >> 5;
+
+    __shared__ __attribute__((aligned(16))) float Qs[32 * QS];  // the query tile, then the merged output
+    __shared__ float Mm[4 * 32], Ml[4 * 32], Mx[32], Dn[32];
 
     int64_t s0 = a.seq_offsets[r], s1 = a.seq_offsets[r + 1];
     s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);
@@ -362,40 +388,135 @@ __global__ __launch_bounds__(kGenThreads) void prefix_attn_generic_kernel(Prefix
     const T* vp = static_cast<const T*>(a.vp) + s0 * a.ps.tok + hoff;
     const T* kb = static_cast<const T*>(a.k) + boff;
     const T* vb = static_cast<const T*>(a.v) + boff;
-    if (tid < a.d) qs[tid] = ld_elem(static_cast<const T*>(a.q), boff + i * a.qs.tok + tid);
+    // this work-group's chunks: [c_lo, c_hi) of the pair's 32-key chunks
+    const int64_t nall = (nk + 31) / 32;
+    const int64_t c_lo = nall * sp / a.splits, c_hi = nall * (sp + 1) / a.splits;
+
+    // query rows past B read row B - 1 (never stored)
+    for (int idx = tid; idx < 32 * D / 4; idx += 256) {
+        const int qi = idx / (D / 4), c4 = idx % (D / 4);
+        const int qr = 32 * qt + qi < a.B ? 32 * qt + qi : a.B - 1;
+        *reinterpret_cast<f32x4*>(Qs + qi * QS + 4 * c4) =
+            sa_ld4<T>(static_cast<const T*>(a.q) + boff + static_cast<int64_t>(qr) * a.qs.tok + 4 * c4);
+    }
     __syncthreads();
 
-    float m = -INFINITY, l = 0.0f, acc = 0.0f;
-    for (int64_t t0 = 0; t0 < nk; t0 += kGenThreads) {
-        const int64_t t = t0 + tid;
-        float s = -INFINITY;
-        if (t < nk) {
-            const T* kr = t < np ? kp + t * a.ps.tok : kb + (t - np) * a.qs.tok;
-            float dot = 0.0f;
-            for (int e = 0; e < a.d; ++e) dot = fmaf(qs[e], ld_elem(kr, e), dot);
-            s = dot * a.scale;
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x16 acc[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[ct] = f32x16{};
+    for (int64_t c = c_lo + wv; c < c_hi; c += 4) {
+        // key row of lane ln (past the end: the last key, masked)
+        int64_t t = 32 * c + ln;
+        t = t < nk ? t : nk - 1;
+        const T* krow = t < np ? kp + t * a.ps.tok : kb + (t - np) * a.qs.tok;
+        f32x16 sacc = f32x16{};
+#pragma unroll 4
+        for (int gi = 0; gi < D / 8; ++gi) {
+            const int k0 = 8 * gi + 4 * g;
+            const f32x4 x = sa_ld4<T>(krow + k0);
+            const f32x4 y = *reinterpret_cast<const f32x4*>(Qs + ln * QS + k0);
+            sacc = mfma32f(x[0], y[0], sacc);
+            sacc = mfma32f(x[1], y[1], sacc);
+            sacc = mfma32f(x[2], y[2], sacc);
+            sacc = mfma32f(x[3], y[3], sacc);
         }
-        const float m_new = fmaxf(m, block_max(s, red));
-        const float alpha = expf(m - m_new);
-        const float p = t < nk ? expf(s - m_new) : 0.0f;
-        ps[tid] = p;
-        l = l * alpha + block_sum(p, red);
-        if (tid < a.d) {
-            acc *= alpha;
-            const int64_t tn = nk - t0 < kGenThreads ? nk - t0 : kGenThreads;
-            for (int64_t j = 0; j < tn; ++j) {
-                const int64_t tt = t0 + j;
-                const T* vr = tt < np ? vp + tt * a.ps.tok : vb + (tt - np) * a.qs.tok;
-                acc = fmaf(ps[j], ld_elem(vr, tid), acc);
+        // online softmax of query ln over the chunk's keys 8 (v/4) + 4 g + v%4
+        float mc = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t j = 32 * c + 8 * (v >> 2) + 4 * g + (v & 3);
+            const float sv = j < nk ? sacc[v] * a.scale : -INFINITY;
+            sacc[v] = sv;
+            mc = fmaxf(mc, sv);
+        }
+        mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
+        const float m_new = fmaxf(m_run, mc);  // finite: the chunk has a key
+        const float alpha = expf(m_run - m_new);
+        float ls = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            sacc[v] = expf(sacc[v] - m_new);
+            ls += sacc[v];
+        }
+        ls += __shfl_xor(ls, 32, 64);
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[ct][v] *= alpha;
+        // out^T += V^T P^T: lane (ln, g) gives V[key][CT ln + ct] for the
+        // keys 8 b + 4 g + z of its k order
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                int64_t tv = 32 * c + 8 * b + 4 * g + z;
+                tv = tv < nk ? tv : nk - 1;  // weight 0
+                float vv[CT];
+                sa_ldn<T, CT>((tv < np ? vp + tv * a.ps.tok : vb + (tv - np) * a.qs.tok) + CT * ln, vv);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) acc[ct] = mfma32f(vv[ct], sacc[4 * b + z], acc[ct]);
             }
-        }
-        m = m_new;
-        __syncthreads();
     }
-    if (tid < a.d) {
-        T* out = static_cast<T*>(a.out) + static_cast<int64_t>(r) * a.os.req + static_cast<int64_t>(h) * a.os.head +
-                 static_cast<int64_t>(i) * a.os.tok;
-        st_elem(out, tid, acc / l);
+
+    // merge the four waves: each scales its rows to the common maximum, then
+    // they add into Qs (now the output tile [query][column]) in wave order
+    if (g == 0) {
+        Mm[wv * 32 + ln] = m_run;
+        Ml[wv * 32 + ln] = l_run;
+    }
+    __syncthreads();  // also: every wave is done with the query tile
+    {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, Mm[w * 32 + ln]);
+        float den = 0.0f, mine = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            // a wave (or, split, the whole work-group) with no keys: weight 0
+            const float mw = Mm[w * 32 + ln];
+            const float sc = mw == -INFINITY ? 0.0f : expf(mw - M);
+            den += sc * Ml[w * 32 + ln];
+            if (w == wv) mine = sc;
+        }
+        if (wv == 0 && g == 0) {
+            Mx[ln] = M;
+            Dn[ln] = den;
+        }
+        for (int w = 0; w < 4; ++w) {
+            if (w == wv) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        float* o = Qs + ln * QS + CT * (8 * (v >> 2) + 4 * g + (v & 3)) + ct;
+                        *o = (w == 0 ? 0.0f : *o) + mine * acc[ct][v];
+                    }
+            }
+            __syncthreads();
+        }
+    }
+    // rows of the merged tile: thread -> (query, four columns)
+    for (int idx = tid; idx < 32 * D / 4; idx += 256) {
+        const int qi = idx / (D / 4), c4 = idx % (D / 4);
+        if (32 * qt + qi >= a.B) continue;
+        const f32x4 num = *reinterpret_cast<const f32x4*>(Qs + qi * QS + 4 * c4);
+        if (a.splits > 1) {
+            float* rec = a.part + (static_cast<int64_t>(pq) * a.splits + sp) * prefix_part_floats(D);
+            *reinterpret_cast<f32x4*>(rec + qi * D + 4 * c4) = num;
+            if (c4 == 0) {
+                rec[32 * D + qi] = Mx[qi];
+                rec[32 * D + 32 + qi] = Dn[qi];
+            }
+            continue;
+        }
+        const float inv = 1.0f / Dn[qi];
+        T* orow = static_cast<T*>(a.out) + static_cast<int64_t>(r) * a.os.req + static_cast<int64_t>(h) * a.os.head +
+                  static_cast<int64_t>(32 * qt + qi) * a.os.tok + 4 * c4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st_elem(orow, e, num[e] * inv);
     }
 }
 
@@ -413,7 +534,7 @@ int prefix_query_tiles(int B) { return (B + 31) / 32; }
 
 int prefix_attention_splits(int R, int H, int d, int B, int io, int64_t total_tokens)
 {
-    if (io != BHA_BF16 || B > 64 || (d != 64 && d != 128) || R <= 0) return 1;
+    if (B > 64 || (d != 64 && d != 128) || R <= 0) return 1;
     const int64_t pairs = static_cast<int64_t>(R) * H * prefix_query_tiles(B);
     const int64_t avg_chunks = (total_tokens / R + B + 31) / 32;
     int64_t sp = (kSplitTargetWgs + pairs - 1) / pairs;
@@ -437,18 +558,31 @@ hipError_t launch_prefix_attention_mfma(const PrefixArgs& a, hipStream_t s)
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const dim3 mgrid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * a.B));
-        if (a.d == 128) hipLaunchKernelGGL(prefix_attn_merge_kernel<128>, mgrid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL(prefix_attn_merge_kernel<64>, mgrid, dim3(256), 0, s, a);
+        if (a.d == 128) hipLaunchKernelGGL((prefix_attn_merge_kernel<uint16_t, 128>), mgrid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((prefix_attn_merge_kernel<uint16_t, 64>), mgrid, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t prefix_f32_launch(const PrefixArgs& a, hipStream_t s)
+{
+    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * prefix_query_tiles(a.B) * a.splits));
+    hipLaunchKernelGGL((prefix_attn_f32_kernel<T, D>), grid, dim3(256), 0, s, a);
+    if (a.splits > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const dim3 mgrid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * a.B));
+        hipLaunchKernelGGL((prefix_attn_merge_kernel<T, D>), mgrid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_prefix_attention_generic(const PrefixArgs& a, hipStream_t s)
 {
-    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * a.B)), block(kGenThreads);
-    if (a.io == BHA_BF16) hipLaunchKernelGGL(prefix_attn_generic_kernel<uint16_t>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(prefix_attn_generic_kernel<float>, grid, block, 0, s, a);
-    return hipGetLastError();
+    if (a.splits < 1 || a.splits > kSplitMax || (a.splits > 1 && !a.part)) return hipErrorInvalidValue;
+    if (a.io == BHA_BF16) return a.d == 128 ? prefix_f32_launch<uint16_t, 128>(a, s) : prefix_f32_launch<uint16_t, 64>(a, s);
+    return a.d == 128 ? prefix_f32_launch<float, 128>(a, s) : prefix_f32_launch<float, 64>(a, s);
 }
 
 }  // namespace bha

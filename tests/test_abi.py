@@ -279,8 +279,8 @@ def test_prefix_attention_workspace_size(lib):
     assert ws(ctypes.byref(_dims(num_requests=256, num_heads=16)), 256 * 4096) == 0
     # short prefixes are not split (fewer than 16 chunks of 32 keys per split)
     assert ws(ctypes.byref(_dims(num_requests=1, num_heads=16)), 100) == 0
-    # the float32 path never splits
-    assert ws(ctypes.byref(_dims(num_requests=1, num_heads=16, io_dtype=0)), 32768) == 0
+    # the float32 path splits the same way into the same fp32 partial records
+    assert ws(ctypes.byref(_dims(num_requests=1, num_heads=16, io_dtype=0)), 32768) == n
     assert ws(ctypes.byref(_dims(num_requests=0)), 10) == 0
     assert ws(ctypes.byref(_dims(head_dim=96)), 10) == UNSUP
     assert ws(ctypes.byref(_dims()), -1) == DIMS

@@ -419,7 +419,7 @@ def test_forward_commit_equals_forward_then_commit(dev, io, b):
 
 
 PREFIX = [("bf16", 128, 32), ("bf16", 128, 17), ("bf16", 64, 32), ("bf16", 64, 5), ("bf16", 128, 40),
-          ("bf16", 64, 64), ("f32", 128, 32), ("f32", 64, 9)]
+          ("bf16", 64, 64), ("f32", 128, 32), ("f32", 64, 9), ("f32", 128, 40), ("f32", 64, 64)]
 
 
 @pytest.mark.parametrize("io,d,b", PREFIX)
@@ -486,22 +486,23 @@ def test_prefix_attention_offsets_are_clamped(dev):
         assert torch.equal(y[r], y_r[0]), r
 
 
-@pytest.mark.parametrize("d,b", [(128, 32), (64, 32), (128, 48)])
-def test_prefix_attention_split_matches_oracle(dev, d, b):
+@pytest.mark.parametrize("io,d,b", [("bf16", 128, 32), ("bf16", 64, 32), ("bf16", 128, 48), ("f32", 128, 32),
+                                    ("f32", 64, 48)])
+def test_prefix_attention_split_matches_oracle(dev, io, d, b):
     # few pairs with long prefixes: the keys of each pair are split over several
     # work-groups (the request with no prefix leaves some splits without keys);
     # the same call with a workspace too small to split, and with one that
     # allows half the splits, agree with the oracle too
-    case = synth.make_case("tiny", R=3, H=2, d=d, FW=64, B=b, io="bf16", blocks=(20000 // b + 1, 20000 // b + 1),
+    case = synth.make_case("tiny", R=3, H=2, d=d, FW=64, B=b, io=io, blocks=(20000 // b + 1, 20000 // b + 1),
                            gamma="uniform")
     lens = np.array([0, 20000, 40])
     offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     kp = np.concatenate([case.prefix_k[r][:lens[r]] for r in range(case.R)])
     vp = np.concatenate([case.prefix_v[r][:lens[r]] for r in range(case.R)])
     T = kp.shape[0]
-    q, k, v = (to_device(x, "bf16", dev) for x in (case.q, case.k, case.v))
-    kd, vd, od = to_device(kp, "bf16", dev), to_device(vp, "bf16", dev), torch.from_numpy(offs).to(dev)
-    full = bha.prefix_attention_workspace(case.R, case.H, d, b, T)
+    q, k, v = (to_device(x, io, dev) for x in (case.q, case.k, case.v))
+    kd, vd, od = to_device(kp, io, dev), to_device(vp, io, dev), torch.from_numpy(offs).to(dev)
+    full = bha.prefix_attention_workspace(case.R, case.H, d, b, T, dtype=q.dtype)
     part = case.R * case.H * ((b + 31) // 32) * (32 * d + 64) * 4
     assert full > 0 and full % part == 0
     n_split = full // part
@@ -519,9 +520,9 @@ def test_prefix_attention_split_matches_oracle(dev, d, b):
                 ref = oracle.prefix_attention(case.q[r, :, h], case.k[r, :, h], case.v[r, :, h],
                                               kp[offs[r]:offs[r + 1], h], vp[offs[r]:offs[r + 1], h])
                 worst = max(worst, normwise_err(y[r, :, h], ref, None))
-        _log(f"[prefix-attn split] d={d} workspace={name} ({n_split} splits in full) lens={lens.tolist()} "
-             f"err {worst:.2e}")
-        assert worst <= TOL["bf16"]
+        _log(f"[prefix-attn split] io={io} d={d} workspace={name} ({n_split} splits in full) "
+             f"lens={lens.tolist()} err {worst:.2e}")
+        assert worst <= TOL[io]
 
 
 @pytest.mark.parametrize("io", ["bf16", "f32"])
