@@ -206,13 +206,14 @@ __global__ __launch_bounds__(kThreads) void forward_generic_kernel(ForwardArgs a
                 acc = mfma32f(x[2], y[2], acc);
                 acc = mfma32f(x[3], y[3], acc);
             }
-            // S[f][c] for f = k0 .. k0 + 3 of this column are 16 contiguous bytes
+            // S[f][c] for f = k0 .. k0 + 3 of this column are 16 contiguous
+            // bytes; read once: non-temporal (158.7 -> 151.5 us at 256 x 16 pairs)
             const float* sp = rec + static_cast<int64_t>(ct) * (F / 4) * 128 + l32 * 4;
 #pragma unroll 4
             for (int g = 0; g < F / 8; ++g) {
                 const int k0 = 8 * g + 4 * hf;
                 const f32x4 x = *reinterpret_cast<const f32x4*>(Phs + l32 * FS + k0);
-                const f32x4 y = ld4(sp + (k0 >> 2) * 128);
+                const f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(sp + (k0 >> 2) * 128));
                 acc = mfma32f(x[0], y[0], acc);
                 acc = mfma32f(x[1], y[1], acc);
                 acc = mfma32f(x[2], y[2], acc);
