@@ -525,6 +525,79 @@ def test_prefix_attention_split_matches_oracle(dev, io, d, b):
         assert worst <= TOL[io]
 
 
+def test_large_token_strides_take_the_fp32_kernels(dev):
+    # bf16 tokens 2^25 elements (64 MiB) apart: past the 32-bit in-chunk
+    # offsets of the matrix-core kernels, so prefill, forward, commit and
+    # prefix attention run on the fp32-arithmetic kernels; each against the
+    # oracle
+    R, H, d, FW, B, TS = 2, 1, 64, 32, 3, 1 << 25
+    case = synth.make_case("tiny", R=R, H=H, d=d, FW=FW, B=B, io="bf16", blocks=(1, 1), gamma="uniform")
+    F = case.F
+    buf = torch.zeros(R * B * TS, dtype=torch.bfloat16, device=dev)
+    pbuf = torch.zeros(R * B * TS, dtype=torch.bfloat16, device=dev)
+
+    def tok_view(i, x):  # [R][B][H][d], the i-th H*d run at the start of each token's slot
+        t = buf.as_strided((R, B, H, d), (B * TS, TS, d, 1), i * H * d)
+        if x is not None:
+            t.copy_(to_device(x, "bf16", dev))
+        return t
+
+    q, k, v = (tok_view(i, x) for i, x in enumerate((case.q, case.k, case.v)))
+    out = tok_view(3, None)
+    kp_h = np.concatenate([case.prefix_k[r] for r in range(R)])
+    vp_h = np.concatenate([case.prefix_v[r] for r in range(R)])
+    T = kp_h.shape[0]
+    kp = pbuf.as_strided((T, H, d), (TS, d, 1), 0)
+    vp = pbuf.as_strided((T, H, d), (TS, d, 1), H * d)
+    kp.copy_(to_device(kp_h, "bf16", dev))
+    vp.copy_(to_device(vp_h, "bf16", dev))
+    offs_h = np.concatenate([[0], np.cumsum([case.prefix_k[r].shape[0] for r in range(R)])]).astype(np.int32)
+    offs = torch.from_numpy(offs_h).to(dev)
+    w = to_device(case.w, "bf16", dev)
+    gamma = torch.from_numpy(case.gamma).to(dev)
+    slots = torch.from_numpy(case.slot_ids).to(dev)
+    state = bha.new_state(case.num_slots, H, d, FW, dev)
+
+    def plain():
+        torch.cuda.synchronize()
+        return record_to_plain(state.cpu().numpy()[case.slot_ids], d, F)
+
+    def built(with_block):
+        S = np.zeros((R, H, F, d))
+        Z = np.zeros((R, H, F))
+        for r in range(R):
+            for h in range(H):
+                kk, vv = case.prefix_k[r][:, h], case.prefix_v[r][:, h]
+                if with_block:
+                    kk, vv = np.concatenate([kk, case.k[r, :, h]]), np.concatenate([vv, case.v[r, :, h]])
+                S[r, h], Z[r, h] = oracle.state_build(kk.astype(np.float64), vv.astype(np.float64), case.w[h])
+        return S, Z
+
+    errs = {}
+    bha.state_prefill(kp, vp, offs, w, state, slots)
+    S, Z = plain()
+    S_ref, Z_ref = built(False)
+    errs["prefill"] = max(normwise_err(S, S_ref, (2, 3)), normwise_err(Z, Z_ref, (2,)))
+    bha.block_forward(q, k, v, w, gamma, state, slots, out=out)
+    y = to_host(out)
+    ref = oracle.block_forward_batch(pairs(case.q), pairs(case.k), pairs(case.v), case.w, case.gamma, S, Z,
+                                     nthreads=NTHREADS)
+    errs["forward"] = normwise_err(pairs(y), ref, (2, 3))
+    bha.state_commit(k, v, w, state, slots)
+    S, Z = plain()
+    S_ref, Z_ref = built(True)
+    errs["commit"] = max(normwise_err(S, S_ref, (2, 3)), normwise_err(Z, Z_ref, (2,)))
+    bha.prefix_attention(q, k, v, kp, vp, offs, out=out)
+    y = to_host(out)
+    errs["prefix_attention"] = max(
+        normwise_err(y[r, :, h], oracle.prefix_attention(case.q[r, :, h], case.k[r, :, h], case.v[r, :, h],
+                                                         kp_h[offs_h[r]:offs_h[r + 1], h],
+                                                         vp_h[offs_h[r]:offs_h[r + 1], h]), None)
+        for r in range(R) for h in range(H))
+    _log(f"[large strides] {', '.join(f'{k_} err {e:.2e}' for k_, e in errs.items())}")
+    assert max(errs.values()) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("io", ["bf16", "f32"])
 def test_state_is_consistent_across_block_sizes(dev, io):
     # blocks of 32, 16, 8, 1, 64 and 5 tokens committed in turn into one state
