@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kCommitThreads) void commit_generic_kernel(CommitAr
     __shared__ __attribute__((aligned(16))) float xv[TC * VS];
     __shared__ __attribute__((aligned(16))) float xk[TC * KS];
     static_assert(LQ >= 1 && LQ * NT * 4 == TC * D, "whole pieces per thread");
-    static_assert(TC * FS >= kPrefillOrderMax + 1, "request counts fit the phi buffer");
+    static_assert(TC * FS >= kPrefillOrderLds, "the ordering scratch fits the phi buffer");
     const int r = prefill_request<NT>(a, pair / a.H, tid, reinterpret_cast<int*>(ph));
 
     const int slot = a.slot_ids[r];

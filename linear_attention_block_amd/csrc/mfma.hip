@@ -1346,7 +1346,7 @@ void prefill_mfma_kernel(CommitArgs a)
     const int n16 = lane & 15, q = lane >> 4;
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[P::LDS];
-    static_assert(P::LDS >= 4 * (kPrefillOrderMax + 1), "request counts fit the LDS");
+    static_assert(P::LDS >= 4 * kPrefillOrderLds, "the ordering scratch fits the LDS");
     const int r = prefill_request<NT>(a, pair / a.H, tid, reinterpret_cast<int*>(smem));
     uint16_t* const Vs = reinterpret_cast<uint16_t*>(smem);
     uint16_t* const Ps = Vs + P::NBUF * CT * D;

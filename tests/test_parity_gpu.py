@@ -295,18 +295,18 @@ def test_prefill_ragged_matches_oracle_build(dev, io, d, fw):
     assert worst <= TOL[io]
 
 
-@pytest.mark.parametrize("io,R", [("bf16", 1024), ("bf16", 1025), ("f32", 1024), ("f32", 1025)])
-def test_prefill_many_requests(dev, io, R):
-    # up to 1024 requests the work-groups take the requests longest first
-    # (ranked in the kernel), beyond that in request order; lengths 0..12
-    # give many ties and empty ranges. Each request's state against the
-    # oracle's build over its own tokens.
-    case = synth.make_case("tiny", R=R, H=1, d=64, FW=32, B=1, io=io, blocks=(0, 12), gamma="uniform")
+@pytest.mark.parametrize("io,R,H", [("bf16", 2048, 1), ("bf16", 2049, 1), ("f32", 585, 14), ("f32", 586, 14)])
+def test_prefill_many_requests(dev, io, R, H):
+    # up to 2048 requests and 8192 (request, head) pairs the work-groups take
+    # the requests longest first (selected in the kernel), beyond either in
+    # request order; lengths 0..12 give many ties and empty ranges. Each
+    # request's state against the oracle's build over its own tokens.
+    case = synth.make_case("tiny", R=R, H=H, d=64, FW=32, B=1, io=io, blocks=(0, 12), gamma="uniform")
     lens = case.n_blocks.copy()
     offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     kp = np.concatenate([case.prefix_k[r][:lens[r]] for r in range(R)])
     vp = np.concatenate([case.prefix_v[r][:lens[r]] for r in range(R)])
-    state = bha.new_state(case.num_slots, 1, case.d, case.FW, dev)
+    state = bha.new_state(case.num_slots, H, case.d, case.FW, dev)
     bha.state_prefill(to_device(kp, io, dev), to_device(vp, io, dev), torch.from_numpy(offs).to(dev),
                       to_device(case.w, io, dev), state, torch.from_numpy(case.slot_ids).to(dev))
     torch.cuda.synchronize()
@@ -317,10 +317,11 @@ def test_prefill_many_requests(dev, io, R):
         if n == 0:
             assert not S[r].any() and not Z[r].any()
             continue
-        S_ref, Z_ref = oracle.state_build(case.prefix_k[r][:n, 0].astype(np.float64),
-                                          case.prefix_v[r][:n, 0].astype(np.float64), case.w[0])
-        worst = max(worst, normwise_err(S[r, 0], S_ref, None), normwise_err(Z[r, 0], Z_ref, None))
-    _log(f"[prefill-many] io={io} R={R} empty={(lens == 0).sum()} err {worst:.2e}")
+        for h in range(H):
+            S_ref, Z_ref = oracle.state_build(case.prefix_k[r][:n, h].astype(np.float64),
+                                              case.prefix_v[r][:n, h].astype(np.float64), case.w[h])
+            worst = max(worst, normwise_err(S[r, h], S_ref, None), normwise_err(Z[r, h], Z_ref, None))
+    _log(f"[prefill-many] io={io} R={R} H={H} empty={(lens == 0).sum()} err {worst:.2e}")
     assert worst <= TOL[io]
 
 
