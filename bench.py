@@ -211,43 +211,35 @@ def gqa_cycle(args, log) -> dict:
         layers.append(dict(fwd=bha.prepare_forward_gqa(q, k, v, w, gamma, state, slots, out),
                            com=bha.prepare_commit(k, v, w, state, slots), keep=(q, k, v, w, gamma, state, out)))
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps * (nd + 1) * nl)]
+    # one event pair around each step's forwards and one around its commits
+    def ev_pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def step(it):
+    def step(evs=None):
+        if evs is not None:
+            evs[0][0].record()
         for _ in range(nd):
             for lay in layers:
-                if it is not None:
-                    e0, e1 = next(it)
-                    e0.record()
                 lay["fwd"]()
-                if it is not None:
-                    e1.record()
+        if evs is not None:
+            evs[0][1].record()
+            evs[1][0].record()
         for lay in layers:
-            if it is not None:
-                e0, e1 = next(it)
-                e0.record()
             lay["com"]()
-            if it is not None:
-                e1.record()
+        if evs is not None:
+            evs[1][1].record()
 
+    ev = [(ev_pair(), ev_pair()) for _ in range(args.steps)]
     for _ in range(args.warmup):
-        step(None)
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    it = iter(ev)
-    for _ in range(args.steps):
-        step(it)
+    for st in range(args.steps):
+        step(ev[st])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    per = (nd + 1) * nl
-    fwd_ms, com_ms = [], []
-    for st in range(args.steps):
-        blk = ev[st * per:(st + 1) * per]
-        fwd_ms += [a.elapsed_time(b) for a, b in blk[:nd * nl]]
-        com_ms += [a.elapsed_time(b) for a, b in blk[nd * nl:]]
-    fwd_avg = sum(fwd_ms) / len(fwd_ms) * 1e-3
-    com_avg = sum(com_ms) / len(com_ms) * 1e-3
+    fwd_avg = sum(f0.elapsed_time(f1) for (f0, f1), _ in ev) * 1e-3 / (args.steps * nd * nl)
+    com_avg = sum(c0.elapsed_time(c1) for _, (c0, c1) in ev) * 1e-3 / (args.steps * nl)
     fb = forward_gqa_bytes(R, H, HK, d, FW, B)
     cb = commit_bytes(R, HK, d, FW, B)
     value = args.steps * nd * nl * R * B / elapsed
@@ -521,57 +513,61 @@ def main() -> int:
     n_fwd, n_com = nd_plain * nl, nl
     if args.staggered:
         nd_plain, n_fwd, n_com = nd, nd * nl, 0
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps * (n_fwd + n_com))]
+    # Each step is timed by one event pair around its forwards and one around
+    # its commits (per-launch events would add their own cost to the step);
+    # a launch's average duration is its group's time over its launches, gaps
+    # between back-to-back launches included.
+    def ev_pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    def step(evs):
-        it = iter(evs) if evs is not None else None
+    def step(evs=None, per_launch=None):
+        def run(fn):
+            if per_launch is None:
+                fn()
+            else:
+                e0, e1 = ev_pair()
+                e0.record()
+                fn()
+                e1.record()
+                per_launch.append((e0, e1))
+
+        if evs is not None:
+            evs[0][0].record()
         if args.staggered:
             for i in range(nd):
                 for lay in layers:
-                    if it is not None:
-                        e0, e1 = next(it)
-                        e0.record()
-                        lay["stag"][i]()
-                        e1.record()
-                    else:
-                        lay["stag"][i]()
-            return
-        for _ in range(nd_plain):
+                    run(lay["stag"][i])
+        else:
+            for _ in range(nd_plain):
+                for lay in layers:
+                    run(lay["fwd"])
+        if evs is not None:
+            evs[0][1].record()
+            evs[1][0].record()
+        if not args.staggered:
             for lay in layers:
-                if it is not None:
-                    e0, e1 = next(it)
-                    e0.record()
-                    lay["fwd"]()
-                    e1.record()
-                else:
-                    lay["fwd"]()
-        for lay in layers:
-            if it is not None:
-                e0, e1 = next(it)
-                e0.record()
-                lay["com"]()
-                e1.record()
-            else:
-                lay["com"]()
+                run(lay["com"])
+        if evs is not None:
+            evs[1][1].record()
 
+    ev = [(ev_pair(), ev_pair()) for _ in range(args.steps)]
     for _ in range(args.warmup):
-        step(None)
+        step()
     torch.cuda.synchronize()
-    per = n_fwd + n_com
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(ev[s * per:(s + 1) * per])
+        step(ev[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    fwd_ms, com_ms = [], []
-    for s in range(args.steps):
-        blk = ev[s * per:(s + 1) * per]
-        fwd_ms += [a.elapsed_time(b) for a, b in blk[:n_fwd]]
-        com_ms += [a.elapsed_time(b) for a, b in blk[n_fwd:]]
-    fwd_avg = sum(fwd_ms) / len(fwd_ms) * 1e-3
-    com_avg = sum(com_ms) / len(com_ms) * 1e-3 if com_ms else None
+    fwd_avg = sum(f0.elapsed_time(f1) for (f0, f1), _ in ev) * 1e-3 / (args.steps * n_fwd)
+    com_avg = (sum(c0.elapsed_time(c1) for _, (c0, c1) in ev) * 1e-3 / (args.steps * n_com)) if n_com else None
+    # the spread of single launches: one more step with an event pair around
+    # every launch, outside the timed region
+    per_launch = []
+    step(per_launch=per_launch)
+    torch.cuda.synchronize()
+    fwd_ms = [a.elapsed_time(b) for a, b in per_launch[:n_fwd]]
     fb = forward_bytes(R, H, d, FW, B)
     if args.staggered:
         # every launch writes back the records of the 1/nd of requests it commits
@@ -634,18 +630,20 @@ def main() -> int:
     c1.record()
     torch.cuda.synchronize()
     copy_gbps = 2 * ctx_src.numel() * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    # and a plain streaming read of the same bytes (a sum reduction)
-    ctx_sum = torch.empty((), dtype=torch.float32, device=dev)
-    torch.sum(ctx_src, dim=0, out=ctx_sum)
+    # and a plain streaming read of the same bytes: sums of 4096-float rows
+    # (of torch's reductions the one that streams fastest here)
+    ctx_rows = ctx_src[: ctx_src.numel() // 4096 * 4096].view(-1, 4096)
+    ctx_sum = torch.empty(ctx_rows.shape[0], dtype=torch.float32, device=dev)
+    torch.sum(ctx_rows, dim=1, out=ctx_sum)
     c0.record()
     for _ in range(5):
-        torch.sum(ctx_src, dim=0, out=ctx_sum)
+        torch.sum(ctx_rows, dim=1, out=ctx_sum)
     c1.record()
     torch.cuda.synchronize()
-    read_gbps = ctx_src.numel() * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del ctx_src, ctx_dst, ctx_sum
+    read_gbps = ctx_rows.numel() * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del ctx_src, ctx_dst, ctx_sum, ctx_rows
     log(f"context: torch device copy of {fb / 1e6:.0f} MB runs at {copy_gbps:.0f} GB/s (read + write); "
-        f"a sum over the same bytes reads at {read_gbps:.0f} GB/s")
+        f"row sums over the same bytes read at {read_gbps:.0f} GB/s")
 
     achieved = fb / fwd_avg / 1e9
     result = {
@@ -684,10 +682,11 @@ def main() -> int:
                        f"bha_block_forward: forward_mfma_kernel<{d},{FW},1> (persistent, bf16 MFMA)"),
             "bytes_per_launch": fb,
             "avg_launch_us": fwd_avg * 1e6,
-            "launches": len(fwd_ms),
-            "launch_us_p10_median_p90": [float(x) * 1e3 for x in np.percentile(fwd_ms, [10, 50, 90])],
+            "launches": args.steps * n_fwd,
+            "timing": "one event pair around each step's forwards; average over its launches, gaps included",
+            "single_launch_us_p10_median_p90": [float(x) * 1e3 for x in np.percentile(fwd_ms, [10, 50, 90])],
         },
-        "context": {"torch_copy_GBps": copy_gbps, "torch_sum_read_GBps": read_gbps},
+        "context": {"torch_copy_GBps": copy_gbps, "torch_row_sum_read_GBps": read_gbps},
         "commit": None if args.staggered else {
             "kernel": ("bha_state_commit" if args.separate_commit
                        else "bha_block_forward_commit (last denoising step and commit, one pass)"),

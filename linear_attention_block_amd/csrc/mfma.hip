@@ -1515,6 +1515,8 @@ static hipError_t launch_forward(const ForwardArgs& a, hipStream_t s)
     if (a.B > 32) return hipErrorNotSupported;
     if (a.G == 2) return launch_forward_gqa<D, FW, 2>(a, s);
     if (a.G == 4) return launch_forward_gqa<D, FW, 4>(a, s);
+    if constexpr (FW <= 64)
+        if (a.G == 8) return launch_forward_gqa<D, FW, 8>(a, s);
     return hipErrorNotSupported;
 }
 
