@@ -96,8 +96,8 @@ extern "C" int bha_block_forward_gqa(const bha_dims* dims, int32_t num_kv_heads,
 }
 
 // A commit of B tokens per request: the commit kernel (bf16, B <= 32), the
-// prefill kernel over each request's B rows (bf16, B <= 64), else the plain
-// kernel.
+// prefill kernel over each request's B rows (bf16, B <= 64), else the
+// fp32-arithmetic commit kernel.
 static hipError_t launch_commit_any(const CommitArgs& a, hipStream_t stream)
 {
     hipError_t e = launch_commit_mfma(a, stream);

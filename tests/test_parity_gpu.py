@@ -141,7 +141,7 @@ def test_b16_bf16_end_to_end(dev):
 SWEEP = [
     # (io, d, FW, B): bf16 takes the matrix-core kernels (B <= 32: one query tile
     # and the commit kernel; 33..64: two query tiles and commits through the
-    # prefill kernel), fp32 the plain kernels
+    # prefill kernel), fp32 the fp32-arithmetic kernels
     ("bf16", 128, 64, 32), ("bf16", 128, 64, 1), ("bf16", 128, 64, 17), ("bf16", 128, 32, 32),
     ("bf16", 128, 128, 32), ("bf16", 64, 32, 8), ("bf16", 64, 64, 31), ("bf16", 64, 128, 32),
     ("bf16", 128, 64, 33), ("bf16", 64, 32, 64), ("bf16", 128, 64, 48), ("bf16", 128, 128, 64),
