@@ -526,6 +526,39 @@ def test_prefix_attention_split_matches_oracle(dev, io, d, b):
         assert worst <= TOL[io]
 
 
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_normaliser_halves_count_the_tokens(dev, io):
+    # each half of phi sums to 1 per token, so each half of Z sums to the
+    # number of tokens folded in: a ragged prefill (0..300 tokens), then a
+    # 32-token block commit, then a fused forward + commit of another block
+    R, H, d, FW, B = 7, 3, 128, 64, 32
+    case = synth.make_case("tiny", R=R, H=H, d=d, FW=FW, B=1, io=io, blocks=(0, 300), gamma="uniform")
+    lens = case.n_blocks.copy()
+    lens[:2] = [0, 1]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    kp = np.concatenate([case.prefix_k[r][:lens[r]] for r in range(R)])
+    vp = np.concatenate([case.prefix_v[r][:lens[r]] for r in range(R)])
+    w = to_device(case.w, io, dev)
+    slots = torch.from_numpy(case.slot_ids).to(dev)
+    state = bha.new_state(case.num_slots, H, d, FW, dev)
+    bha.state_prefill(to_device(kp, io, dev), to_device(vp, io, dev), torch.from_numpy(offs).to(dev), w, state,
+                      slots)
+    g = np.random.default_rng(3)
+    blk = [synth.bf16_to_f32(synth.bf16_bits(g.standard_normal((R, B, H, d)).astype(np.float32)))
+           for _ in range(5)]
+    q1, k1, v1, k2, v2 = (to_device(x, io, dev) for x in blk)
+    bha.state_commit(k1, v1, w, state, slots)
+    out = torch.empty_like(q1)
+    bha.block_forward_commit(q1, k2, v2, w, torch.from_numpy(case.gamma).to(dev), state, slots, out=out)
+    torch.cuda.synchronize()
+    _, Z = record_to_plain(state.cpu().numpy()[case.slot_ids], d, 2 * FW)
+    n_tok = (lens + 2 * B).astype(np.float64)[:, None]
+    err = max(np.abs(Z[..., :FW].sum(-1) - n_tok).max(), np.abs(Z[..., FW:].sum(-1) - n_tok).max())
+    rel = err / n_tok.max()
+    _log(f"[Z halves] io={io} max |sum Z half - tokens| {err:.2e} ({rel:.1e} of {int(n_tok.max())})")
+    assert rel <= 1e-5
+
+
 def test_large_token_strides_take_the_fp32_kernels(dev):
     # bf16 tokens 2^25 elements (64 MiB) apart: past the 32-bit in-chunk
     # offsets of the matrix-core kernels, so prefill, forward, commit and
