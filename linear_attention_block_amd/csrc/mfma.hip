@@ -624,14 +624,26 @@ struct alignas(16) GqaLds {
     __device__ float* sc() { return reinterpret_cast<float*>(u + PB_BYTES + PP_BYTES); }
 };
 
+// Operand loads one unit ahead (registers held across the unit), except for
+// four query heads at FW = 64: there the next unit's four heads of Q would
+// not fit beside two work-groups per CU, so each unit loads its own operands
+// at its start and the second work-group covers the wait. Measured at 256
+// requests x 16 query heads over 4 K/V heads: 41.8 us prefetching at one
+// work-group per CU, 34.8 us loading in place at two (in place at one: 46.9;
+// for two and eight heads in place is 2-5 % slower at unchanged occupancy).
+template <int D, int FW, int G>
+constexpr bool gqa_sync_operands()
+{
+    return D == 128 && G == 4 && FW == 64;
+}
+
 // Resident work-groups per CU: two, unless the F = 256 state slice (128
-// registers) leaves room for one, or four heads' next-pair Q prefetch would
-// spill at FW = 64 (measured: one work-group without spills, 42.3 us against
-// 48.9 us with them, at 256 requests x 16 query heads over 4 K/V heads).
+// registers), eight heads' operands, or four heads' prefetched operands at
+// FW = 64 leave room for one.
 template <int D, int FW, int G>
 constexpr int gqa_wpe()
 {
-    return FW >= 128 || (G >= 4 && FW >= 64) ? 1 : 2;
+    return FW >= 128 || G >= 8 || (G >= 4 && FW >= 64 && !gqa_sync_operands<D, FW, G>()) ? 1 : 2;
 }
 
 // Block logits s^T = K Q^T for the 32 staged queries at Qrows (masked beyond
@@ -698,21 +710,29 @@ __attribute__((amdgpu_waves_per_eu(gqa_wpe<D, FW, G>(), gqa_wpe<D, FW, G>()))) v
     const int count = (npairs - p + NG - 1) / NG;
     PairOperands<D, FW, 1, G> op;
     f32x4 sv[C::NSL];
-    op.load(a, p, slot_of(p), tid);
+    // the state record of unit u with slot id sl (slot 0's for an out-of-range slot)
+    auto rec_of = [&](int u, int sl) {
+        const bool ok = sl >= 0 && sl < a.num_slots;
+        return a.state + (static_cast<int64_t>(ok ? sl : 0) * HK + u % HK) * static_cast<int64_t>(D + 1) * F;
+    };
+    constexpr bool SYNC = gqa_sync_operands<D, FW, G>();
+    if constexpr (!SYNC) op.load(a, p, slot_of(p), tid);
     __builtin_amdgcn_sched_barrier(0);
-    load_state_slice(op.rec + wv * F * 32, lane, sv);
+    load_state_slice((SYNC ? rec_of(p, slot_of(p)) : op.rec) + wv * F * 32, lane, sv);
     __builtin_amdgcn_sched_barrier(0);
+    int slot_cur = slot_of(p);
     int slot_next = slot_of(p + NG);
     for (int k = 0; k < count; ++k) {
         const int live = k + 1 < count ? 1 : 0;
         const int pn = live ? p + NG : p;
-        const bool valid = op.valid;
         const int r = p / HK;
         int slot_after = slot_of(pn + NG);
         __syncthreads();  // every wave is done with the previous pair's LDS operands
+        if constexpr (SYNC) op.load(a, p, __builtin_amdgcn_readfirstlane(slot_cur), tid);
+        const bool valid = op.valid;
         op.store_to(Qs, Ks, sm.Vs, sm.Zs, tid);
         __syncthreads();
-        op.load(a, pn, __builtin_amdgcn_readfirstlane(slot_next), tid, live);
+        if constexpr (!SYNC) op.load(a, pn, __builtin_amdgcn_readfirstlane(slot_next), tid, live);
 
         // lane indices made opaque each trip: the LDS addresses derived from
         // them are computed in the loop, not kept in registers across it
@@ -764,7 +784,10 @@ __attribute__((amdgpu_waves_per_eu(gqa_wpe<D, FW, G>(), gqa_wpe<D, FW, G>()))) v
             const f32x16 lacc = linear_read<D, FW>(sv, pb, sp, sn);
             if (j == G - 1) {
                 __builtin_amdgcn_sched_barrier(0);
-                load_state_slice(op.rec + wv * F * 32, lane, sv, live);
+                const float* nrec;
+                if constexpr (SYNC) nrec = rec_of(pn, __builtin_amdgcn_readfirstlane(slot_next));
+                else nrec = op.rec;  // the next unit's, loaded one unit ahead
+                load_state_slice(nrec + wv * F * 32, lane, sv, live);
                 __builtin_amdgcn_sched_barrier(0);
             }
             f32x16 vacc = f32x16{};
@@ -774,6 +797,7 @@ __attribute__((amdgpu_waves_per_eu(gqa_wpe<D, FW, G>(), gqa_wpe<D, FW, G>()))) v
             __builtin_amdgcn_sched_barrier(0);  // one head's operands in registers at a time
         }
         asm volatile("" : "+v"(slot_after));
+        slot_cur = slot_next;
         slot_next = slot_after;
         p = pn;
     }
