@@ -52,10 +52,24 @@ struct Cfg {
 // tile's scores and operands do not fit two work-groups' registers at
 // FW >= 64 (measured: one work-group per CU, no spills, is as fast as two
 // with spills).
+// Two query tiles at FW = 64: the next pair's Q, K and V (64 rows each) held
+// in registers across the pair leave room for one work-group per CU; loading
+// each pair's operands at its start instead (only the state slice runs a
+// pair ahead) fits two, the second covering the first's wait. Measured at
+// 256 x 16 pairs, d = 128: 120.9 -> 113.9 us at B = 48, 125.6 -> 121.1 us at
+// B = 64.
+constexpr bool kFwdTwoTileSync = true;
+
+template <int D, int FW, int KT>
+constexpr bool fwd_sync_operands()
+{
+    return kFwdTwoTileSync && KT == 2 && FW == 64;
+}
+
 template <int D, int FW, int KT>
 constexpr int fwd_wpe()
 {
-    return KT > 1 && FW >= 64 ? 1 : Cfg<D, FW>::WPE;
+    return KT > 1 && FW >= 64 && !fwd_sync_operands<D, FW, KT>() ? 1 : Cfg<D, FW>::WPE;
 }
 
 // Issue the 128-bit loads of wave w's slice of the S tiles: load t gives lane
@@ -525,27 +539,36 @@ __attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, KT>(), fwd_wpe<D, FW, KT>())))
     // slot ids run one pair ahead of the operand loads (index clamped in range)
     auto slot_of = [&](int pp) { return a.slot_ids[(pp < npairs ? pp : npairs - 1) / a.H]; };
     const int count = (npairs - p + NG - 1) / NG;  // pairs of this work-group
+    // SYNC: each pair loads its own operands at its start (no registers held
+    // across the pair), and only the state slice runs a pair ahead
+    constexpr bool SYNC = fwd_sync_operands<D, FW, KT>();
+    auto rec_of = [&](int pp, int sl) {
+        const bool ok = sl >= 0 && sl < a.num_slots;
+        return a.state + (static_cast<int64_t>(ok ? sl : 0) * a.H + pp % a.H) * static_cast<int64_t>(D + 1) * F;
+    };
     PairOperands<D, FW, KT> op;
     f32x4 sv[C::NSL];
     // issue order as in the loop (operands, then the slice, then the next
     // slot id), so the waits at the loop head are the same from either side
-    op.load(a, p, slot_of(p), tid);
+    if constexpr (!SYNC) op.load(a, p, slot_of(p), tid);
     __builtin_amdgcn_sched_barrier(0);
-    load_state_slice(op.rec + wv * F * 32, lane, sv);
+    load_state_slice((SYNC ? rec_of(p, slot_of(p)) : op.rec) + wv * F * 32, lane, sv);
     __builtin_amdgcn_sched_barrier(0);
+    int slot_cur = slot_of(p);
     int slot_next = slot_of(p + NG);
     for (int k = 0; k < count; ++k) {
         // the last pair issues placeholder loads, so every trip runs the same
         // memory operations
         const int live = k + 1 < count ? 1 : 0;
         const int pn = live ? p + NG : p;
-        const bool valid = op.valid;
         const int r = p / a.H;
         int slot_after = slot_of(pn + NG);
         __syncthreads();  // every wave is done with the previous pair's LDS operands
+        if constexpr (SYNC) op.load(a, p, __builtin_amdgcn_readfirstlane(slot_cur), tid);
+        const bool valid = op.valid;
         op.store(sm, tid);
         __syncthreads();
-        op.load(a, pn, __builtin_amdgcn_readfirstlane(slot_next), tid, live);
+        if constexpr (!SYNC) op.load(a, pn, __builtin_amdgcn_readfirstlane(slot_next), tid, live);
         // query tile qt: the block's rows 32 qt ..; all but the last tile, then
         // the last, after whose linear read the state slice registers are free
         // for the next pair's slice
@@ -574,7 +597,12 @@ __attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, KT>(), fwd_wpe<D, FW, KT>())))
             lacc = linear_read<D, FW>(sv, pb, sp, sn);
         }
         __builtin_amdgcn_sched_barrier(0);
-        load_state_slice(op.rec + wv * F * 32, lane, sv, live);
+        {
+            const float* nrec;
+            if constexpr (SYNC) nrec = rec_of(pn, __builtin_amdgcn_readfirstlane(slot_next));
+            else nrec = op.rec;  // the next pair's, loaded one pair ahead
+            load_state_slice(nrec + wv * F * 32, lane, sv, live);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kFwdStagedOut && KT == 1) {
             merge_to_lds<D>(a, vacc, lacc, gamma, m, l, den, sn, wv, ln, g, valid, sm.Os);
@@ -587,6 +615,7 @@ __attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, KT>(), fwd_wpe<D, FW, KT>())))
         // vector register: its wait lands here, a whole trip after the load,
         // and covers no load issued since
         asm volatile("" : "+v"(slot_after));
+        slot_cur = slot_next;
         slot_next = slot_after;
         p = pn;
     }
