@@ -388,8 +388,7 @@ def shape_sweep(log) -> dict:
                    "forward_us": tf, "forward_GBps": fb / tf / 1e3, "forward_tokens_per_s": R * B / tf * 1e6,
                    "commit_us": tc, "commit_GBps": cb / tc / 1e3,
                    "path": ("mfma, one query tile; commit kernel" if B <= 32 else
-                            "mfma, two query tiles; commit through the prefill kernel" if FW <= 64 else
-                            "mfma, two query tiles; two-tile commit kernel")}
+                            "mfma, two query tiles; commit through the prefill kernel")}
             log(f"shape B={B} FW={FW}: forward {tf:.1f} us ({row['forward_GBps']:.0f} GB/s, "
                 f"{row['forward_tokens_per_s'] / 1e6:.1f} M tok/s), commit {tc:.1f} us ({row['commit_GBps']:.0f} GB/s) "
                 f"[{row['path']}]")
