@@ -411,6 +411,9 @@ def main() -> int:
     ap.add_argument("--denoise", type=int, default=32, help="denoising forwards per block")
     ap.add_argument("--cpu-sample-requests", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--io", choices=("bf16", "f32"), default="bf16",
+                    help="token dtype of the block cycle (default bf16; f32: the same draws widened, the "
+                         "fp32-arithmetic kernels)")
     ap.add_argument("--separate-commit", action="store_true",
                     help="run every denoising step as a plain forward and commit with bha_state_commit "
                          "(default: the last step of the block is bha_block_forward_commit)")
@@ -462,7 +465,9 @@ def main() -> int:
     if args.kv_heads:
         print(json.dumps(gqa_cycle(args, log)), flush=True)
         return 0
-    case = synth.make_case(args.config, with_prefix=False, with_qkv=False)
+    io = dict(io=args.io)  # every draw in the chosen token dtype (bf16 values, widened for f32)
+    es = 2 if args.io == "bf16" else 4
+    case = synth.make_case(args.config, with_prefix=False, with_qkv=False, **io)
     R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B
     nl, nd = args.layers, args.denoise
     slots = torch.from_numpy(case.slot_ids).to(dev)
@@ -474,9 +479,9 @@ def main() -> int:
     t_setup = time.perf_counter()
     layers, prefill_ms = [], []
     for L in range(nl):
-        w, gamma = synth.device_layer_params(args.config, L, dev)
+        w, gamma = synth.device_layer_params(args.config, L, dev, **io)
         state = bha.new_state(case.num_slots, H, d, FW, dev)
-        pk, pv, offs = synth.device_packed_prefix(args.config, case.n_blocks, dev, layer=L)
+        pk, pv, offs = synth.device_packed_prefix(args.config, case.n_blocks, dev, layer=L, **io)
         if L == 0:
             bha.state_prefill(pk, pv, offs, w, bha.new_state(case.num_slots, H, d, FW, dev), slots)
         p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -488,7 +493,7 @@ def main() -> int:
         if L == 0:
             prefix0 = (pk, pv, offs)  # for the softmax prefix-attention comparison
         del pk, pv
-        q, k, v = synth.device_step_qkv(args.config, 0, R, dev, layer=L)
+        q, k, v = synth.device_step_qkv(args.config, 0, R, dev, layer=L, **io)
         out = torch.empty_like(q)
         masks = [torch.from_numpy((np.arange(R) % nd == i).astype(np.uint8)).to(dev) for i in range(nd)]
         layers.append(dict(w=w, gamma=gamma, state=state, q=q, k=k, v=v, out=out,
@@ -500,7 +505,7 @@ def main() -> int:
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     pre_avg = sum(prefill_ms) / len(prefill_ms) * 1e-3
-    pb = prefill_bytes(T, R, H, d, FW)
+    pb = prefill_bytes(T, R, H, d, FW, es)
     log(f"setup: {nl} layers x {R} requests, prefixes {int(case.n_blocks.min()) * B}.."
         f"{max_blocks * B} tokens ({T} total), {time.perf_counter() - t_setup:.1f} s")
     log(f"prefill: avg {pre_avg * 1e6:.1f} us/launch over {nl} layers, {T / pre_avg / 1e6:.1f} M tokens/s, "
@@ -567,12 +572,12 @@ def main() -> int:
     step(per_launch=per_launch)
     torch.cuda.synchronize()
     fwd_ms = [a.elapsed_time(b) for a, b in per_launch[:n_fwd]]
-    fb = forward_bytes(R, H, d, FW, B)
+    fb = forward_bytes(R, H, d, FW, B, es)
     if args.staggered:
         # every launch writes back the records of the 1/nd of requests it commits
         F_ = 2 * FW
         fb += sum(1 for r in range(R) if r % nd == 0) * H * (d * F_ * 4 + F_ * 4)
-    cb = commit_bytes(R, H, d, FW, B) if args.separate_commit else forward_commit_bytes(R, H, d, FW, B)
+    cb = commit_bytes(R, H, d, FW, B, es) if args.separate_commit else forward_commit_bytes(R, H, d, FW, B, es)
     com_name = "commit" if args.separate_commit else "forward+commit"
     tokens = args.steps * nd * nl * R * B
     value = tokens / elapsed
@@ -602,7 +607,7 @@ def main() -> int:
         e1.record()
     torch.cuda.synchronize()
     sm_avg = sum(a.elapsed_time(b) for a, b in sm_ev) / len(sm_ev) * 1e-3
-    smb = prefix_attention_bytes(T, R, H, d, B)
+    smb = prefix_attention_bytes(T, R, H, d, B, es)
     del sm, sm_out, pk, pv, offs, prefix0
     torch.cuda.empty_cache()
     log(f"softmax prefix attention (same batch, whole prefixes): avg {sm_avg * 1e6:.1f} us/launch, "
@@ -656,7 +661,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.io,
         "data": "synthetic",
         "config": {
             "workload": (f"{args.config}: continuous-batching decode, {R} requests x {H} heads, d={d}, "
@@ -667,7 +672,7 @@ def main() -> int:
                             "with staggered blocks (1/32 of requests per step)" if args.staggered else
                             "within the last forward")),
             "requests": R, "heads": H, "head_dim": d, "feat_half": FW, "block": B,
-            "denoise_steps": nd, "layers": nl, "state_dtype": "f32", "io_dtype": "bf16",
+            "denoise_steps": nd, "layers": nl, "state_dtype": "f32", "io_dtype": args.io,
         },
         "roofline": {
             "bound": "hbm",
@@ -675,10 +680,15 @@ def main() -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
-            "traffic": None if args.staggered else read_traffic(args.config),
-            "kernel": (f"bha_block_forward_commit: forward_commit_mfma_kernel<{d},{FW}> (1/{nd} of requests "
-                       f"commit per launch)" if args.staggered else
-                       f"bha_block_forward: forward_mfma_kernel<{d},{FW},1> (persistent, bf16 MFMA)"),
+            "traffic": None if args.staggered or args.io != "bf16" else read_traffic(args.config),
+            "kernel": ((f"bha_block_forward_commit: forward_commit_mfma_kernel<{d},{FW}> (1/{nd} of requests "
+                        f"commit per launch)" if args.io == "bf16" else
+                        f"bha_block_forward_commit: forward_generic_kernel<float,{d},{FW}> then "
+                        f"commit_generic_kernel<float,{d},{FW}> (1/{nd} of requests commit per launch)")
+                       if args.staggered else
+                       f"bha_block_forward: forward_mfma_kernel<{d},{FW},1> (persistent, bf16 MFMA)"
+                       if args.io == "bf16" else
+                       f"bha_block_forward: forward_generic_kernel<float,{d},{FW}> (fp32 MFMA)"),
             "bytes_per_launch": fb,
             "avg_launch_us": fwd_avg * 1e6,
             "launches": args.steps * n_fwd,
@@ -688,7 +698,8 @@ def main() -> int:
         "context": {"torch_copy_GBps": copy_gbps, "torch_row_sum_read_GBps": read_gbps},
         "commit": None if args.staggered else {
             "kernel": ("bha_state_commit" if args.separate_commit
-                       else "bha_block_forward_commit (last denoising step and commit, one pass)"),
+                       else "bha_block_forward_commit (last denoising step and commit, one pass)" if args.io == "bf16"
+                       else "bha_block_forward_commit (fp32: the forward, then the commit kernel)"),
             "avg_launch_us": com_avg * 1e6,
             "bytes_per_launch": cb,
             "achieved_GBps": cb / com_avg / 1e9,
