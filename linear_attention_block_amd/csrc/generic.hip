@@ -267,9 +267,11 @@ struct Raw4<uint16_t> {
 // whole 1 KB wave accesses; the write-back is non-temporal). Per chunk: its K
 // and V rows, loaded into registers during the previous chunk, go to LDS and
 // the next chunk's loads are issued; the feature logits U = K W^T on 16x16
-// fp32 tiles (W rows from memory, k taken in runs of four per lane); phi(k)
-// per token, 16 threads per token (accurate expf); the Z sums; then
-// dS = phi(K)^T V on 32x32 fp32 tiles over the chunk's tokens. Rows past the
+// fp32 tiles (W rows from memory, k taken in runs of four per lane, two
+// accumulators so consecutive steps do not wait on each other); phi(k) per
+// token, 16 threads per token (accurate expf); the Z sums; then
+// dS = phi(K)^T V on 32x32 fp32 tiles over the chunk's tokens, the wave's
+// tiles interleaved step by step. Rows past the
 // range hold copies of the last K row, zero phi and zero V.
 // ---------------------------------------------------------------------------
 constexpr int kCommitThreads = 512;
@@ -362,18 +364,23 @@ __global__ __launch_bounds__(kCommitThreads) void commit_generic_kernel(CommitAr
             const int mt = ut % (TC / 16), jt = ut / (TC / 16);
             const float* krow = xk + (16 * mt + l16) * KS;
             const T* wrow = W + static_cast<int64_t>(16 * jt + l16) * D;
-            f32x4 c = {};
+            f32x4 c0 = {}, c1 = {};
 #pragma unroll 4
-            for (int g = 0; g < D / 16; ++g) {
+            for (int g = 0; g < D / 16; g += 2) {
                 const int k0 = 16 * g + 4 * q;
                 const f32x4 x = *reinterpret_cast<const f32x4*>(krow + k0), y = ld4(wrow + k0);
-                c = mfma16f(x[0], y[0], c);
-                c = mfma16f(x[1], y[1], c);
-                c = mfma16f(x[2], y[2], c);
-                c = mfma16f(x[3], y[3], c);
+                const f32x4 x1 = *reinterpret_cast<const f32x4*>(krow + k0 + 16), y1 = ld4(wrow + k0 + 16);
+                c0 = mfma16f(x[0], y[0], c0);
+                c1 = mfma16f(x1[0], y1[0], c1);
+                c0 = mfma16f(x[1], y[1], c0);
+                c1 = mfma16f(x1[1], y1[1], c1);
+                c0 = mfma16f(x[2], y[2], c0);
+                c1 = mfma16f(x1[2], y1[2], c1);
+                c0 = mfma16f(x[3], y[3], c0);
+                c1 = mfma16f(x1[3], y1[3], c1);
             }
 #pragma unroll
-            for (int v = 0; v < 4; ++v) u[(16 * mt + 4 * q + v) * US + 16 * jt + l16] = c[v];
+            for (int v = 0; v < 4; ++v) u[(16 * mt + 4 * q + v) * US + 16 * jt + l16] = c0[v] + c1[v];
         }
         __syncthreads();
         {
@@ -414,22 +421,19 @@ __global__ __launch_bounds__(kCommitThreads) void commit_generic_kernel(CommitAr
         if (tid < F)
             for (int t = 0; t < nt; ++t) zacc += ph[t * FS + tid];
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int ti = wave + NW * i;
-            if (ti < NTILE) {
-                const int ft = ti / (D / 32), ct = ti % (D / 32);
-                const float* pa = ph + 32 * ft + l32;
-                const float* va = xv + 32 * ct + l32;
+        for (int g = 0; g < TC / 8; ++g)
 #pragma unroll
-                for (int g = 0; g < TC / 8; ++g) {
+            for (int z = 0; z < 4; ++z) {
+                const int t = 8 * g + 4 * hf + z;
 #pragma unroll
-                    for (int z = 0; z < 4; ++z) {
-                        const int t = 8 * g + 4 * hf + z;
-                        acc[i] = mfma32f(pa[t * FS], va[t * VS], acc[i]);
+                for (int i = 0; i < TPW; ++i) {
+                    const int ti = wave + NW * i;
+                    if (ti < NTILE) {
+                        const int ft = ti / (D / 32), ct = ti % (D / 32);
+                        acc[i] = mfma32f(ph[t * FS + 32 * ft + l32], xv[t * VS + 32 * ct + l32], acc[i]);
                     }
                 }
             }
-        }
     }
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
