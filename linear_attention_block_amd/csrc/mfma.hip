@@ -226,11 +226,11 @@ struct alignas(16) FwdLds {
 
 // The per-pair operands a thread stages through LDS, held in registers from
 // their global loads to the LDS writes.
-template <int D, int FW, int KT = 1, int G = 1>
+template <int D, int FW, int KT = 1, int G = 1, int NT = Cfg<D, FW>::NT>
 struct PairOperands {
     using C = Cfg<D, FW>;
-    RowChunks<D, C::NT, 32 * KT * G> q;
-    RowChunks<D, C::NT, 32 * KT> k, v;
+    RowChunks<D, NT, 32 * KT * G> q;
+    RowChunks<D, NT, 32 * KT> k, v;
     f32x4 z;
     const float* rec;  // the state record the slice loads read (slot 0's for an out-of-range slot)
     bool valid;        // the slot id is in range
@@ -344,6 +344,68 @@ __device__ __forceinline__ f32x16 linear_read(const f32x4 (&sv)[Cfg<D, FW>::NSL]
 #pragma unroll
             for (int v = 0; v < 16; ++v) lacc[v] *= rs;
         }
+        bf16x8 as;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            as[e] = static_cast<__bf16>(sv[2 * kb][e]);
+            as[4 + e] = static_cast<__bf16>(sv[2 * kb + 1][e]);
+        }
+        lacc = mfma32(as, pb[kb], lacc);
+    }
+    return lacc;
+}
+
+// One half of phi(q) for token ln: h = 0 the exponentials of u - max u,
+// h = 1 those of min u - u; the bf16 B operands of that half's linear read,
+// its normaliser s and its share dz = e . Z_h (the same sums phi_operands_at
+// takes over both halves).
+template <int D, int FW>
+__device__ __forceinline__ void phi_half_operands(const uint16_t* Ws, const uint16_t* Qrows, const float* Zs, int ln,
+                                                  int g, int h, bf16x8 (&pb)[FW / 16], float& s, float& dz)
+{
+    using C = Cfg<D, FW>;
+    f32x16 u[FW / 32];
+    feature_logits<D, FW, C::RS>(Ws, Qrows, ln, g, u);
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float sc = h ? -kLog2e : kLog2e;  // base-2 logits of this half's softmax argument
+    float mx = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < FW / 32; ++T)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            u[T][v] *= sc;
+            mx = fmaxf(mx, u[T][v]);
+        }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    s = 0.0f;
+    dz = 0.0f;
+#pragma unroll
+    for (int T = 0; T < FW / 32; ++T)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 z = *reinterpret_cast<const f32x4*>(Zs + h * FW + 32 * T + 8 * q4 + 4 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int v = 4 * q4 + e;
+                const float ex = __builtin_amdgcn_exp2f(u[T][v] - mx);
+                s += ex;
+                dz = fmaf(ex, z[e], dz);
+                pb[2 * T + (v >> 3)][v & 7] = static_cast<__bf16>(ex);
+            }
+        }
+    s += __shfl_xor(s, 32, 64);
+    dz += __shfl_xor(dz, 32, 64);
+}
+
+// The linear read over one feature half, accumulated onto lacc: sv holds
+// that half of the wave's state slice (features 8t + 4g .. + 3 of load t), pb
+// its phi operands.
+template <int FW>
+__device__ __forceinline__ f32x16 linear_read_half(const f32x4 (&sv)[FW / 8], const bf16x8 (&pb)[FW / 16],
+                                                   f32x16 lacc)
+{
+#pragma unroll
+    for (int kb = 0; kb < FW / 16; ++kb) {
         bf16x8 as;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -616,6 +678,106 @@ __attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, KT>(), fwd_wpe<D, FW, KT>())))
         // and covers no load issued since
         asm volatile("" : "+v"(slot_after));
         slot_cur = slot_next;
+        slot_next = slot_after;
+        p = pn;
+    }
+}
+
+// F = 256 with the state slice split by feature half: wave w takes value
+// columns 32 (w % NW) and features [FW (w / NW), FW (w / NW) + FW), a
+// 64-register slice as at F = 128, so two waves share each SIMD (the whole
+// slice, 128 registers, allows one). Both waves of a column slice compute the
+// feature logits and their own half's exponentials, normaliser and Z share.
+// The + half wave reads its half of the state, runs the block softmax and
+// P V, and posts them through LDS; the - half wave scales that accumulator by
+// sn / sp and continues it over its own half -- the one-wave kernel's order of
+// operations, so the output is the same bit for bit -- then merges and stores.
+// Measured at 1,024 x 16 pairs, d = 128, B = 32: 532.4 -> 502.4 us per
+// forward (adding the two halves' partial sums instead of continuing one
+// accumulator: 490.6 us, but no longer the one-wave kernel's result).
+constexpr bool kFwdSplitHalves = true;
+
+template <int D>
+__global__ __launch_bounds__(2 * 64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(2, 2))) void forward_split_kernel(
+    ForwardArgs a, int npairs)
+{
+    constexpr int FW = 128;
+    using C = Cfg<D, FW>;
+    constexpr int F = C::F, NW = C::NW, NT = 2 * C::NT, HS = FW / 8;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int ln = lane & 31, g = lane >> 5;
+    const int cs = wv % NW, hh = wv / NW;  // column slice, feature half
+    const int NG = gridDim.x;
+    int p = blockIdx.x;
+    if (p >= npairs) return;
+    const int h = p % a.H;
+    const float gamma = a.gamma[h];
+
+    __shared__ FwdLds<D, FW> sm;
+    __shared__ float Xl[NW * 16 * 64];  // the + half's linear read, lane order
+    __shared__ float Xv[NW * 16 * 64];  // its P V
+    __shared__ __attribute__((aligned(16))) float Xs[NW * 32 * 4];  // per query: m, l, sp, dp
+    {
+        WChunks<D, FW, NT> wc;
+        wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
+        wc.template store_rows<C::RS>(sm.Ws, tid);
+    }
+
+    auto slot_of = [&](int pp) { return a.slot_ids[(pp < npairs ? pp : npairs - 1) / a.H]; };
+    const int count = (npairs - p + NG - 1) / NG;
+    PairOperands<D, FW, 1, 1, NT> op;
+    f32x4 sv[HS];
+    const int soff = cs * F * 32 + hh * HS * 256;  // this wave's half slice (floats)
+    op.load(a, p, slot_of(p), tid);
+    __builtin_amdgcn_sched_barrier(0);
+    load_state_slice(op.rec + soff, lane, sv);
+    __builtin_amdgcn_sched_barrier(0);
+    int slot_next = slot_of(p + NG);
+    for (int k = 0; k < count; ++k) {
+        const int live = k + 1 < count ? 1 : 0;
+        const int pn = live ? p + NG : p;
+        const bool valid = op.valid;
+        const int r = p / a.H;
+        int slot_after = slot_of(pn + NG);
+        __syncthreads();  // every wave is done with the previous pair's LDS operands
+        op.store(sm, tid);
+        __syncthreads();
+        op.load(a, pn, __builtin_amdgcn_readfirstlane(slot_next), tid, live);
+        bf16x8 pb[FW / 16];
+        float s, dz;
+        phi_half_operands<D, FW>(sm.Ws, sm.Qs, sm.Zs, ln, g, hh, pb, s, dz);
+        if (hh == 0) {
+            const f32x16 lacc = linear_read_half<FW>(sv, pb, f32x16{});
+            __builtin_amdgcn_sched_barrier(0);
+            load_state_slice(op.rec + soff, lane, sv, live);
+            __builtin_amdgcn_sched_barrier(0);
+            float m, l;
+            const f32x16 vacc = block_softmax_pv<D, FW, 1, 1>(a, sm, 0, cs, ln, g, m, l);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                Xl[(cs * 16 + v) * 64 + lane] = lacc[v];
+                Xv[(cs * 16 + v) * 64 + lane] = vacc[v];
+            }
+            if (g == 0) *reinterpret_cast<f32x4*>(Xs + (cs * 32 + ln) * 4) = f32x4{m, l, s, dz};
+        }
+        __syncthreads();
+        if (hh == 1) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(Xs + (cs * 32 + ln) * 4);
+            const float m = x[0], l = x[1], sp = x[2], dp = x[3];
+            const float rs = s / sp;  // s: sn of this half
+            f32x16 lacc, vacc;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                lacc[v] = Xl[(cs * 16 + v) * 64 + lane] * rs;
+                vacc[v] = Xv[(cs * 16 + v) * 64 + lane];
+            }
+            lacc = linear_read_half<FW>(sv, pb, lacc);
+            __builtin_amdgcn_sched_barrier(0);
+            load_state_slice(op.rec + soff, lane, sv, live);
+            __builtin_amdgcn_sched_barrier(0);
+            merge_store(a, vacc, lacc, gamma, m, l, dp / sp + dz / s, s, r, h, cs, ln, g, valid);
+        }
+        asm volatile("" : "+v"(slot_after));
         slot_next = slot_after;
         p = pn;
     }
@@ -1467,6 +1629,20 @@ static hipError_t launch_forward_kt(const ForwardArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
+// The split-slice F = 256 forward: one work-group of 2 NW waves per CU.
+template <int D>
+static hipError_t launch_forward_split(const ForwardArgs& a, hipStream_t s)
+{
+    const int npairs = a.R * a.H;
+    int64_t NG = static_cast<int64_t>(compute_units());
+    NG = (NG / a.H) * a.H;
+    if (NG < a.H) NG = a.H;
+    if (NG > npairs) NG = npairs;
+    hipLaunchKernelGGL((forward_split_kernel<D>), dim3(static_cast<uint32_t>(NG)), dim3(2 * 64 * (D / 32)), 0, s, a,
+                       npairs);
+    return hipGetLastError();
+}
+
 template <int D, int FW, int G>
 static hipError_t launch_forward_gqa(const ForwardArgs& a, hipStream_t s)
 {
@@ -1485,7 +1661,11 @@ static hipError_t launch_forward_gqa(const ForwardArgs& a, hipStream_t s)
 template <int D, int FW>
 static hipError_t launch_forward(const ForwardArgs& a, hipStream_t s)
 {
-    if (a.G == 1) return a.B <= 32 ? launch_forward_kt<D, FW, 1>(a, s) : launch_forward_kt<D, FW, 2>(a, s);
+    if (a.G == 1) {
+        if constexpr (kFwdSplitHalves && D == 128 && FW == 128)
+            if (a.B <= 32) return launch_forward_split<D>(a, s);
+        return a.B <= 32 ? launch_forward_kt<D, FW, 1>(a, s) : launch_forward_kt<D, FW, 2>(a, s);
+    }
     if (a.B > 32) return hipErrorNotSupported;
     if (a.G == 2) return launch_forward_gqa<D, FW, 2>(a, s);
     if (a.G == 4) return launch_forward_gqa<D, FW, 4>(a, s);
