@@ -1262,16 +1262,6 @@ struct PCfg {
     static constexpr int LDS = MAIN > ZRED ? MAIN : ZRED;
 };
 
-// W in LDS as the logits' A fragments in read order: block ks FW/16 + T
-// (1 KiB) holds, at 16-byte slot lane = n16 + 16 q, the elements
-// q d/4 + 8 ks .. + 7 of row 16 T + n16, so each fragment read is one
-// contiguous, conflict-free 1 KiB.
-template <int D, int FW>
-__device__ __forceinline__ bf16x8 w_frag(const uint16_t* Ws, int T, int ks, int lane)
-{
-    return lds_frag(Ws + ((ks * (FW / 16) + T) * 64 + lane) * 8);
-}
-
 // All-reductions over the lane pairs (L, L ^ 16) and (L, L ^ 32) with the
 // gfx950 row-swap instructions (VALU, no LDS round trip): swapping a value
 // with itself leaves each lane holding its own and its partner's.
@@ -1391,10 +1381,19 @@ __device__ __forceinline__ void prefill_phi(const PrefillPair<D, FW>& pp, int c,
     f32x4 u[FW / 16];
 #pragma unroll
     for (int T = 0; T < FW / 16; ++T) u[T] = f32x4{};
+    // W sits in LDS as the logits' A fragments in read order: block
+    // ks FW/16 + T (1 KiB) holds, at 16-byte slot lane = n16 + 16 q, the
+    // elements q d/4 + 8 ks .. + 7 of row 16 T + n16, so each fragment read is
+    // one contiguous, conflict-free 1 KiB. The lane's slot is one address and
+    // the blocks are immediate offsets (an opaque lane offset keeps the sum an
+    // add that the read can fold)
+    int wo = 8 * lane;
+    asm volatile("" : "+v"(wo));
+    const uint16_t* const Wl = Ws + wo;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int T = 0; T < FW / 16; ++T) u[T] = mfma16(w_frag<D, FW>(Ws, T, ks, lane), kf[ks], u[T]);
+        for (int T = 0; T < FW / 16; ++T) u[T] = mfma16(lds_frag(Wl + (ks * (FW / 16) + T) * 512), kf[ks], u[T]);
     if (c + PD < pp.nchunks) prefill_load_k(pp, c + PD, wv, n16, q, kf);
     // per-token extremes and sums over the four k-group lanes (L, L ^ 16,
     // L ^ 32, L ^ 48); the exponentials are base 2 of the scaled differences
@@ -1449,6 +1448,26 @@ __device__ __forceinline__ void prefill_phi(const PrefillPair<D, FW>& pp, int c,
     }
 }
 
+// Element offset, in a piece-swizzled tile of RB pieces per row, of the
+// transposed read that vt_frag_ps issues at step 0 for lane lane: row
+// 4 g + m / 4 (+ 8 for the upper half), piece c0 / 4 + 4 (q & 1) + m % 4.
+template <int RB>
+__device__ __forceinline__ int vt_offset_ps(int c0, int row_add, int lane)
+{
+    const int m = lane & 15, q = lane >> 4, g = lane >> 5;
+    const int piece = (c0 >> 2) + 4 * (q & 1) + (m & 3);
+    const int row = 4 * g + (m >> 2) + row_add;
+    return row * (4 * RB) + ((piece ^ lds_piece_swizzle<RB>(row)) << 2);
+}
+
+__device__ __forceinline__ bf16x8 vt_frag_at(const uint16_t* Xs, int lo_off, int hi_off)
+{
+    const i16x4 lo = lds_read_tr(Xs + lo_off);
+    const i16x4 hi = lds_read_tr(Xs + hi_off);
+    const i16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 // Second half of chunk c: dS = phi(K)^T V over the chunk, this wave's state
 // rows and value columns, accumulated into its state tiles.
 template <int D, int FW>
@@ -1461,11 +1480,49 @@ __device__ __forceinline__ void prefill_ds(int c, int tid, const uint16_t* Vs, c
     const int cs = wv % NC, r0 = (wv / NC) * RW;
     const uint16_t* const Vb = Vs + (P::NBUF == 2 ? (c & 1) : 0) * (CT * D);
     const uint16_t* const Pb = Ps + (P::NBUF == 2 ? (c & 1) : 0) * (CT * F);
+    if constexpr (P::NBUF == 2) {
 #pragma unroll
-    for (int kb = 0; kb < CT / 16; ++kb) {
-        const bf16x8 bv = vt_frag_ps<D / 4>(Vb, 32 * cs, kb, lane);
+        for (int kb = 0; kb < CT / 16; ++kb) {
+            const bf16x8 bv = vt_frag_ps<D / 4>(Vb, 32 * cs, kb, lane);
 #pragma unroll
-        for (int ft = 0; ft < RW / 32; ++ft) st[ft] = mfma32(vt_frag_ps<F / 4>(Pb, r0 + 32 * ft, kb, lane), bv, st[ft]);
+            for (int ft = 0; ft < RW / 32; ++ft)
+                st[ft] = mfma32(vt_frag_ps<F / 4>(Pb, r0 + 32 * ft, kb, lane), bv, st[ft]);
+        }
+    } else {
+        // one work-group per CU: no other work-group's waves hide the LDS
+        // latency, so the fragments of step kb + 1 are read before step kb's
+        // products are issued. The read offsets are formed once: the swizzle
+        // depends on the low four bits of the row only, so step kb is the same
+        // offsets 16 kb rows further on (an immediate offset of the read).
+        const int vlo = vt_offset_ps<D / 4>(32 * cs, 0, lane), vhi = vt_offset_ps<D / 4>(32 * cs, 8, lane);
+        int plo[RW / 32], phi_[RW / 32];
+#pragma unroll
+        for (int ft = 0; ft < RW / 32; ++ft) {
+            plo[ft] = vt_offset_ps<F / 4>(r0 + 32 * ft, 0, lane);
+            phi_[ft] = vt_offset_ps<F / 4>(r0 + 32 * ft, 8, lane);
+        }
+        bf16x8 bv = vt_frag_at(Vb, vlo, vhi);
+        bf16x8 pa[RW / 32];
+#pragma unroll
+        for (int ft = 0; ft < RW / 32; ++ft) pa[ft] = vt_frag_at(Pb, plo[ft], phi_[ft]);
+#pragma unroll
+        for (int kb = 0; kb < CT / 16; ++kb) {
+            bf16x8 bn = bv, pn[RW / 32];
+#pragma unroll
+            for (int ft = 0; ft < RW / 32; ++ft) pn[ft] = pa[ft];
+            if (kb + 1 < CT / 16) {
+                const uint16_t* const vk = Vb + 16 * (kb + 1) * D;
+                const uint16_t* const pk = Pb + 16 * (kb + 1) * F;
+                bn = vt_frag_at(vk, vlo, vhi);
+#pragma unroll
+                for (int ft = 0; ft < RW / 32; ++ft) pn[ft] = vt_frag_at(pk, plo[ft], phi_[ft]);
+            }
+#pragma unroll
+            for (int ft = 0; ft < RW / 32; ++ft) st[ft] = mfma32(pa[ft], bv, st[ft]);
+            bv = bn;
+#pragma unroll
+            for (int ft = 0; ft < RW / 32; ++ft) pa[ft] = pn[ft];
+        }
     }
 }
 
@@ -1566,6 +1623,7 @@ void prefill_mfma_kernel(CommitArgs a)
         for (int c = 0; c < pp.nchunks; ++c) {
             int tl = tid;
             asm volatile("" : "+v"(tl));
+            tl &= NT - 1;  // known in range: index arithmetic stays unsigned shifts
             __syncthreads();  // W rows staged; every wave is done with the previous chunk
             prefill_phi(pp, c, tl, Vs, Ps, Ws, vr, kf, zl);
             __syncthreads();
