@@ -49,13 +49,16 @@ __device__ __forceinline__ f32x4 ld4(const uint16_t* p)
 // steps); the state's 32-column panels make its operand loads whole 1 KB rows.
 // The record is read once per work-group.
 // ---------------------------------------------------------------------------
+// Six work-groups per CU where the LDS allows it (FW <= 64: 25.6 KB each, at
+// most 80 registers); the state stream of some overlaps the logits and
+// softmaxes of others.
 template <typename T, int D, int FW>
-__global__ __launch_bounds__(kThreads) void forward_generic_kernel(ForwardArgs a)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void forward_generic_kernel(ForwardArgs a)
 {
     constexpr int F = 2 * FW;
-    constexpr int US = FW + 4;  // LDS row strides (floats)
-    constexpr int PS = 64 + 4;
+    constexpr int PS = 64 + 4;  // LDS row strides (floats)
     constexpr int FS = F + 4;
+    constexpr int US = FS;      // U shares the rows of Phi' (see below)
     constexpr int NU = FW / 32;  // feature-logit column tiles
     constexpr int NQ = FW / 4;   // features per thread in the softmax
     const int pair = blockIdx.x;
@@ -64,9 +67,12 @@ __global__ __launch_bounds__(kThreads) void forward_generic_kernel(ForwardArgs a
     const int l32 = lane & 31, hf = lane >> 5;
     const int B = a.B, NK = (B + 31) >> 5;
 
-    __shared__ __attribute__((aligned(16))) float Us[32 * US];
     __shared__ __attribute__((aligned(16))) float Ps[32 * PS];
     __shared__ __attribute__((aligned(16))) float Phs[32 * FS];
+    // U row i lies in Phi' row i: the softmax reads row i of U and then writes
+    // row i of Phi' from the eight threads of row i, all of one wave, whose
+    // LDS accesses complete in program order
+    float* const Us = Phs;
 
     T* const ob = static_cast<T*>(a.out) + static_cast<int64_t>(r) * a.os.req + static_cast<int64_t>(h) * a.os.head;
     const int slot = a.slot_ids[r];
