@@ -1260,7 +1260,27 @@ struct PCfg {
     static constexpr int MAIN = 2 * (NBUF * CT * (D + F) + FW * D);
     static constexpr int ZRED = 4 * CT * F;             // fp32 Z partials of every token slot
     static constexpr int LDS = MAIN > ZRED ? MAIN : ZRED;
+    // one-buffer loop: each wave's four state tiles are 2 x 2 (two column
+    // slices, 64 rows) rather than 4 x 1, so a step of dS reads four operand
+    // fragments instead of five
+    static constexpr bool SQ = NBUF == 1 && NC % 2 == 0 && RW == 128;
 };
+
+// State tile i of wave wv in the prefill: its first row and column slice.
+template <int D, int FW>
+__device__ __forceinline__ int ptile_row(int wv, int i)
+{
+    using P = PCfg<D, FW>;
+    if constexpr (P::SQ) return (wv / (P::NC / 2)) * 64 + 32 * (i / 2);
+    else return (wv / P::NC) * P::RW + 32 * i;
+}
+template <int D, int FW>
+__device__ __forceinline__ int ptile_col(int wv, int i)
+{
+    using P = PCfg<D, FW>;
+    if constexpr (P::SQ) return 2 * (wv % (P::NC / 2)) + i % 2;
+    else return wv % P::NC;
+}
 
 // All-reductions over the lane pairs (L, L ^ 16) and (L, L ^ 32) with the
 // gfx950 row-swap instructions (VALU, no LDS round trip): swapping a value
@@ -1494,34 +1514,46 @@ __device__ __forceinline__ void prefill_ds(int c, int tid, const uint16_t* Vs, c
         // products are issued. The read offsets are formed once: the swizzle
         // depends on the low four bits of the row only, so step kb is the same
         // offsets 16 kb rows further on (an immediate offset of the read).
-        const int vlo = vt_offset_ps<D / 4>(32 * cs, 0, lane), vhi = vt_offset_ps<D / 4>(32 * cs, 8, lane);
-        int plo[RW / 32], phi_[RW / 32];
+        // operand fragments of one step: V of the wave's NV column slices, phi(K)
+        // of its NP row tiles; tile i takes row operand i / NV and column i % NV
+        constexpr int NV = P::SQ ? 2 : 1, NP = RW / 32 / NV;
+        int vlo[NV], vhi[NV], plo[NP], phi_[NP];
 #pragma unroll
-        for (int ft = 0; ft < RW / 32; ++ft) {
-            plo[ft] = vt_offset_ps<F / 4>(r0 + 32 * ft, 0, lane);
-            phi_[ft] = vt_offset_ps<F / 4>(r0 + 32 * ft, 8, lane);
+        for (int b = 0; b < NV; ++b) {
+            vlo[b] = vt_offset_ps<D / 4>(32 * ptile_col<D, FW>(wv, b), 0, lane);
+            vhi[b] = vt_offset_ps<D / 4>(32 * ptile_col<D, FW>(wv, b), 8, lane);
         }
-        bf16x8 bv = vt_frag_at(Vb, vlo, vhi);
-        bf16x8 pa[RW / 32];
 #pragma unroll
-        for (int ft = 0; ft < RW / 32; ++ft) pa[ft] = vt_frag_at(Pb, plo[ft], phi_[ft]);
+        for (int a = 0; a < NP; ++a) {
+            plo[a] = vt_offset_ps<F / 4>(ptile_row<D, FW>(wv, NV * a), 0, lane);
+            phi_[a] = vt_offset_ps<F / 4>(ptile_row<D, FW>(wv, NV * a), 8, lane);
+        }
+        bf16x8 bv[NV], pa[NP];
+#pragma unroll
+        for (int b = 0; b < NV; ++b) bv[b] = vt_frag_at(Vb, vlo[b], vhi[b]);
+#pragma unroll
+        for (int a = 0; a < NP; ++a) pa[a] = vt_frag_at(Pb, plo[a], phi_[a]);
 #pragma unroll
         for (int kb = 0; kb < CT / 16; ++kb) {
-            bf16x8 bn = bv, pn[RW / 32];
+            bf16x8 bn[NV], pn[NP];
 #pragma unroll
-            for (int ft = 0; ft < RW / 32; ++ft) pn[ft] = pa[ft];
+            for (int b = 0; b < NV; ++b) bn[b] = bv[b];
+#pragma unroll
+            for (int a = 0; a < NP; ++a) pn[a] = pa[a];
             if (kb + 1 < CT / 16) {
                 const uint16_t* const vk = Vb + 16 * (kb + 1) * D;
                 const uint16_t* const pk = Pb + 16 * (kb + 1) * F;
-                bn = vt_frag_at(vk, vlo, vhi);
 #pragma unroll
-                for (int ft = 0; ft < RW / 32; ++ft) pn[ft] = vt_frag_at(pk, plo[ft], phi_[ft]);
+                for (int b = 0; b < NV; ++b) bn[b] = vt_frag_at(vk, vlo[b], vhi[b]);
+#pragma unroll
+                for (int a = 0; a < NP; ++a) pn[a] = vt_frag_at(pk, plo[a], phi_[a]);
             }
 #pragma unroll
-            for (int ft = 0; ft < RW / 32; ++ft) st[ft] = mfma32(pa[ft], bv, st[ft]);
-            bv = bn;
+            for (int t = 0; t < RW / 32; ++t) st[t] = mfma32(pa[t / NV], bv[t % NV], st[t]);
 #pragma unroll
-            for (int ft = 0; ft < RW / 32; ++ft) pa[ft] = pn[ft];
+            for (int b = 0; b < NV; ++b) bv[b] = bn[b];
+#pragma unroll
+            for (int a = 0; a < NP; ++a) pa[a] = pn[a];
         }
     }
 }
@@ -1535,7 +1567,6 @@ void prefill_mfma_kernel(CommitArgs a)
     const int pair = blockIdx.x;
     const int h = pair % a.H;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int cs = wv % NC, r0 = (wv / NC) * RW;
     const int n16 = lane & 15, q = lane >> 4;
 
     __shared__ __attribute__((aligned(16))) uint8_t smem[P::LDS];
@@ -1582,17 +1613,24 @@ void prefill_mfma_kernel(CommitArgs a)
         }
     }
 
-    // state tiles: rows r0 + 32 ft + (C layout), columns 32 cs + lane % 32
+    // state tile ft: rows ptile_row + (C layout), columns 32 ptile_col + lane % 32
     f32x16 st[RW / 32];
-    const f32x4* const sp4 = reinterpret_cast<const f32x4*>(rec + 32 * (cs * F + r0)) + lane;
+    // (tiles of one column slice: one base, the tiles at fixed offsets)
+    const f32x4* const sp0 = reinterpret_cast<const f32x4*>(
+                                 rec + 32 * (ptile_col<D, FW>(wv, 0) * F + ptile_row<D, FW>(wv, 0))) + lane;
 #pragma unroll
-    for (int ft = 0; ft < RW / 32; ++ft)
+    for (int ft = 0; ft < RW / 32; ++ft) {
+        const f32x4* const sp4 =
+            P::SQ ? reinterpret_cast<const f32x4*>(
+                        rec + 32 * (ptile_col<D, FW>(wv, ft) * F + ptile_row<D, FW>(wv, ft))) + lane
+                  : sp0 + 4 * ft * 64;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const f32x4 x = __builtin_nontemporal_load(sp4 + (4 * ft + i) * 64);
+            const f32x4 x = __builtin_nontemporal_load(sp4 + i * 64);
 #pragma unroll
             for (int e = 0; e < 4; ++e) st[ft][4 * i + e] = x[e];
         }
+    }
     float zl[FW / 2];  // this lane's token slot: features 16 T + 4 q + e of the + half, then the - half
 #pragma unroll
     for (int i = 0; i < FW / 2; ++i) zl[i] = 0.0f;
@@ -1632,14 +1670,18 @@ void prefill_mfma_kernel(CommitArgs a)
         __syncthreads();
     }
 
-    f32x4* const dst = reinterpret_cast<f32x4*>(rec + 32 * (cs * F + r0)) + lane;
+    f32x4* const dst0 = reinterpret_cast<f32x4*>(rec + 32 * (ptile_col<D, FW>(wv, 0) * F + ptile_row<D, FW>(wv, 0))) + lane;
 #pragma unroll
-    for (int ft = 0; ft < RW / 32; ++ft)
+    for (int ft = 0; ft < RW / 32; ++ft) {
+        f32x4* const dst =
+            P::SQ ? reinterpret_cast<f32x4*>(rec + 32 * (ptile_col<D, FW>(wv, ft) * F + ptile_row<D, FW>(wv, ft))) + lane
+                  : dst0 + 4 * ft * 64;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const f32x4 x = {st[ft][4 * i], st[ft][4 * i + 1], st[ft][4 * i + 2], st[ft][4 * i + 3]};
-            __builtin_nontemporal_store(x, dst + (4 * ft + i) * 64);
+            __builtin_nontemporal_store(x, dst + i * 64);
         }
+    }
 
     // Z: the token slots' fp32 partials, reduced in a fixed order
     float* const zrow = Zr + (16 * wv + n16) * F + 4 * q;
