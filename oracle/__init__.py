@@ -45,27 +45,32 @@ def build(force: bool = False) -> str:
     return _LIB_PATH
 
 
+def _open(path: str):
+    """Load an oracle library from ``path`` with its call signatures set."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    D = ctypes.c_double
+    lib.bha_ref_feature_map.argtypes = [I, I, I, P, P, P]
+    lib.bha_ref_state_commit.argtypes = [I, I, I, P, P, P, P, P]
+    lib.bha_ref_state_build.argtypes = [I, I, I, P, P, P, P, P]
+    lib.bha_ref_block_forward.argtypes = [I, I, I, P, P, P, P, D, D, P, P, P]
+    lib.bha_ref_block_forward_batch.argtypes = [I, I, I, I, I, P, P, P, P, P, D, P, P, P, I]
+    lib.bha_ref_state_commit_batch.argtypes = [I, I, I, I, I, P, P, P, P, P, I]
+    lib.bha_ref_prefix_attention.argtypes = [I, I, I, P, P, P, P, P, D, P]
+    lib.bha_ref_prefix_attention.restype = None
+    for f in (lib.bha_ref_feature_map, lib.bha_ref_state_commit, lib.bha_ref_state_build,
+              lib.bha_ref_block_forward, lib.bha_ref_block_forward_batch,
+              lib.bha_ref_state_commit_batch):
+        f.restype = None
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         build()
-        lib = ctypes.CDLL(_LIB_PATH)
-        P = ctypes.c_void_p
-        I = ctypes.c_int
-        D = ctypes.c_double
-        lib.bha_ref_feature_map.argtypes = [I, I, I, P, P, P]
-        lib.bha_ref_state_commit.argtypes = [I, I, I, P, P, P, P, P]
-        lib.bha_ref_state_build.argtypes = [I, I, I, P, P, P, P, P]
-        lib.bha_ref_block_forward.argtypes = [I, I, I, P, P, P, P, D, D, P, P, P]
-        lib.bha_ref_block_forward_batch.argtypes = [I, I, I, I, I, P, P, P, P, P, D, P, P, P, I]
-        lib.bha_ref_state_commit_batch.argtypes = [I, I, I, I, I, P, P, P, P, P, I]
-        lib.bha_ref_prefix_attention.argtypes = [I, I, I, P, P, P, P, P, D, P]
-        lib.bha_ref_prefix_attention.restype = None
-        for f in (lib.bha_ref_feature_map, lib.bha_ref_state_commit, lib.bha_ref_state_build,
-                  lib.bha_ref_block_forward, lib.bha_ref_block_forward_batch,
-                  lib.bha_ref_state_commit_batch):
-            f.restype = None
-        _lib = lib
+        _lib = _open(_LIB_PATH)
     return _lib
 
 
