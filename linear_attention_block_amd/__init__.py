@@ -177,22 +177,31 @@ def _check_device(dev, *ts):
             raise ValueError("all tensors must be on the same device")
 
 
-def feature_map(x: torch.Tensor, w: torch.Tensor, *, stream=None) -> torch.Tensor:
-    """phi(x) = [softmax(x W), softmax(-x W)] -> float32 [R][B][H][2FW]."""
-    lib = load_library()
+def _feature_map_args(x, w, out, stream):
     xs = _tok_strides(x, "x")
     R, B, H, d = x.shape
     fw, wh = _w_stride(w, H, d)
     if w.dtype != x.dtype:
         raise TypeError("w must have the dtype of x")
     _check_device(x.device, w)
-    phi = torch.empty((R, B, H, 2 * fw), dtype=torch.float32, device=x.device)
+    if out is None:
+        out = torch.empty((R, B, H, 2 * fw), dtype=torch.float32, device=x.device)
+    elif out.shape != (R, B, H, 2 * fw) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [R][B][H][2FW] tensor")
+    _check_device(x.device, out)
     dims = bha_dims(R, H, d, fw, B, _io_dtype(x), 0.0)
-    st = lib.bha_feature_map(ctypes.byref(dims), _ptr(x), ctypes.byref(xs), _ptr(w), wh,
-                             _ptr(phi), _stream(x.device, stream))
+    args = (ctypes.byref(dims), _ptr(x), ctypes.byref(xs), _ptr(w), wh, _ptr(out), _stream(x.device, stream))
+    return args, (dims, xs), out
+
+
+def feature_map(x: torch.Tensor, w: torch.Tensor, *, out=None, stream=None) -> torch.Tensor:
+    """phi(x) = [softmax(x W), softmax(-x W)] -> float32 [R][B][H][2FW]."""
+    lib = load_library()
+    args, _keep, out = _feature_map_args(x, w, out, stream)
+    st = lib.bha_feature_map(*args)
     if st != 0:
         raise BhaError("bha_feature_map", st)
-    return phi
+    return out
 
 
 def _forward_args(q, k, v, w, gamma, state, slot_ids, out, scale, stream):
@@ -480,6 +489,12 @@ def prepare_prefix_attention(q, k, v, kp, vp, seq_offsets, out, *, scale: float 
     args, keep = _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream, workspace)
     keep = keep + (q, k, v, kp, vp, seq_offsets, out)
     return _Prepared(load_library().bha_prefix_attention, "bha_prefix_attention", args, keep)
+
+
+def prepare_feature_map(x, w, out, *, stream=None):
+    """Marshal a bha_feature_map call once, for launch-rate-bound loops."""
+    args, keep, out = _feature_map_args(x, w, out, stream)
+    return _Prepared(load_library().bha_feature_map, "bha_feature_map", args, keep + (x, w, out))
 
 
 def prepare_commit(k, v, w, state, slot_ids, *, stream=None):

@@ -9,10 +9,25 @@
 
 using namespace bha;
 
-static int launch_status(hipError_t e)
+// The status of the launches a call enqueued (each launcher returns its
+// launches' own status; the thread's sticky last error is not consulted).
+static int launch_status(hipError_t e) { return e == hipSuccess ? BHA_OK : BHA_ERR_HIP; }
+
+// Kernel choice is made on the host before anything is enqueued: one
+// launcher per call, picked by its *_supported predicate.
+static hipError_t launch_forward_any(const ForwardArgs& a, hipStream_t stream)
 {
-    if (e != hipSuccess) return BHA_ERR_HIP;
-    return (hipGetLastError() == hipSuccess) ? BHA_OK : BHA_ERR_HIP;
+    return forward_mfma_supported(a) ? launch_forward_mfma(a, stream) : launch_forward_generic(a, stream);
+}
+
+// A commit of B tokens per request: the commit kernel (bf16, B <= 32), the
+// prefill kernel over each request's B rows (bf16, B <= 64), else the
+// fp32-arithmetic commit kernel.
+static hipError_t launch_commit_any(const CommitArgs& a, hipStream_t stream)
+{
+    if (commit_mfma_supported(a)) return launch_commit_mfma(a, stream);
+    if (prefill_mfma_supported(a)) return launch_prefill_mfma(a, stream);
+    return launch_commit_generic(a, stream);
 }
 
 extern "C" int bha_feature_map(const bha_dims* dims, const void* x, const bha_strides* xs,
@@ -30,7 +45,8 @@ extern "C" int bha_feature_map(const bha_dims* dims, const void* x, const bha_st
     a.R = dims->num_requests; a.H = dims->num_heads; a.d = dims->head_dim;
     a.FW = dims->feat_half; a.B = dims->block_size; a.io = dims->io_dtype;
     a.x = x; a.xs = *xs; a.w = w; a.wh = w_head_stride; a.phi = phi;
-    return launch_status(launch_feature_map_generic(a, stream));
+    return launch_status(feature_map_mfma_supported(a) ? launch_feature_map_mfma(a, stream)
+                                                       : launch_feature_map_generic(a, stream));
 }
 
 extern "C" int bha_block_forward(const bha_dims* dims, const void* q, const void* k, const void* v,
@@ -57,9 +73,7 @@ extern "C" int bha_block_forward(const bha_dims* dims, const void* q, const void
     a.q = q; a.k = k; a.v = v; a.qs = *qkv; a.ks = *qkv; a.G = 1;
     a.w = w; a.wh = w_head_stride; a.gamma = gamma;
     a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids; a.out = out; a.os = *outs;
-    hipError_t e = launch_forward_mfma(a, stream);
-    if (e == hipErrorNotSupported) e = launch_forward_generic(a, stream);
-    return launch_status(e);
+    return launch_status(launch_forward_any(a, stream));
 }
 
 extern "C" int bha_block_forward_gqa(const bha_dims* dims, int32_t num_kv_heads, const void* q,
@@ -90,20 +104,7 @@ extern "C" int bha_block_forward_gqa(const bha_dims* dims, int32_t num_kv_heads,
     a.q = q; a.k = k; a.v = v; a.qs = *qs; a.ks = *kvs; a.G = dims->num_heads / num_kv_heads;
     a.w = w; a.wh = w_head_stride; a.gamma = gamma;
     a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids; a.out = out; a.os = *outs;
-    hipError_t e = launch_forward_mfma(a, stream);
-    if (e == hipErrorNotSupported) e = launch_forward_generic(a, stream);
-    return launch_status(e);
-}
-
-// A commit of B tokens per request: the commit kernel (bf16, B <= 32), the
-// prefill kernel over each request's B rows (bf16, B <= 64), else the
-// fp32-arithmetic commit kernel.
-static hipError_t launch_commit_any(const CommitArgs& a, hipStream_t stream)
-{
-    hipError_t e = launch_commit_mfma(a, stream);
-    if (e == hipErrorNotSupported) e = launch_prefill_mfma(a, stream);
-    if (e == hipErrorNotSupported) e = launch_commit_generic(a, stream);
-    return e;
+    return launch_status(launch_forward_any(a, stream));
 }
 
 extern "C" int bha_state_commit(const bha_dims* dims, const void* k, const void* v,
@@ -156,14 +157,11 @@ extern "C" int bha_block_forward_commit(const bha_dims* dims, const void* q, con
     c.k = k; c.v = v; c.ks = *qkv; c.w = w; c.wh = w_head_stride;
     c.state = state; c.num_slots = num_slots; c.slot_ids = slot_ids;
     c.seq_offsets = nullptr; c.total_tokens = 0; c.commit_mask = commit_mask;
-    hipError_t e = launch_forward_commit_mfma(a, c, stream);
-    if (e == hipErrorNotSupported) {
-        // the same result in two launches: the forward reads the state before
-        // the commit changes it (both on the caller's stream)
-        e = launch_forward_mfma(a, stream);
-        if (e == hipErrorNotSupported) e = launch_forward_generic(a, stream);
-        if (e == hipSuccess) e = launch_commit_any(c, stream);
-    }
+    if (forward_commit_mfma_supported(a)) return launch_status(launch_forward_commit_mfma(a, c, stream));
+    // the same result in two launches: the forward reads the state before the
+    // commit changes it (both on the caller's stream)
+    hipError_t e = launch_forward_any(a, stream);
+    if (e == hipSuccess) e = launch_commit_any(c, stream);
     return launch_status(e);
 }
 
@@ -196,9 +194,7 @@ extern "C" int bha_state_prefill(const bha_dims* dims, const void* k, const void
     a.k = k; a.v = v; a.ks = ps; a.w = w; a.wh = w_head_stride;
     a.state = state; a.num_slots = num_slots; a.slot_ids = slot_ids;
     a.seq_offsets = seq_offsets; a.total_tokens = total_tokens; a.commit_mask = nullptr;
-    hipError_t e = launch_prefill_mfma(a, stream);
-    if (e == hipErrorNotSupported) e = launch_commit_generic(a, stream);
-    return launch_status(e);
+    return launch_status(prefill_mfma_supported(a) ? launch_prefill_mfma(a, stream) : launch_commit_generic(a, stream));
 }
 
 static int64_t prefix_workspace_bytes(const bha_dims* d, int splits)
@@ -265,9 +261,8 @@ extern "C" int bha_prefix_attention(const bha_dims* dims, const void* q, const v
     a.scale = dims->scale > 0.0f ? dims->scale : 1.0f / sqrtf((float)dims->head_dim);
     a.q = q; a.k = k; a.v = v; a.qs = *qkv; a.kp = kp; a.vp = vp; a.ps = ps;
     a.seq_offsets = seq_offsets; a.total_tokens = total_tokens; a.out = out; a.os = *outs;
-    hipError_t e = launch_prefix_attention_mfma(a, stream);
-    if (e == hipErrorNotSupported) e = launch_prefix_attention_generic(a, stream);
-    return launch_status(e);
+    return launch_status(prefix_attention_mfma_supported(a) ? launch_prefix_attention_mfma(a, stream)
+                                                            : launch_prefix_attention_generic(a, stream));
 }
 
 extern "C" int64_t bha_state_record_floats(int32_t head_dim, int32_t feat_half)

@@ -221,8 +221,30 @@ struct PhiArgs {
     float* phi;
 };
 
-// Softmax prefix attention: matrix-core kernel (bf16, B <= 32) and the plain
-// kernel for every size and both I/O dtypes.
+// Enqueues one kernel and returns that launch's own status. The thread's
+// sticky last error (hipGetLastError) is neither read nor cleared: it may hold
+// an error left by an earlier, unrelated call, which must not decide whether
+// this launch happened.
+template <typename T>
+struct same_type {
+    using type = T;
+};
+template <typename... KA>
+inline hipError_t launch_kernel(void (*kernel)(KA...), dim3 grid, dim3 block, hipStream_t s,
+                                typename same_type<KA>::type... args)
+{
+    void* argv[] = {static_cast<void*>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, s);
+}
+
+// Kernel choice is made on the host from the arguments alone: each
+// *_supported predicate says whether its launcher covers the call; a launcher
+// is only called for arguments its predicate accepts, and returns the status
+// of the launches it enqueued.
+
+// Softmax prefix attention: matrix-core kernel (bf16, B <= 64, 32-bit row
+// offsets) and the fp32-arithmetic kernel for every size and both I/O dtypes.
+bool prefix_attention_mfma_supported(const PrefixArgs& a);
 hipError_t launch_prefix_attention_mfma(const PrefixArgs& a, hipStream_t s);
 hipError_t launch_prefix_attention_generic(const PrefixArgs& a, hipStream_t s);
 
@@ -231,14 +253,19 @@ hipError_t launch_forward_generic(const ForwardArgs& a, hipStream_t s);
 hipError_t launch_commit_generic(const CommitArgs& a, hipStream_t s);
 hipError_t launch_feature_map_generic(const PhiArgs& a, hipStream_t s);
 
-// bf16 MFMA kernels for bf16 I/O and B <= 32. Return hipErrorNotSupported
-// (without launching) for sizes they do not cover.
+// bf16 MFMA kernels for bf16 I/O.
+bool forward_mfma_supported(const ForwardArgs& a);
 hipError_t launch_forward_mfma(const ForwardArgs& a, hipStream_t s);
+bool commit_mfma_supported(const CommitArgs& a);
 hipError_t launch_commit_mfma(const CommitArgs& a, hipStream_t s);
+bool prefill_mfma_supported(const CommitArgs& a);
 hipError_t launch_prefill_mfma(const CommitArgs& a, hipStream_t s);
 // Forward of the block's last denoising step and the commit of its K, V in one
 // pass over each pair's state (bf16, B <= 32); c carries the commit mask.
+bool forward_commit_mfma_supported(const ForwardArgs& a);
 hipError_t launch_forward_commit_mfma(const ForwardArgs& a, const CommitArgs& c, hipStream_t s);
+bool feature_map_mfma_supported(const PhiArgs& a);
+hipError_t launch_feature_map_mfma(const PhiArgs& a, hipStream_t s);
 
 // Host-side argument checks (no HIP calls); see bha_validate.cpp.
 int validate_dims(const bha_dims* d);

@@ -501,59 +501,46 @@ __global__ __launch_bounds__(64) void feature_map_generic_kernel(PhiArgs a)
 }  // namespace
 
 template <typename T, int D>
-static void forward_dispatch(const ForwardArgs& a, hipStream_t s, dim3 grid)
+static hipError_t forward_dispatch(const ForwardArgs& a, hipStream_t s, dim3 grid)
 {
     switch (a.FW) {
-        case 32: hipLaunchKernelGGL((forward_generic_kernel<T, D, 32>), grid, dim3(kThreads), 0, s, a); break;
-        case 64: hipLaunchKernelGGL((forward_generic_kernel<T, D, 64>), grid, dim3(kThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL((forward_generic_kernel<T, D, 128>), grid, dim3(kThreads), 0, s, a); break;
+        case 32: return launch_kernel(forward_generic_kernel<T, D, 32>, grid, dim3(kThreads), s, a);
+        case 64: return launch_kernel(forward_generic_kernel<T, D, 64>, grid, dim3(kThreads), s, a);
+        default: return launch_kernel(forward_generic_kernel<T, D, 128>, grid, dim3(kThreads), s, a);
     }
 }
 
 hipError_t launch_forward_generic(const ForwardArgs& a, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H));
-    if (a.io == BHA_BF16) {
-        if (a.d == 128) forward_dispatch<uint16_t, 128>(a, s, grid);
-        else forward_dispatch<uint16_t, 64>(a, s, grid);
-    } else {
-        if (a.d == 128) forward_dispatch<float, 128>(a, s, grid);
-        else forward_dispatch<float, 64>(a, s, grid);
-    }
-    return hipGetLastError();
+    if (a.io == BHA_BF16)
+        return a.d == 128 ? forward_dispatch<uint16_t, 128>(a, s, grid) : forward_dispatch<uint16_t, 64>(a, s, grid);
+    return a.d == 128 ? forward_dispatch<float, 128>(a, s, grid) : forward_dispatch<float, 64>(a, s, grid);
 }
 
 template <typename T, int D>
-static void commit_dispatch(const CommitArgs& a, hipStream_t s, dim3 grid)
+static hipError_t commit_dispatch(const CommitArgs& a, hipStream_t s, dim3 grid)
 {
     switch (a.FW) {
-        case 32: hipLaunchKernelGGL((commit_generic_kernel<T, D, 32>), grid, dim3(kCommitThreads), 0, s, a); break;
-        case 64: hipLaunchKernelGGL((commit_generic_kernel<T, D, 64>), grid, dim3(kCommitThreads), 0, s, a); break;
-        default: hipLaunchKernelGGL((commit_generic_kernel<T, D, 128>), grid, dim3(kCommitThreads), 0, s, a); break;
+        case 32: return launch_kernel(commit_generic_kernel<T, D, 32>, grid, dim3(kCommitThreads), s, a);
+        case 64: return launch_kernel(commit_generic_kernel<T, D, 64>, grid, dim3(kCommitThreads), s, a);
+        default: return launch_kernel(commit_generic_kernel<T, D, 128>, grid, dim3(kCommitThreads), s, a);
     }
 }
 
 hipError_t launch_commit_generic(const CommitArgs& a, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H));
-    if (a.io == BHA_BF16) {
-        if (a.d == 128) commit_dispatch<uint16_t, 128>(a, s, grid);
-        else commit_dispatch<uint16_t, 64>(a, s, grid);
-    } else {
-        if (a.d == 128) commit_dispatch<float, 128>(a, s, grid);
-        else commit_dispatch<float, 64>(a, s, grid);
-    }
-    return hipGetLastError();
+    if (a.io == BHA_BF16)
+        return a.d == 128 ? commit_dispatch<uint16_t, 128>(a, s, grid) : commit_dispatch<uint16_t, 64>(a, s, grid);
+    return a.d == 128 ? commit_dispatch<float, 128>(a, s, grid) : commit_dispatch<float, 64>(a, s, grid);
 }
 
 hipError_t launch_feature_map_generic(const PhiArgs& a, hipStream_t s)
 {
-    const int64_t nblk = static_cast<int64_t>(a.R) * a.B * a.H;
-    if (a.io == BHA_BF16)
-        hipLaunchKernelGGL(feature_map_generic_kernel<uint16_t>, dim3(static_cast<uint32_t>(nblk)), dim3(64), 0, s, a);
-    else
-        hipLaunchKernelGGL(feature_map_generic_kernel<float>, dim3(static_cast<uint32_t>(nblk)), dim3(64), 0, s, a);
-    return hipGetLastError();
+    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.B * a.H));
+    if (a.io == BHA_BF16) return launch_kernel(feature_map_generic_kernel<uint16_t>, grid, dim3(64), s, a);
+    return launch_kernel(feature_map_generic_kernel<float>, grid, dim3(64), s, a);
 }
 
 }  // namespace bha

@@ -1699,6 +1699,96 @@ void prefill_mfma_kernel(CommitArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Feature map (bha_feature_map, bf16 tokens)
+// ---------------------------------------------------------------------------
+// One work-group of D/32 waves per (head, 32 D/32 consecutive tokens of the
+// [R][B] batch). W_h and the tokens' rows go to LDS; each wave then takes 32
+// tokens: u^T = W^T X^T on the matrix cores (lane = token, as in the
+// forward), both softmaxes of each token in fp32 (lanes n and n + 32 hold
+// halves of token n's logits), and phi stored in fp32 straight from the
+// accumulator registers: 16 bytes per lane, lanes n and n + 32 writing 32
+// contiguous bytes of token n's row, every row whole after FW / 8 stores.
+// Roofline: HBM. Algorithmic bytes per (token, head): the row read (2 d) and
+// phi written (4 F); W once per head per launch.
+template <int D, int FW>
+__global__ __launch_bounds__(64 * (D / 32)) void feature_map_mfma_kernel(PhiArgs a, int tiles)
+{
+    using C = Cfg<D, FW>;
+    constexpr int NT = C::NT, TOK = 32 * C::NW, CH = D / 8, F = C::F;
+    __shared__ alignas(16) uint16_t Ws[FW * C::RS];
+    __shared__ alignas(16) uint16_t Xs[TOK * C::RS];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ln = lane & 31, g = lane >> 5;
+    const int h = blockIdx.x / tiles;
+    const int64_t ntok = static_cast<int64_t>(a.R) * a.B;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x % tiles) * TOK;
+    {
+        WChunks<D, FW, NT> wc;
+        wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
+        wc.template store_rows<C::RS>(Ws, tid);
+    }
+    // the tile's rows, 16 bytes per thread per step (rows past the batch read
+    // its last row and are not stored)
+    u32x4 xv[TOK * CH / NT];
+#pragma unroll
+    for (int i = 0; i < TOK * CH / NT; ++i) {
+        const int idx = tid + i * NT, row = idx / CH, ch = idx % CH;
+        const int64_t tk = t0 + row < ntok ? t0 + row : ntok - 1;
+        const int64_t r = tk / a.B, t = tk % a.B;
+        const uint16_t* src = static_cast<const uint16_t*>(a.x) + r * a.xs.req + t * a.xs.tok +
+                              static_cast<int64_t>(h) * a.xs.head + 8 * ch;
+        xv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+    }
+#pragma unroll
+    for (int i = 0; i < TOK * CH / NT; ++i) {
+        const int idx = tid + i * NT, row = idx / CH, ch = idx % CH;
+        *reinterpret_cast<u32x4*>(Xs + row * C::RS + 8 * ch) = xv[i];
+    }
+    __syncthreads();
+    f32x16 u[FW / 32];
+    feature_logits<D, FW, C::RS>(Ws, Xs + 32 * wv * C::RS, ln, g, u);
+    constexpr float kLog2e = 1.4426950408889634f;
+#pragma unroll
+    for (int T = 0; T < FW / 32; ++T)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) u[T][v] *= kLog2e;  // base-2 logits
+    float mx, mn;
+    logit_range<FW>(u, mx, mn);
+    float sp = 0.0f, sn = 0.0f;
+    f32x16 en[FW / 32];
+#pragma unroll
+    for (int T = 0; T < FW / 32; ++T)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float x = u[T][v];
+            u[T][v] = __builtin_amdgcn_exp2f(x - mx);
+            en[T][v] = __builtin_amdgcn_exp2f(mn - x);
+            sp += u[T][v];
+            sn += en[T][v];
+        }
+    sp += __shfl_xor(sp, 32, 64);
+    sn += __shfl_xor(sn, 32, 64);
+    const float ip = 1.0f / sp, in = 1.0f / sn;
+    const int64_t tk = t0 + 32 * wv + ln;
+    if (tk >= ntok) return;
+    float* const out = a.phi + (tk * a.H + h) * F;
+#pragma unroll
+    for (int T = 0; T < FW / 32; ++T)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            // features 32 T + 8 q4 + 4 g .. + 3 of each half
+            const int f0 = 32 * T + 8 * q4 + 4 * g;
+            f32x4 pv, nv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pv[e] = u[T][4 * q4 + e] * ip;
+                nv[e] = en[T][4 * q4 + e] * in;
+            }
+            *reinterpret_cast<f32x4*>(out + f0) = pv;
+            *reinterpret_cast<f32x4*>(out + FW + f0) = nv;
+        }
+}
+
 // Compute units of the current device (cached per device ordinal).
 static int compute_units()
 {
@@ -1724,9 +1814,8 @@ static hipError_t launch_forward_kt(const ForwardArgs& a, hipStream_t s)
     NG = (NG / a.H) * a.H;
     if (NG < a.H) NG = a.H;
     if (NG > npairs) NG = npairs;
-    hipLaunchKernelGGL((forward_mfma_kernel<D, FW, KT>), dim3(static_cast<uint32_t>(NG)), dim3(64 * (D / 32)), 0, s,
-                       a, npairs);
-    return hipGetLastError();
+    return launch_kernel(forward_mfma_kernel<D, FW, KT>, dim3(static_cast<uint32_t>(NG)), dim3(64 * (D / 32)), s, a,
+                         npairs);
 }
 
 // The split-slice F = 256 forward: one work-group of 2 NW waves per CU.
@@ -1738,9 +1827,8 @@ static hipError_t launch_forward_split(const ForwardArgs& a, hipStream_t s)
     NG = (NG / a.H) * a.H;
     if (NG < a.H) NG = a.H;
     if (NG > npairs) NG = npairs;
-    hipLaunchKernelGGL((forward_split_kernel<D>), dim3(static_cast<uint32_t>(NG)), dim3(2 * 64 * (D / 32)), 0, s, a,
-                       npairs);
-    return hipGetLastError();
+    return launch_kernel(forward_split_kernel<D>, dim3(static_cast<uint32_t>(NG)), dim3(2 * 64 * (D / 32)), s, a,
+                         npairs);
 }
 
 template <int D, int FW, int G>
@@ -1751,13 +1839,12 @@ static hipError_t launch_forward_gqa(const ForwardArgs& a, hipStream_t s)
     NG = (NG / hk) * hk;
     if (NG < hk) NG = hk;
     if (NG > npairs) NG = npairs;
-    hipLaunchKernelGGL((forward_gqa_mfma_kernel<D, FW, G>), dim3(static_cast<uint32_t>(NG)), dim3(64 * (D / 32)), 0,
-                       s, a, npairs);
-    return hipGetLastError();
+    return launch_kernel(forward_gqa_mfma_kernel<D, FW, G>, dim3(static_cast<uint32_t>(NG)), dim3(64 * (D / 32)), s,
+                         a, npairs);
 }
 
 // Blocks of up to 64 tokens with one query head per K/V head; up to 32 tokens
-// with 2 or 4 query heads per K/V head.
+// with 2, 4 (or, at FW <= 64, 8) query heads per K/V head.
 template <int D, int FW>
 static hipError_t launch_forward(const ForwardArgs& a, hipStream_t s)
 {
@@ -1766,12 +1853,10 @@ static hipError_t launch_forward(const ForwardArgs& a, hipStream_t s)
             if (a.B <= 32) return launch_forward_split<D>(a, s);
         return a.B <= 32 ? launch_forward_kt<D, FW, 1>(a, s) : launch_forward_kt<D, FW, 2>(a, s);
     }
-    if (a.B > 32) return hipErrorNotSupported;
     if (a.G == 2) return launch_forward_gqa<D, FW, 2>(a, s);
     if (a.G == 4) return launch_forward_gqa<D, FW, 4>(a, s);
-    if constexpr (FW <= 64)
-        if (a.G == 8) return launch_forward_gqa<D, FW, 8>(a, s);
-    return hipErrorNotSupported;
+    if constexpr (FW <= 64) return launch_forward_gqa<D, FW, 8>(a, s);
+    return hipErrorInvalidValue;  // excluded by forward_mfma_supported
 }
 
 template <int D>
@@ -1780,8 +1865,7 @@ static hipError_t forward_by_fw(const ForwardArgs& a, hipStream_t s)
     switch (a.FW) {
         case 32: return launch_forward<D, 32>(a, s);
         case 64: return launch_forward<D, 64>(a, s);
-        case 128: return launch_forward<D, 128>(a, s);
-        default: return hipErrorNotSupported;
+        default: return launch_forward<D, 128>(a, s);
     }
 }
 
@@ -1790,56 +1874,25 @@ static hipError_t prefill_by_fw(const CommitArgs& a, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>(a.R * a.H));
     switch (a.FW) {
-        case 32: hipLaunchKernelGGL((prefill_mfma_kernel<D, 32>), grid, dim3(PCfg<D, 32>::NT), 0, s, a); break;
-        case 64: hipLaunchKernelGGL((prefill_mfma_kernel<D, 64>), grid, dim3(PCfg<D, 64>::NT), 0, s, a); break;
-        case 128: hipLaunchKernelGGL((prefill_mfma_kernel<D, 128>), grid, dim3(PCfg<D, 128>::NT), 0, s, a); break;
-        default: return hipErrorNotSupported;
+        case 32: return launch_kernel(prefill_mfma_kernel<D, 32>, grid, dim3(PCfg<D, 32>::NT), s, a);
+        case 64: return launch_kernel(prefill_mfma_kernel<D, 64>, grid, dim3(PCfg<D, 64>::NT), s, a);
+        default: return launch_kernel(prefill_mfma_kernel<D, 128>, grid, dim3(PCfg<D, 128>::NT), s, a);
     }
-    return hipGetLastError();
 }
 
+// Blocks of 33..64 rows are not taken here but by the prefill kernel over
+// each request's B rows (at FW = 128 a kernel folding two 32-token tiles into
+// the register slice in turn measured 357.6 / 360.4 us against 274.1 / 276.9
+// us for the prefill kernel at B = 48 / 64, 256 x 16 pairs, d = 128).
 template <int D>
 static hipError_t commit_by_fw(const CommitArgs& a, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>(a.R * a.H)), block(64 * (D / 32));
-    // blocks of 33..64 rows: the prefill kernel over each request's B rows
-    // (at FW = 128 a kernel folding two 32-token tiles into the register
-    // slice in turn measured 357.6 / 360.4 us against 274.1 / 276.9 us for
-    // the prefill kernel at B = 48 / 64, 256 x 16 pairs, d = 128)
-    if (a.B > 32) return hipErrorNotSupported;
     switch (a.FW) {
-        case 32: hipLaunchKernelGGL((commit_mfma_kernel<D, 32>), grid, block, 0, s, a); break;
-        case 64: hipLaunchKernelGGL((commit_mfma_kernel<D, 64>), grid, block, 0, s, a); break;
-        case 128: hipLaunchKernelGGL((commit_mfma_kernel<D, 128>), grid, block, 0, s, a); break;
-        default: return hipErrorNotSupported;
+        case 32: return launch_kernel(commit_mfma_kernel<D, 32>, grid, block, s, a);
+        case 64: return launch_kernel(commit_mfma_kernel<D, 64>, grid, block, s, a);
+        default: return launch_kernel(commit_mfma_kernel<D, 128>, grid, block, s, a);
     }
-    return hipGetLastError();
-}
-
-}  // namespace
-
-// The matrix-core kernels address a block's rows with 32-bit offsets.
-static bool small_token_stride(int64_t tok) { return tok >= 0 && tok < (int64_t(1) << 25); }
-
-hipError_t launch_forward_mfma(const ForwardArgs& a, hipStream_t s)
-{
-    if (a.io != BHA_BF16 || a.B > 64) return hipErrorNotSupported;
-    if (!small_token_stride(a.qs.tok) || !small_token_stride(a.ks.tok) || !small_token_stride(a.os.tok))
-        return hipErrorNotSupported;
-    if (a.d == 128) return forward_by_fw<128>(a, s);
-    if (a.d == 64) return forward_by_fw<64>(a, s);
-    return hipErrorNotSupported;
-}
-
-hipError_t launch_prefill_mfma(const CommitArgs& a, hipStream_t s)
-{
-    // packed ranges (seq_offsets), or blocks of B <= 64 rows per request
-    if (a.io != BHA_BF16 || (a.seq_offsets == nullptr && a.B > 64)) return hipErrorNotSupported;
-    // in-chunk offsets (up to 128 rows) are 32-bit
-    if (a.ks.tok >= (int64_t(1) << 23)) return hipErrorNotSupported;
-    if (a.d == 128) return prefill_by_fw<128>(a, s);
-    if (a.d == 64) return prefill_by_fw<64>(a, s);
-    return hipErrorNotSupported;
 }
 
 template <int D>
@@ -1847,31 +1900,95 @@ static hipError_t forward_commit_by_fw(const ForwardArgs& a, const CommitArgs& c
 {
     const dim3 grid(static_cast<uint32_t>(a.R * a.H)), block(64 * (D / 32));
     switch (a.FW) {
-        case 32: hipLaunchKernelGGL((forward_commit_mfma_kernel<D, 32>), grid, block, 0, s, a, c); break;
-        case 64: hipLaunchKernelGGL((forward_commit_mfma_kernel<D, 64>), grid, block, 0, s, a, c); break;
-        case 128: hipLaunchKernelGGL((forward_commit_mfma_kernel<D, 128>), grid, block, 0, s, a, c); break;
-        default: return hipErrorNotSupported;
+        case 32: return launch_kernel(forward_commit_mfma_kernel<D, 32>, grid, block, s, a, c);
+        case 64: return launch_kernel(forward_commit_mfma_kernel<D, 64>, grid, block, s, a, c);
+        default: return launch_kernel(forward_commit_mfma_kernel<D, 128>, grid, block, s, a, c);
     }
-    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t feature_map_by_fw(const PhiArgs& a, hipStream_t s)
+{
+    constexpr int TOK = 32 * (D / 32);
+    const int64_t tiles = (static_cast<int64_t>(a.R) * a.B + TOK - 1) / TOK;
+    const dim3 grid(static_cast<uint32_t>(tiles * a.H)), block(64 * (D / 32));
+    const int nt = static_cast<int>(tiles);
+    switch (a.FW) {
+        case 32: return launch_kernel(feature_map_mfma_kernel<D, 32>, grid, block, s, a, nt);
+        case 64: return launch_kernel(feature_map_mfma_kernel<D, 64>, grid, block, s, a, nt);
+        default: return launch_kernel(feature_map_mfma_kernel<D, 128>, grid, block, s, a, nt);
+    }
+}
+
+}  // namespace
+
+// The matrix-core kernels address a block's rows with 32-bit offsets.
+static bool small_token_stride(int64_t tok) { return tok >= 0 && tok < (int64_t(1) << 25); }
+
+static bool mfma_sizes(int d, int FW) { return (d == 64 || d == 128) && (FW == 32 || FW == 64 || FW == 128); }
+
+bool forward_mfma_supported(const ForwardArgs& a)
+{
+    if (a.io != BHA_BF16 || a.B < 1 || a.B > 64 || !mfma_sizes(a.d, a.FW)) return false;
+    if (!small_token_stride(a.qs.tok) || !small_token_stride(a.ks.tok) || !small_token_stride(a.os.tok)) return false;
+    if (a.G == 1) return true;
+    // grouped K/V heads: one 32-token tile, 2 or 4 query heads per K/V head,
+    // or 8 at FW <= 64
+    return a.B <= 32 && (a.G == 2 || a.G == 4 || (a.G == 8 && a.FW <= 64));
+}
+
+hipError_t launch_forward_mfma(const ForwardArgs& a, hipStream_t s)
+{
+    return a.d == 128 ? forward_by_fw<128>(a, s) : forward_by_fw<64>(a, s);
+}
+
+bool prefill_mfma_supported(const CommitArgs& a)
+{
+    // packed ranges (seq_offsets), or blocks of B <= 64 rows per request;
+    // in-chunk offsets (up to 128 rows) are 32-bit
+    if (a.io != BHA_BF16 || !mfma_sizes(a.d, a.FW)) return false;
+    if (a.seq_offsets == nullptr && (a.B < 1 || a.B > 64)) return false;
+    return a.ks.tok >= 0 && a.ks.tok < (int64_t(1) << 23);
+}
+
+hipError_t launch_prefill_mfma(const CommitArgs& a, hipStream_t s)
+{
+    return a.d == 128 ? prefill_by_fw<128>(a, s) : prefill_by_fw<64>(a, s);
+}
+
+bool forward_commit_mfma_supported(const ForwardArgs& a)
+{
+    if (a.io != BHA_BF16 || a.B < 1 || a.B > 32 || a.G != 1 || !mfma_sizes(a.d, a.FW)) return false;
+    return small_token_stride(a.qs.tok) && small_token_stride(a.ks.tok) && small_token_stride(a.os.tok);
 }
 
 hipError_t launch_forward_commit_mfma(const ForwardArgs& a, const CommitArgs& c, hipStream_t s)
 {
-    if (a.io != BHA_BF16 || a.B > 32 || a.G != 1) return hipErrorNotSupported;
-    if (!small_token_stride(a.qs.tok) || !small_token_stride(a.ks.tok) || !small_token_stride(a.os.tok))
-        return hipErrorNotSupported;
-    if (a.d == 128) return forward_commit_by_fw<128>(a, c, s);
-    if (a.d == 64) return forward_commit_by_fw<64>(a, c, s);
-    return hipErrorNotSupported;
+    return a.d == 128 ? forward_commit_by_fw<128>(a, c, s) : forward_commit_by_fw<64>(a, c, s);
+}
+
+bool commit_mfma_supported(const CommitArgs& a)
+{
+    if (a.io != BHA_BF16 || a.seq_offsets != nullptr || a.B < 1 || a.B > 32 || !mfma_sizes(a.d, a.FW)) return false;
+    return small_token_stride(a.ks.tok);
 }
 
 hipError_t launch_commit_mfma(const CommitArgs& a, hipStream_t s)
 {
-    if (a.io != BHA_BF16 || a.B > 64) return hipErrorNotSupported;
-    if (!small_token_stride(a.ks.tok)) return hipErrorNotSupported;
-    if (a.d == 128) return commit_by_fw<128>(a, s);
-    if (a.d == 64) return commit_by_fw<64>(a, s);
-    return hipErrorNotSupported;
+    return a.d == 128 ? commit_by_fw<128>(a, s) : commit_by_fw<64>(a, s);
+}
+
+// phi is stored with 16-byte stores: its base must be 16-byte aligned (the
+// ABI asks for 4; other pointers take the fp32-arithmetic kernel)
+bool feature_map_mfma_supported(const PhiArgs& a)
+{
+    return a.io == BHA_BF16 && a.B >= 1 && mfma_sizes(a.d, a.FW) && a.xs.req >= 0 && a.xs.tok >= 0 &&
+           a.xs.head >= 0 && reinterpret_cast<uintptr_t>(a.phi) % 16 == 0;
+}
+
+hipError_t launch_feature_map_mfma(const PhiArgs& a, hipStream_t s)
+{
+    return a.d == 128 ? feature_map_by_fw<128>(a, s) : feature_map_by_fw<64>(a, s);
 }
 
 }  // namespace bha

@@ -546,39 +546,34 @@ int prefix_attention_splits(int R, int H, int d, int B, int io, int64_t total_to
     return sp < 2 ? 1 : static_cast<int>(sp);
 }
 
+bool prefix_attention_mfma_supported(const PrefixArgs& a)
+{
+    // per-lane offsets within a block and a chunk are 32-bit
+    return a.io == BHA_BF16 && a.B >= 1 && a.B <= 64 && (a.d == 64 || a.d == 128) && a.qs.tok >= 0 &&
+           a.qs.tok < (int64_t(1) << 25) && a.ps.tok >= 0 && a.ps.tok < (int64_t(1) << 25);
+}
+
 hipError_t launch_prefix_attention_mfma(const PrefixArgs& a, hipStream_t s)
 {
-    if (a.io != BHA_BF16 || a.B > 64) return hipErrorNotSupported;
-    // per-lane offsets within a block and a chunk are 32-bit
-    if (a.qs.tok >= (int64_t(1) << 25) || a.ps.tok >= (int64_t(1) << 25)) return hipErrorNotSupported;
     if (a.splits < 1 || a.splits > kSplitMax || (a.splits > 1 && !a.part)) return hipErrorInvalidValue;
     const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * prefix_query_tiles(a.B) * a.splits)),
         block(256);
-    if (a.d == 128) hipLaunchKernelGGL(prefix_attn_mfma_kernel<128>, grid, block, 0, s, a);
-    else if (a.d == 64) hipLaunchKernelGGL(prefix_attn_mfma_kernel<64>, grid, block, 0, s, a);
-    else return hipErrorNotSupported;
-    if (a.splits > 1) {
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        const dim3 mgrid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * a.B));
-        if (a.d == 128) hipLaunchKernelGGL((prefix_attn_merge_kernel<uint16_t, 128>), mgrid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((prefix_attn_merge_kernel<uint16_t, 64>), mgrid, dim3(256), 0, s, a);
-    }
-    return hipGetLastError();
+    hipError_t e = a.d == 128 ? launch_kernel(prefix_attn_mfma_kernel<128>, grid, block, s, a)
+                              : launch_kernel(prefix_attn_mfma_kernel<64>, grid, block, s, a);
+    if (e != hipSuccess || a.splits == 1) return e;
+    const dim3 mgrid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * a.B));
+    return a.d == 128 ? launch_kernel(prefix_attn_merge_kernel<uint16_t, 128>, mgrid, dim3(256), s, a)
+                      : launch_kernel(prefix_attn_merge_kernel<uint16_t, 64>, mgrid, dim3(256), s, a);
 }
 
 template <typename T, int D>
 static hipError_t prefix_f32_launch(const PrefixArgs& a, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * prefix_query_tiles(a.B) * a.splits));
-    hipLaunchKernelGGL((prefix_attn_f32_kernel<T, D>), grid, dim3(256), 0, s, a);
-    if (a.splits > 1) {
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        const dim3 mgrid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * a.B));
-        hipLaunchKernelGGL((prefix_attn_merge_kernel<T, D>), mgrid, dim3(256), 0, s, a);
-    }
-    return hipGetLastError();
+    const hipError_t e = launch_kernel(prefix_attn_f32_kernel<T, D>, grid, dim3(256), s, a);
+    if (e != hipSuccess || a.splits == 1) return e;
+    const dim3 mgrid(static_cast<uint32_t>(static_cast<int64_t>(a.R) * a.H * a.B));
+    return launch_kernel(prefix_attn_merge_kernel<T, D>, mgrid, dim3(256), s, a);
 }
 
 hipError_t launch_prefix_attention_generic(const PrefixArgs& a, hipStream_t s)

@@ -158,17 +158,32 @@ def test_shape_sweep(dev, io, d, fw, b):
     _full_check(case, dev)
 
 
-def test_feature_map(dev):
-    for io, d, fw in (("bf16", 128, 64), ("f32", 64, 32), ("bf16", 64, 128)):
-        case = synth.make_case("tiny", R=3, H=2, d=d, FW=fw, B=7, io=io, with_prefix=False)
+FEATURE_MAP = [
+    # (io, d, FW, R, B, strided): bf16 takes the matrix-core kernel (tiles of
+    # 32 d / 32 tokens of one head: one partial tile, several tiles with a
+    # ragged tail, token rows seen through a view of a fused tensor), fp32 the
+    # fp32-arithmetic kernel
+    ("bf16", 128, 64, 3, 7, False), ("f32", 64, 32, 3, 7, False), ("bf16", 64, 128, 3, 7, False),
+    ("bf16", 128, 128, 9, 33, False), ("bf16", 128, 32, 5, 64, True), ("bf16", 64, 64, 7, 19, True),
+    ("f32", 128, 128, 4, 9, True),
+]
+
+
+@pytest.mark.parametrize("io,d,fw,R,b,strided", FEATURE_MAP)
+def test_feature_map(dev, io, d, fw, R, b, strided):
+    case = synth.make_case("tiny", R=R, H=3, d=d, FW=fw, B=b, io=io, with_prefix=False)
+    if strided:
+        # x = q, a view of a fused [R][B][3][H][d] tensor
+        x = to_device(np.stack([case.q, case.k, case.v], axis=2), io, dev)[:, :, 0]
+    else:
         x = to_device(case.q, io, dev)
-        phi = to_host(bha.feature_map(x, to_device(case.w, io, dev)))
-        ref = np.empty_like(phi)
-        for h in range(case.H):
-            ref[:, :, h] = oracle.phi(case.q[:, :, h].reshape(-1, d), case.w[h]).reshape(3, 7, 2 * fw)
-        err = normwise_err(phi, ref, (3,))
-        _log(f"[feature_map] io={io} d={d} FW={fw} err {err:.2e}")
-        assert err <= 1e-5
+    phi = to_host(bha.feature_map(x, to_device(case.w, io, dev)))
+    ref = np.empty_like(phi)
+    for h in range(case.H):
+        ref[:, :, h] = oracle.phi(case.q[:, :, h].reshape(-1, d), case.w[h]).reshape(R, b, 2 * fw)
+    err = normwise_err(phi, ref, (3,))
+    _log(f"[feature_map] io={io} d={d} FW={fw} R={R} B={b} strided={strided} err {err:.2e}")
+    assert err <= 1e-5
 
 
 def test_strided_views_and_shared_map(dev):
@@ -733,3 +748,37 @@ def test_forward_gqa_matches_oracle(dev, io, d, fw, b, g):
         assert same
     else:
         assert e_mha <= TOL[io]
+
+
+@pytest.mark.parametrize("io,b", [("bf16", 32), ("bf16", 48), ("f32", 16)])
+def test_pending_hip_error_does_not_change_a_commit(dev, io, b):
+    # An error left pending on the thread by an unrelated HIP call (here an
+    # invalid hipSetDevice) must not decide what a library call does: one
+    # bha_state_commit after it returns BHA_OK and folds the block in exactly
+    # once -- bit-identical to the same commit with nothing pending. The HIP
+    # runtime's symbols are resolved through libbha.so's own dependencies, so
+    # the error is set in the runtime the library uses.
+    import ctypes
+
+    case = synth.make_case("tiny", R=4, H=2, d=128, FW=64, B=b, io=io, blocks=(1, 2), gamma="uniform")
+    run = Run(case, dev)
+    run.build_state()
+    k, v = to_device(case.k, io, dev), to_device(case.v, io, dev)
+    ref = run.state.clone()
+    bha.state_commit(k, v, run.w, ref, run.slots)
+    com = bha.prepare_commit(k, v, run.w, run.state, run.slots)
+    torch.cuda.synchronize()
+    hip = bha.load_library()
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    hip.hipSetDevice.restype = ctypes.c_int
+    hip.hipGetLastError.argtypes = []
+    hip.hipGetLastError.restype = ctypes.c_int
+    hip.hipGetLastError()
+    assert hip.hipSetDevice(1 << 20) != 0  # leaves hipErrorInvalidDevice pending
+    try:
+        com()  # raises BhaError unless the call returns BHA_OK
+    finally:
+        pending = hip.hipGetLastError()  # cleared before torch looks at it
+    torch.cuda.synchronize()
+    _log(f"[pending error] io={io} B={b}: commit returned BHA_OK with error {pending} pending before it")
+    assert torch.equal(run.state, ref)
