@@ -2,8 +2,10 @@
 
     python -m linear_attention_block_amd.build
 
-Every source under ``csrc/`` is compiled with hipcc for gfx950 only and linked
-into ``linear_attention_block_amd/libbha.so``. Packed fp32 instructions are
+The library's sources under ``csrc/`` are compiled with hipcc for gfx950 only
+and linked into ``linear_attention_block_amd/libbha.so``; the HBM streaming
+probe (``csrc/stream_probe.hip``, interface ``include/bha_probe.h``) is linked
+on its own into ``linear_attention_block_amd/libbha_probe.so``. Packed fp32 instructions are
 disabled on the device side (``-packed-fp32-ops``); hipcc's host pass warns that
 it does not know that feature, which is harmless.
 """
@@ -18,8 +20,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libbha.so")
+PROBE_OUT = os.path.join(HERE, "libbha_probe.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["bha_api.cpp", "bha_validate.cpp", "generic.hip", "mfma.hip", "softmax_attn.hip"]
+PROBE_SOURCES = ["stream_probe.hip"]
 
 
 def hipcc() -> str:
@@ -56,14 +60,19 @@ def build(verbose: bool = False) -> str:
             print("\n".join(msgs))
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = OUT + ".tmp%d" % os.getpid()
-    cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, OUT)
+    with cf.ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+
+    def link(objects, out):
+        tmp = out + ".tmp%d" % os.getpid()
+        cmd = [cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objects, "-o", tmp]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link of {os.path.basename(out)} failed:\n" + res.stdout + res.stderr)
+        os.replace(tmp, out)
+
+    link(objs[:len(SOURCES)], OUT)
+    link(objs[len(SOURCES):], PROBE_OUT)
     return OUT
 
 

@@ -312,3 +312,42 @@ def test_forward_gqa_validation(lib):
     assert fwd_gqa(lib, _dims(), num_slots=0) == DIMS
     assert fwd_gqa(lib, _dims(head_dim=96)) == UNSUP
     assert fwd_gqa(lib, _dims(), outs=bha_strides(0, 256, 128)) == STRIDE
+
+
+# ------------------------------------------------------------------ streaming probe library
+PROBE_HEADER = os.path.join(ROOT, "include", "bha_probe.h")
+
+
+def test_probe_library_exports_every_header_symbol():
+    from linear_attention_block_amd import probe
+
+    if not os.path.exists(probe.LIB_PATH):
+        pytest.skip("libbha_probe.so not built")
+    src = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    fns = sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(bha_probe_\w+)\s*\(", src, flags=re.M)))
+    assert fns == ["bha_probe_sink_floats", "bha_probe_stream", "bha_probe_trip_read_bytes",
+                   "bha_probe_trip_write_bytes"]
+    plib = probe.load_library()
+    for name in fns:
+        assert hasattr(plib, name), name
+
+
+def test_probe_rejects_bad_arguments_on_the_host():
+    from linear_attention_block_amd import probe
+
+    if not os.path.exists(probe.LIB_PATH):
+        pytest.skip("libbha_probe.so not built")
+    plib = probe.load_library()
+    good = probe.cfg(16, 1, 1, 2, 2)
+    assert plib.bha_probe_trip_read_bytes(ctypes.byref(good)) == 4 * 16 * 1024
+    assert plib.bha_probe_trip_write_bytes(ctypes.byref(good)) == 4 * 2 * 1024
+    P = ctypes.c_void_p
+    for bad in (probe.cfg(12, 1, 1, 2, 0), probe.cfg(16, 3, 1, 2, 0), probe.cfg(16, 1, 2, 2, 0),
+                probe.cfg(16, 1, 1, 0, 0), probe.cfg(16, 1, 1, 9, 0), probe.cfg(16, 1, 1, 2, 9)):
+        assert plib.bha_probe_trip_read_bytes(ctypes.byref(bad)) == -1
+        assert plib.bha_probe_stream(ctypes.byref(bad), P(FAKE), 1, P(FAKE), P(FAKE), None) == -1
+    assert plib.bha_probe_stream(None, P(FAKE), 1, P(FAKE), P(FAKE), None) == -1
+    assert plib.bha_probe_stream(ctypes.byref(good), None, 1, P(FAKE), P(FAKE), None) == -1
+    assert plib.bha_probe_stream(ctypes.byref(good), P(FAKE), 0, P(FAKE), P(FAKE), None) == -1
+    assert plib.bha_probe_stream(ctypes.byref(good), P(FAKE), 1, None, P(FAKE), None) == -1  # stores need dst
+    assert plib.bha_probe_stream(ctypes.byref(good), P(FAKE + 8), 1, P(FAKE), P(FAKE), None) == -1
