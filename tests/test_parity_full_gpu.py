@@ -4,8 +4,9 @@ The batch is the one bench.py times: every request's state is built on the GPU
 by chained commits of its whole prefix (drawn on the device), then one forward
 of the whole batch and one commit run in the same launch configuration. The
 oracle then checks, one pair at a time:
-  * sampled forward outputs, from the same fp32 state bytes the kernel read;
-  * the commit on sampled pairs, from the same pre-commit state;
+  * the forward output of every pair, from the same fp32 state bytes the
+    kernel read;
+  * the commit of every pair, from the same pre-commit state;
   * the chained GPU state of the shortest and longest requests against the
     oracle's state built from scratch over their whole prefix;
   * one ragged prefill launch over the same prefix tokens (packed): every pair
@@ -23,12 +24,13 @@ import torch
 import linear_attention_block_amd as bha
 import oracle
 import synth
-from helpers import normwise_err, record_to_plain, to_host
+from helpers import normwise_err, pairs, record_to_plain, to_host
 
 pytestmark = pytest.mark.gpu
 
 NTHREADS = min(16, os.cpu_count() or 1)
 TOL = 2e-2
+CHUNK = 256  # requests per oracle batch
 
 
 @pytest.fixture(scope="module")
@@ -69,7 +71,7 @@ def _check_prefix_attention(name, q, k, v, pk, pv, offs, y, track, seed, n_pairs
     assert err <= TOL
 
 
-def _run_full(name, dev, n_pairs=24, seed=0):
+def _run_full(name, dev, seed=0):
     case = synth.make_case(name, with_prefix=False, with_qkv=False)
     R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B
     F = 2 * FW
@@ -125,22 +127,23 @@ def _run_full(name, dev, n_pairs=24, seed=0):
           f"S err {e_fc[0]:.2e}, Z err {e_fc[1]:.2e}", flush=True)
     assert e_fc[0] <= 1e-5 and e_fc[1] <= 1e-5
 
+    # every (request, head) pair against the oracle, in chunks of requests:
+    # the forward from the same fp32 state bytes the kernel read, the commit
+    # from the same pre-commit state
     w64 = w.float().cpu().numpy().astype(np.float64)
     g64 = gamma.cpu().numpy().astype(np.float64)
-    rng = np.random.default_rng(seed)
-    rs = rng.integers(0, R, size=n_pairs)
-    hs = rng.integers(0, H, size=n_pairs)
-    qh, kh, vh, oh = (to_host(t) for t in (q, k, v, out))
     err_f = err_c = 0.0
-    for r, h in zip(rs, hs):
-        S, Z = record_to_plain(pre[r, h], d, F)
-        ref = oracle.block_forward(qh[r, :, h], kh[r, :, h], vh[r, :, h], w64[h], g64[h], S, Z)
-        err_f = max(err_f, normwise_err(oh[r, :, h], ref, None))
-        S2, Z2 = S.copy(), Z.copy()
-        oracle.state_commit(S2, Z2, kh[r, :, h], vh[r, :, h], w64[h])
-        Sg, Zg = record_to_plain(post[r, h], d, F)
-        err_c = max(err_c, normwise_err(Sg, S2, None), normwise_err(Zg, Z2, None))
-    print(f"[{name}] forward err {err_f:.2e}, commit err {err_c:.2e} over {n_pairs} sampled pairs", flush=True)
+    for r0 in range(0, R, CHUNK):
+        r1 = min(R, r0 + CHUNK)
+        qh, kh, vh = (pairs(to_host(t[r0:r1])) for t in (q, k, v))
+        S, Z = record_to_plain(pre[r0:r1], d, F)
+        S, Z = np.ascontiguousarray(S), np.ascontiguousarray(Z)
+        ref = oracle.block_forward_batch(qh, kh, vh, w64, g64, S, Z, nthreads=NTHREADS)
+        err_f = max(err_f, normwise_err(pairs(to_host(out[r0:r1])), ref, (2, 3)))
+        oracle.state_commit_batch(S, Z, kh, vh, w64, nthreads=NTHREADS)
+        Sg, Zg = record_to_plain(post[r0:r1], d, F)
+        err_c = max(err_c, normwise_err(Sg, S, (2, 3)), normwise_err(Zg, Z, (2,)))
+    print(f"[{name}] forward err {err_f:.2e}, commit err {err_c:.2e} over all {R * H} pairs", flush=True)
     assert err_f <= TOL and err_c <= TOL
 
     for r in track:
@@ -168,11 +171,16 @@ def test_decode256_full_size(dev):
     _run_full("decode256", dev)
 
 
+def test_long_context_16k_full_size(dev):
+    # 64 requests x 16 heads with 16,384-token prefixes
+    _run_full("longctx16k", dev)
+
+
 def test_long_context_32k_full_size(dev):
     # 64 requests x 16 heads with 32,768-token prefixes
-    _run_full("longctx32k", dev, n_pairs=16)
+    _run_full("longctx32k", dev)
 
 
 def test_wide2048_full_size(dev):
     # 2,048 requests x 16 heads, FW=128 (F=256), prefixes 512..4,096 tokens
-    _run_full("wide2048", dev, n_pairs=16)
+    _run_full("wide2048", dev)

@@ -1,0 +1,109 @@
+"""GPU parity of the persistent forward kernels at production grid sizes.
+
+The matrix-core forwards run a persistent grid of (resident work-groups per
+CU) x CUs work-groups, each taking pairs b, b + G, b + 2G, ... with the next
+pair's slot id, operands and state slice issued ahead of the current pair's
+arithmetic. A small batch gives every work-group one pair and never reaches
+that loop; these tests run 256 requests x 16 heads (4,096 pairs, or 512 to
+2,048 (request, K/V head) units), so every work-group takes several, and
+compare EVERY pair with the fp64 oracle computed from the same fp32 state
+bytes the kernel read. One request carries an out-of-range slot in the middle
+of the batch: its rows must come out NaN while the pairs around it, whose
+look-ahead loads run through it, stay exact.
+
+Covered: blocks of 48 and 64 tokens (two 32-token query tiles) at FW = 32, 64
+and 128; grouped K/V heads with 2, 4 and 8 query heads per K/V head.
+States: one ragged prefill over 0..4 blocks of 32 tokens per request (zero
+records included). Bar: normwise 2e-2 (bf16 I/O, fp32 accumulation).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_block_amd as bha
+import oracle
+import synth
+from helpers import normwise_err, pairs, record_to_plain, to_host
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = min(16, os.cpu_count() or 1)
+TOL = 2e-2
+R, H, D = 256, 16, 128
+BAD = 77  # request given an out-of-range slot
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU visible")
+    bha.load_library()
+    return torch.device("cuda:0")
+
+
+def _states(dev, fw, hk):
+    """Slots, W (hk heads), and states built by one ragged prefill."""
+    case = synth.make_case("decode256", with_prefix=False, with_qkv=False, FW=fw)
+    nb = np.random.default_rng(5).integers(0, 5, size=R)
+    w, _ = synth.device_layer_params("decode256", 0, dev, FW=fw, H=hk)
+    _, gamma = synth.device_layer_params("decode256", 0, dev, FW=fw, H=H)
+    slots = torch.from_numpy(case.slot_ids).to(dev)
+    state = bha.new_state(case.num_slots, hk, D, fw, dev)
+    pk, pv, offs = synth.device_packed_prefix("decode256", nb, dev, FW=fw, H=hk)
+    bha.state_prefill(pk, pv, offs, w, state, slots)
+    torch.cuda.synchronize()
+    bad = case.slot_ids.copy()
+    bad[BAD] = case.num_slots
+    return case, w, gamma, slots, torch.from_numpy(bad).to(dev), state
+
+
+def _check_all_pairs(y, q, k, v, w, gamma, state, slot_ids, g, fw, tag):
+    hk = H // g
+    rec = state.cpu().numpy()[slot_ids]  # [R][hk][rec]
+    S, Z = record_to_plain(rec, D, 2 * fw)
+    rep = lambda a: np.repeat(a, g, axis=1)  # noqa: E731  K/V head -> its query heads
+    kq = rep(pairs(to_host(k)))
+    vq = rep(pairs(to_host(v)))
+    ref = oracle.block_forward_batch(pairs(to_host(q)), kq, vq, np.repeat(to_host(w), g, axis=0),
+                                     gamma.cpu().numpy().astype(np.float64), rep(S), rep(Z), nthreads=NTHREADS)
+    yh = pairs(to_host(y))  # [R][H][B][d]
+    assert np.all(np.isnan(yh[BAD])), f"[{tag}] request with an out-of-range slot must be NaN"
+    good = np.ones(R, dtype=bool)
+    good[BAD] = False
+    assert np.all(np.isfinite(yh[good])), f"[{tag}] non-finite outputs outside the bad request"
+    err = normwise_err(yh[good], ref[good], (2, 3))
+    cus = torch.cuda.get_device_properties(y.device).multi_processor_count
+    print(f"[{tag}] {R * hk} units on a persistent grid over {cus} CUs: err {err:.2e} over all "
+          f"{int(good.sum()) * H} (request, query head) pairs", flush=True)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("fw,b", [(32, 48), (32, 64), (64, 48), (64, 64), (128, 48), (128, 64)])
+def test_two_tile_forward_every_pair(dev, fw, b):
+    case, w, gamma, _, slots_bad, state = _states(dev, fw, H)
+    q, k, v = synth.device_step_qkv("decode256", 0, R, dev, FW=fw, B=b)
+    y = bha.block_forward(q, k, v, w, gamma, state, slots_bad)
+    torch.cuda.synchronize()
+    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, fw, f"two-tile FW={fw} B={b}")
+
+
+@pytest.mark.parametrize("fw,hk", [(64, 8), (64, 4), (64, 2), (32, 4), (32, 2), (128, 8), (128, 4)])
+def test_grouped_forward_every_pair(dev, fw, hk):
+    g = H // hk
+    case, w, gamma, _, slots_bad, state = _states(dev, fw, hk)
+    q = synth.device_step_qkv("decode256", 0, R, dev, FW=fw)[0]
+    _, k, v = synth.device_step_qkv("decode256", 0, R, dev, FW=fw, H=hk)
+    y = bha.block_forward_gqa(q, k, v, w, gamma, state, slots_bad)
+    torch.cuda.synchronize()
+    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, g, fw, f"grouped FW={fw} G={g}")
+
+
+def test_one_tile_forward_every_pair(dev):
+    # the headline kernel (B = 32, FW = 64) at the decode256 grid, every pair
+    case, w, gamma, _, slots_bad, state = _states(dev, 64, H)
+    q, k, v = synth.device_step_qkv("decode256", 0, R, dev)
+    y = bha.block_forward(q, k, v, w, gamma, state, slots_bad)
+    torch.cuda.synchronize()
+    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, 64, "one-tile FW=64 B=32")
