@@ -39,6 +39,14 @@ if ROOT not in sys.path:
 
 METRIC = "active-block tokens/s through block-hybrid attn; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+# streaming-probe configurations reported as context (include/bha_probe.h):
+# 16-byte loads per lane per trip, trips in flight per wave, non-temporal
+# loads, work-groups per CU, KiB written per wave per trip
+PROBE_CONFIGS = (
+    ("read_only_forward_shape", dict(loads_per_lane=16, buffers=1, nontemporal=1, wgs_per_cu=2, store_kb_per_wave=0)),
+    ("read_only_deep", dict(loads_per_lane=32, buffers=1, nontemporal=0, wgs_per_cu=3, store_kb_per_wave=0)),
+    ("read_write_11_to_1", dict(loads_per_lane=32, buffers=1, nontemporal=1, wgs_per_cu=2, store_kb_per_wave=3)),
+)
 KERNEL_SOURCES = ("linear_attention_block_amd/csrc/mfma.hip", "linear_attention_block_amd/csrc/bha_device.hpp",
                   "linear_attention_block_amd/csrc/bha_internal.hpp",
                   "linear_attention_block_amd/csrc/bha_mfma.hpp")
@@ -129,7 +137,10 @@ def record_to_plain(rec, d, F):
 
 
 def cpu_baseline(layer, case, denoise, n_req, log):
-    """Time the fp64 oracle on one block cycle of the first n_req requests."""
+    """Time the fp64 oracle on one block cycle of the first n_req requests,
+    median of three runs, on the host's cores (at most 16 threads: the host
+    share of one GPU on the box), and the same cycle for n_req / 16 requests on
+    one thread."""
     import numpy as np
     import torch
 
@@ -137,7 +148,12 @@ def cpu_baseline(layer, case, denoise, n_req, log):
 
     R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B
     n_req = min(n_req, R)
-    nthreads = max(1, min(16, os.cpu_count() or 1))
+    host_cpus = os.cpu_count() or 1
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = host_cpus
+    nthreads = max(1, min(16, usable))
 
     def host(t):
         return np.ascontiguousarray(
@@ -158,22 +174,51 @@ def cpu_baseline(layer, case, denoise, n_req, log):
         oracle.state_commit_batch(S_, Z_, k[:n], v[:n], w, nthreads=threads)
         return time.perf_counter() - t0
 
-    dt = cycle(n_req, nthreads)
+    dts = [cycle(n_req, nthreads) for _ in range(3)]
+    dt = float(np.median(dts))
     n1 = max(1, n_req // 16)
-    dt1 = cycle(n1, 1)
-    log(f"cpu oracle: {n_req} requests x {H} heads, {denoise} forwards + 1 commit in {dt:.2f} s "
-        f"on {nthreads} threads; {n1} requests in {dt1:.2f} s on 1 thread")
+    dts1 = [cycle(n1, 1) for _ in range(3)]
+    dt1 = float(np.median(dts1))
+    log(f"cpu oracle: {n_req} requests x {H} heads, {denoise} forwards + 1 commit: median {dt:.2f} s of "
+        f"{', '.join(f'{x:.2f}' for x in dts)} on {nthreads} threads ({host_cpus} logical CPUs on the host, "
+        f"{usable} usable); {n1} requests on 1 thread: median {dt1:.2f} s")
     return {
         "value": denoise * n_req * B / dt,
         "unit": "tokens/s",
         "cores": nthreads,
+        "threads": nthreads,
+        "host_logical_cpus": host_cpus,
+        "usable_cpus": usable,
+        "thread_cap": "16 threads at most: the host CPU share of one GPU on the box",
         "kind": "oracle",
         "sample": (f"one block cycle ({denoise} forwards + 1 commit, one layer) of the first {n_req} "
-                   f"of {R} requests, all {H} heads, same workload and state; fp64 C oracle, "
-                   f"{dt:.2f} s wall"),
+                   f"of {R} requests, all {H} heads, same workload and state; fp64 C oracle; median of "
+                   f"3 runs ({', '.join(f'{x:.2f}' for x in dts)} s wall)"),
         "value_1thread": denoise * n1 * B / dt1,
-        "sample_1thread": f"the same cycle for the first {n1} requests on one thread, {dt1:.2f} s wall",
+        "sample_1thread": (f"the same cycle for the first {n1} requests on one thread, median of 3 runs "
+                           f"({', '.join(f'{x:.2f}' for x in dts1)} s wall)"),
     }
+
+
+def feature_map_bytes(R, H, d, FW, B, es=2):
+    """Algorithmic HBM bytes of one bha_feature_map launch: every token row read
+    (d elements), phi written (2 FW float32 per token and head), W once per head."""
+    return R * B * H * (d * es + 2 * FW * 4) + H * FW * d * es
+
+
+def probe_context(fwd_read, fwd_write, log):
+    """The HBM streaming probe (libbha_probe.so) at the forward's byte count:
+    read only, and the forward's read/write mix. Median of 10 launches each,
+    on rotating regions of the source so no launch finds its bytes cached."""
+    from linear_attention_block_amd import probe
+
+    out = {}
+    for tag, c in PROBE_CONFIGS:
+        cfg = probe.cfg(**c)
+        moved, t, gbps = probe.stream_gbps(cfg, fwd_read)
+        out[tag] = {"GBps": gbps, "frac": gbps / PEAK_HBM_GBS, "us": t * 1e6, "bytes": moved, "config": c}
+        log(f"probe {tag}: {moved / 1e6:.0f} MB in {t * 1e6:.1f} us = {gbps:.0f} GB/s ({gbps / PEAK_HBM_GBS:.1%})")
+    return out
 
 
 def gqa_cycle(args, log) -> dict:
@@ -623,6 +668,47 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"copy calibration: 3 x {args.copy_calibration_mib} MiB device copies")
 
+    # the standalone commit (bha_state_commit), on copies of the states: one
+    # event pair around 5 rounds over the layers (consecutive commits touch
+    # different layers' pools, as in the cycle)
+    com_ms = None
+    if not args.staggered:
+        snaps = [lay["state"].clone() for lay in layers]
+        coms = [bha.prepare_commit(lay["k"], lay["v"], lay["w"], st, slots) for lay, st in zip(layers, snaps)]
+        for c in coms:
+            c()
+        s0, s1 = ev_pair()
+        s0.record()
+        for _ in range(5):
+            for c in coms:
+                c()
+        s1.record()
+        torch.cuda.synchronize()
+        com_ms = s0.elapsed_time(s1) / (5 * len(coms))
+        del coms, snaps
+        torch.cuda.empty_cache()
+    scb = commit_bytes(R, H, d, FW, B, es)
+    if com_ms is not None:
+        log(f"standalone commit: avg {com_ms * 1e3:.1f} us/launch, {scb / com_ms / 1e6:.0f} GB/s algorithmic "
+            f"({scb / 1e6:.1f} MB/launch)")
+
+    # the feature map of each layer's queries (bha_feature_map), 5 rounds over the layers
+    phi_out = torch.empty((R, B, H, 2 * FW), dtype=torch.float32, device=dev)
+    fms = [bha.prepare_feature_map(lay["q"], lay["w"], phi_out) for lay in layers]
+    fms[0]()
+    f0, f1 = ev_pair()
+    f0.record()
+    for _ in range(5):
+        for fm in fms:
+            fm()
+    f1.record()
+    torch.cuda.synchronize()
+    fm_ms = f0.elapsed_time(f1) / (5 * len(fms))
+    fmb = feature_map_bytes(R, H, d, FW, B, es)
+    del phi_out, fms
+    log(f"feature map: avg {fm_ms * 1e3:.1f} us/launch, {fmb / fm_ms / 1e6:.0f} GB/s algorithmic "
+        f"({fmb / 1e6:.1f} MB/launch, {R * B * H} token-heads)")
+
     # context: a plain device-to-device copy of the forward's byte count (read + write)
     ctx_src = torch.empty(fb // 4, dtype=torch.float32, device=dev)
     ctx_dst = torch.empty_like(ctx_src)
@@ -648,6 +734,8 @@ def main() -> int:
     del ctx_src, ctx_dst, ctx_sum, ctx_rows
     log(f"context: torch device copy of {fb / 1e6:.0f} MB runs at {copy_gbps:.0f} GB/s (read + write); "
         f"row sums over the same bytes read at {read_gbps:.0f} GB/s")
+    out_bytes = R * B * H * d * es
+    probes = probe_context(fb - out_bytes, out_bytes, log)
 
     achieved = fb / fwd_avg / 1e9
     result = {
@@ -695,7 +783,9 @@ def main() -> int:
             "timing": "one event pair around each step's forwards; average over its launches, gaps included",
             "single_launch_us_p10_median_p90": [float(x) * 1e3 for x in np.percentile(fwd_ms, [10, 50, 90])],
         },
-        "context": {"torch_copy_GBps": copy_gbps, "torch_row_sum_read_GBps": read_gbps},
+        "context": {"torch_copy_GBps": copy_gbps, "torch_row_sum_read_GBps": read_gbps,
+                    "stream_probe": probes,
+                    "forward_over_probe": {k_: achieved / p_["GBps"] for k_, p_ in probes.items()}},
         "commit": None if args.staggered else {
             "kernel": ("bha_state_commit" if args.separate_commit
                        else "bha_block_forward_commit (last denoising step and commit, one pass)" if args.io == "bf16"
@@ -704,6 +794,24 @@ def main() -> int:
             "bytes_per_launch": cb,
             "achieved_GBps": cb / com_avg / 1e9,
             "frac": cb / com_avg / 1e9 / PEAK_HBM_GBS,
+        },
+        "standalone_commit": None if com_ms is None else {
+            "kernel": (f"bha_state_commit: commit_mfma_kernel<{d},{FW}>" if args.io == "bf16" and B <= 32
+                       else "bha_state_commit"),
+            "avg_launch_us": com_ms * 1e3,
+            "bytes_per_launch": scb,
+            "achieved_GBps": scb / com_ms / 1e6,
+            "frac": scb / com_ms / 1e6 / PEAK_HBM_GBS,
+            "committed_tokens_per_s": R * B / (com_ms * 1e-3),
+            "timing": "on copies of the states, one event pair around 5 rounds over the layers",
+        },
+        "feature_map": {
+            "kernel": (f"bha_feature_map: feature_map_mfma_kernel<{d},{FW}>" if args.io == "bf16"
+                       else "bha_feature_map: feature_map_generic_kernel<float>"),
+            "avg_launch_us": fm_ms * 1e3,
+            "bytes_per_launch": fmb,
+            "achieved_GBps": fmb / fm_ms / 1e6,
+            "frac": fmb / fm_ms / 1e6 / PEAK_HBM_GBS,
         },
         "prefill": {
             "workload": f"one bha_state_prefill launch per layer over all {R} requests' packed prefixes "
