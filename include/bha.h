@@ -85,7 +85,8 @@ typedef enum {
     BHA_ERR_ALIGN = -4,       /* pointer not aligned as stated above */
     BHA_ERR_STRIDE = -5,      /* negative or misaligned stride, rows overlapping */
     BHA_ERR_DTYPE = -6,       /* io_dtype not a bha_dtype value */
-    BHA_ERR_HIP = -7          /* the HIP runtime reported an error at launch */
+    BHA_ERR_HIP = -7,         /* the HIP runtime reported an error at launch */
+    BHA_ERR_SCRATCH = -8      /* more scratch than the static buffer of the allocation-free call */
 } bha_status;
 
 typedef enum { BHA_F32 = 0, BHA_BF16 = 1 } bha_dtype;
@@ -247,6 +248,33 @@ int bha_prefix_attention(const bha_dims* dims, const void* q, const void* k, con
 /* Workspace bytes bha_prefix_attention uses for these dims and total_tokens
  * (0: no split), or a negative bha_status for invalid arguments. */
 int64_t bha_prefix_attention_workspace(const bha_dims* dims, int64_t total_tokens);
+
+/*
+ * bha_prefix_attention_noalloc -- bha_prefix_attention for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Arguments, layouts and result are
+ * those of bha_prefix_attention with a full workspace (the same split, so the
+ * same output bit for bit), but the split's partial results go to a static
+ * device buffer of bha_prefix_attention_noalloc_scratch_bytes() bytes (9 MiB)
+ * that the library holds on every GPU it runs on until the process ends. The
+ * call allocates and frees nothing; its first call on a device looks the
+ * buffer's address up once (with that device current). It runs on the current
+ * device: `stream` must belong to it.
+ *   Errors: as bha_prefix_attention; a call whose split would need more than
+ *   the buffer returns BHA_ERR_SCRATCH and enqueues nothing (the split rule of
+ *   this version needs at most 8,486,400 bytes, so this is never returned).
+ *   Concurrency: every call on one GPU uses that GPU's one buffer, which keeps
+ *   the last call's contents (nothing in it needs to start at zero). Calls
+ *   that overlap in time on one GPU -- on other streams or from other threads
+ *   -- race on it; the caller must serialise them.
+ */
+int bha_prefix_attention_noalloc(const bha_dims* dims, const void* q, const void* k, const void* v,
+                                 const bha_strides* qkv, const void* kp, const void* vp, const bha_strides* kvp,
+                                 const int32_t* seq_offsets, int64_t total_tokens, void* out,
+                                 const bha_strides* outs, hipStream_t stream);
+
+/* Bytes of the static device buffer bha_prefix_attention_noalloc uses. */
+int64_t bha_prefix_attention_noalloc_scratch_bytes(void);
 
 /* Floats in one (slot, head) state record: (d + 1) * 2 * FW. Returns -1 for
  * unsupported sizes. Host only; touches no device. */

@@ -42,7 +42,8 @@ BHA_BF16 = 1
 # Every symbol include/bha.h declares.
 EXPORTED_SYMBOLS = (
     "bha_feature_map", "bha_block_forward", "bha_block_forward_gqa", "bha_block_forward_commit", "bha_state_commit", "bha_state_prefill",
-    "bha_prefix_attention", "bha_prefix_attention_workspace",
+    "bha_prefix_attention", "bha_prefix_attention_workspace", "bha_prefix_attention_noalloc",
+    "bha_prefix_attention_noalloc_scratch_bytes",
     "bha_state_record_floats", "bha_status_string", "bha_version",
 )
 
@@ -100,6 +101,10 @@ def load_library():
     lib.bha_prefix_attention.restype = ctypes.c_int
     lib.bha_prefix_attention_workspace.argtypes = [PD, I64]
     lib.bha_prefix_attention_workspace.restype = ctypes.c_int64
+    lib.bha_prefix_attention_noalloc.argtypes = [PD, P, P, P, PS, P, P, PS, P, I64, P, PS, P]
+    lib.bha_prefix_attention_noalloc.restype = ctypes.c_int
+    lib.bha_prefix_attention_noalloc_scratch_bytes.argtypes = []
+    lib.bha_prefix_attention_noalloc_scratch_bytes.restype = ctypes.c_int64
     lib.bha_state_record_floats.argtypes = [I32, I32]
     lib.bha_state_record_floats.restype = I64
     lib.bha_status_string.argtypes = [ctypes.c_int]
@@ -382,6 +387,9 @@ def state_prefill(k, v, seq_offsets, w, state, slot_ids, *, stream=None) -> None
         raise BhaError("bha_state_prefill", st)
 
 
+_NO_WORKSPACE = object()  # marshal a prefix-attention call without a workspace argument
+
+
 def _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream, workspace):
     qs = _tok_strides(q, "q")
     R, B, H, d = q.shape
@@ -407,16 +415,21 @@ def _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream, workspace):
     dims = bha_dims(R, H, d, 64, B, _io_dtype(q), float(scale))
     ps = bha_strides(0, kp.stride(0), kp.stride(1))
     T = kp.shape[0]
-    if workspace is None:
+    if workspace is _NO_WORKSPACE:
+        workspace = None
+        wptr, wbytes = None, 0
+    elif workspace is None:
         need = load_library().bha_prefix_attention_workspace(ctypes.byref(dims), T)
         if need < 0:
             raise BhaError("bha_prefix_attention_workspace", int(need))
         workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=q.device)
     elif workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor")
-    _check_device(q.device, workspace)
+    if workspace is not None:
+        _check_device(q.device, workspace)
+        wptr, wbytes = _ptr(workspace), workspace.numel()
     return (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(qs), _ptr(kp), _ptr(vp), ctypes.byref(ps),
-            _ptr(seq_offsets), T, _ptr(workspace), workspace.numel(), _ptr(out), ctypes.byref(os_),
+            _ptr(seq_offsets), T, wptr, wbytes, _ptr(out), ctypes.byref(os_),
             _stream(q.device, stream)), (dims, qs, ps, os_, workspace)
 
 
@@ -444,6 +457,24 @@ def prefix_attention(q, k, v, kp, vp, seq_offsets, *, out=None, scale: float = 0
     if st != 0:
         raise BhaError("bha_prefix_attention", st)
     return out
+
+
+def prefix_attention_noalloc(q, k, v, kp, vp, seq_offsets, *, out, scale: float = 0.0,
+                             stream=None) -> torch.Tensor:
+    """bha_prefix_attention_noalloc: the same attention as ``prefix_attention``
+    with a full workspace, its split partials kept in the library's static
+    device buffer; ``out`` must be given (nothing is allocated)."""
+    lib = load_library()
+    args, _keep = _prefix_args(q, k, v, kp, vp, seq_offsets, out, scale, stream, _NO_WORKSPACE)
+    # the same arguments without the workspace pointer and size
+    st = lib.bha_prefix_attention_noalloc(*args[:10], *args[12:])
+    if st != 0:
+        raise BhaError("bha_prefix_attention_noalloc", st)
+    return out
+
+
+def prefix_attention_noalloc_scratch_bytes() -> int:
+    return int(load_library().bha_prefix_attention_noalloc_scratch_bytes())
 
 
 class _Prepared:

@@ -214,14 +214,13 @@ extern "C" int64_t bha_prefix_attention_workspace(const bha_dims* dims, int64_t 
                                                                 dims->block_size, dims->io_dtype, total_tokens));
 }
 
-extern "C" int bha_prefix_attention(const bha_dims* dims, const void* q, const void* k, const void* v,
-                                    const bha_strides* qkv, const void* kp, const void* vp, const bha_strides* kvp,
-                                    const int32_t* seq_offsets, int64_t total_tokens, void* workspace,
-                                    int64_t workspace_bytes, void* out, const bha_strides* outs, hipStream_t stream)
+// Validation and marshalling shared by the two prefix-attention entry points;
+// fills everything but the split and its partial-result buffer.
+static int prefix_prepare(const bha_dims* dims, const void* q, const void* k, const void* v, const bha_strides* qkv,
+                          const void* kp, const void* vp, const bha_strides* kvp, const int32_t* seq_offsets,
+                          int64_t total_tokens, void* out, const bha_strides* outs, PrefixArgs& a)
 {
-    int st = validate_dims(dims);
-    if (st != BHA_OK) return st;
-    if (dims->num_requests == 0) return BHA_OK;
+    int st;
     if ((st = validate_tokens(q, qkv, dims, false)) != BHA_OK) return st;
     if ((st = validate_tokens(k, qkv, dims, false)) != BHA_OK) return st;
     if ((st = validate_tokens(v, qkv, dims, false)) != BHA_OK) return st;
@@ -244,6 +243,33 @@ extern "C" int bha_prefix_attention(const bha_dims* dims, const void* q, const v
         ps.tok = qkv->tok;
         ps.head = qkv->head;
     }
+    a.part = nullptr;
+    a.splits = 1;
+    a.R = dims->num_requests; a.H = dims->num_heads; a.d = dims->head_dim;
+    a.B = dims->block_size; a.io = dims->io_dtype;
+    a.scale = dims->scale > 0.0f ? dims->scale : 1.0f / sqrtf((float)dims->head_dim);
+    a.q = q; a.k = k; a.v = v; a.qs = *qkv; a.kp = kp; a.vp = vp; a.ps = ps;
+    a.seq_offsets = seq_offsets; a.total_tokens = total_tokens; a.out = out; a.os = *outs;
+    return BHA_OK;
+}
+
+static hipError_t launch_prefix_any(const PrefixArgs& a, hipStream_t stream)
+{
+    return prefix_attention_mfma_supported(a) ? launch_prefix_attention_mfma(a, stream)
+                                              : launch_prefix_attention_generic(a, stream);
+}
+
+extern "C" int bha_prefix_attention(const bha_dims* dims, const void* q, const void* k, const void* v,
+                                    const bha_strides* qkv, const void* kp, const void* vp, const bha_strides* kvp,
+                                    const int32_t* seq_offsets, int64_t total_tokens, void* workspace,
+                                    int64_t workspace_bytes, void* out, const bha_strides* outs, hipStream_t stream)
+{
+    int st = validate_dims(dims);
+    if (st != BHA_OK) return st;
+    if (dims->num_requests == 0) return BHA_OK;
+    PrefixArgs a;
+    if ((st = prefix_prepare(dims, q, k, v, qkv, kp, vp, kvp, seq_offsets, total_tokens, out, outs, a)) != BHA_OK)
+        return st;
     if (workspace_bytes < 0) return BHA_ERR_DIMS;
     if (workspace && reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return BHA_ERR_ALIGN;
     // the split the workspace allows (fewer splits, down to none, when it is short)
@@ -253,17 +279,35 @@ extern "C" int bha_prefix_attention(const bha_dims* dims, const void* q, const v
     const int64_t fit = workspace ? workspace_bytes / per_split : 0;
     if (splits > fit) splits = static_cast<int>(fit);
     if (splits < 2) splits = 1;
-    PrefixArgs a;
     a.part = splits > 1 ? static_cast<float*>(workspace) : nullptr;
     a.splits = splits;
-    a.R = dims->num_requests; a.H = dims->num_heads; a.d = dims->head_dim;
-    a.B = dims->block_size; a.io = dims->io_dtype;
-    a.scale = dims->scale > 0.0f ? dims->scale : 1.0f / sqrtf((float)dims->head_dim);
-    a.q = q; a.k = k; a.v = v; a.qs = *qkv; a.kp = kp; a.vp = vp; a.ps = ps;
-    a.seq_offsets = seq_offsets; a.total_tokens = total_tokens; a.out = out; a.os = *outs;
-    return launch_status(prefix_attention_mfma_supported(a) ? launch_prefix_attention_mfma(a, stream)
-                                                            : launch_prefix_attention_generic(a, stream));
+    return launch_status(launch_prefix_any(a, stream));
 }
+
+extern "C" int bha_prefix_attention_noalloc(const bha_dims* dims, const void* q, const void* k, const void* v,
+                                            const bha_strides* qkv, const void* kp, const void* vp,
+                                            const bha_strides* kvp, const int32_t* seq_offsets,
+                                            int64_t total_tokens, void* out, const bha_strides* outs,
+                                            hipStream_t stream)
+{
+    int st = validate_dims(dims);
+    if (st != BHA_OK) return st;
+    if (dims->num_requests == 0) return BHA_OK;
+    PrefixArgs a;
+    if ((st = prefix_prepare(dims, q, k, v, qkv, kp, vp, kvp, seq_offsets, total_tokens, out, outs, a)) != BHA_OK)
+        return st;
+    // the split bha_prefix_attention takes with a full workspace
+    const int splits = prefix_attention_splits(dims->num_requests, dims->num_heads, dims->head_dim,
+                                               dims->block_size, dims->io_dtype, total_tokens);
+    if (prefix_workspace_bytes(dims, splits) > kNoAllocScratchBytes) return BHA_ERR_SCRATCH;
+    void* scratch_ptr = nullptr;
+    if (noalloc_scratch(&scratch_ptr) != hipSuccess) return BHA_ERR_HIP;
+    a.part = splits > 1 ? static_cast<float*>(scratch_ptr) : nullptr;
+    a.splits = splits;
+    return launch_status(launch_prefix_any(a, stream));
+}
+
+extern "C" int64_t bha_prefix_attention_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 extern "C" int64_t bha_state_record_floats(int32_t head_dim, int32_t feat_half)
 {
@@ -283,6 +327,8 @@ extern "C" const char* bha_status_string(int status)
         case BHA_ERR_STRIDE: return "BHA_ERR_STRIDE: negative, misaligned or overlapping stride";
         case BHA_ERR_DTYPE: return "BHA_ERR_DTYPE: io_dtype is not a bha_dtype value";
         case BHA_ERR_HIP: return "BHA_ERR_HIP: the HIP runtime reported an error";
+        case BHA_ERR_SCRATCH:
+            return "BHA_ERR_SCRATCH: the call needs more scratch than the library's static device buffer";
         default: return "unknown bha_status";
     }
 }

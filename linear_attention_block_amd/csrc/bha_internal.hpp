@@ -205,6 +205,12 @@ struct PrefixArgs {
 // unnormalised output [32][d], then the running maximum and normaliser [32] each.
 __host__ __device__ inline int64_t prefix_part_floats(int d) { return 32 * static_cast<int64_t>(d) + 64; }
 
+// Bytes of the static buffer the allocation-free prefix attention keeps its
+// split partials in, and its address on the current device (looked up once
+// per device).
+constexpr int64_t kNoAllocScratchBytes = int64_t(9) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Key-sequence splits the matrix-core prefix attention uses for these sizes
 // (1 when the pairs alone fill the GPU or the path does not apply).
 int prefix_attention_splits(int R, int H, int d, int B, int io, int64_t total_tokens);

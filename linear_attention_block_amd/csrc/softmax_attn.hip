@@ -30,6 +30,8 @@
 //
 // fp32 path (float32 I/O, and bf16 with token strides too large for the
 // kernel above): the same layout and split on the fp32 matrix cores.
+#include <mutex>
+
 #include "bha_device.hpp"
 #include "bha_internal.hpp"
 #include "bha_mfma.hpp"
@@ -532,6 +534,39 @@ constexpr int64_t kSplitTargetWgs = 256;
 constexpr int64_t kSplitMinChunks = 16;
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Allocation-free split partials (bha_prefix_attention_noalloc)
+// ---------------------------------------------------------------------------
+// For callers that cannot allocate, the split's partial records go to this
+// static buffer instead of a caller workspace. Its size covers the largest
+// split prefix_attention_splits picks: a split happens only for fewer than
+// kSplitTargetWgs (request, head, query tile) units, each split at most
+// ceil(kSplitTargetWgs / units) ways, so at most 2 kSplitTargetWgs - 2 = 510
+// records of prefix_part_floats(128) floats (16,640 bytes): 8,486,400 bytes.
+// Each GPU the library runs on holds its own copy until the process ends.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+static_assert((2 * kSplitTargetWgs - 2) * 4 * (32 * 128 + 64) <= kNoAllocScratchBytes,
+              "the largest split fits the static buffer");
+
+// This device's address of `scratch`, looked up with hipGetSymbolAddress on
+// the first call on each device (with that device current) and kept; in host
+// code the array's own name is not a device address.
+hipError_t noalloc_scratch(void** ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static void* addr[kMaxDevices];
+    static hipError_t err[kMaxDevices];
+    static std::once_flag once[kMaxDevices];
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(once[dev], [dev] { err[dev] = hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(scratch)); });
+    if (err[dev] != hipSuccess) return err[dev];
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 int prefix_query_tiles(int B) { return (B + 31) / 32; }
 
