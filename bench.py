@@ -234,7 +234,7 @@ def gqa_cycle(args, log) -> dict:
     import synth
 
     dev = torch.device("cuda:0")
-    case = synth.make_case(args.config, with_prefix=False, with_qkv=False)
+    case = synth.make_case(args.config, R=args.requests or None, with_prefix=False, with_qkv=False)
     R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B
     HK = args.kv_heads
     if HK < 1 or H % HK:
@@ -452,6 +452,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="decode256",
                     choices=["decode256", "b16", "longctx2k", "longctx16k", "longctx32k", "wide2048"])
+    ap.add_argument("--requests", type=int, default=0,
+                    help="override the workload's request count (the first R requests of its seeded draw)")
     ap.add_argument("--layers", type=int, default=6, help="block-hybrid layer instances (default 6)")
     ap.add_argument("--denoise", type=int, default=32, help="denoising forwards per block")
     ap.add_argument("--cpu-sample-requests", type=int, default=256)
@@ -512,7 +514,7 @@ def main() -> int:
         return 0
     io = dict(io=args.io)  # every draw in the chosen token dtype (bf16 values, widened for f32)
     es = 2 if args.io == "bf16" else 4
-    case = synth.make_case(args.config, with_prefix=False, with_qkv=False, **io)
+    case = synth.make_case(args.config, R=args.requests or None, with_prefix=False, with_qkv=False, **io)
     R, H, d, FW, B = case.R, case.H, case.d, case.FW, case.B
     nl, nd = args.layers, args.denoise
     slots = torch.from_numpy(case.slot_ids).to(dev)
@@ -768,7 +770,8 @@ def main() -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
-            "traffic": None if args.staggered or args.io != "bf16" else read_traffic(args.config),
+            "traffic": (None if args.staggered or args.io != "bf16" or args.requests
+                        else read_traffic(args.config)),
             "kernel": ((f"bha_block_forward_commit: forward_commit_mfma_kernel<{d},{FW}> (1/{nd} of requests "
                         f"commit per launch)" if args.io == "bf16" else
                         f"bha_block_forward_commit: forward_generic_kernel<float,{d},{FW}> then "

@@ -1030,6 +1030,13 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
     float* rec = a.state + (static_cast<int64_t>(slot) * a.H + h) * static_cast<int64_t>(D + 1) * F;
     f32x4 sv[C::NSL];
     load_state_slice(rec + wv * F * 32, lane, sv);
+    // Z goes out with the slice (thread tid holds Z[tid + j NT]), so the
+    // work-group ends with stores only, not a dependent read of Z after the
+    // products
+    constexpr int ZPT = (F + C::NT - 1) / C::NT;
+    float zold[ZPT];
+#pragma unroll
+    for (int j = 0; j < ZPT; ++j) zold[j] = tid + j * C::NT < F ? rec[D * F + tid + j * C::NT] : 0.0f;
     kc.template store_rows<C::RS>(Ks, tid);
     vc.template store_transposed<C::VS>(Vt, tid);
     wc.template store_rows<C::RS>(Ws, tid);
@@ -1091,11 +1098,15 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
     for (int t = 0; t < C::NSL; ++t) __builtin_nontemporal_store(sv[t], dst + t * 64);
 
     // dZ = sum_t phi(k_t), fp32 from the LDS copy
-    for (int f = tid; f < F; f += C::NT) {
-        float z = 0.0f;
 #pragma unroll
-        for (int t = 0; t < 32; ++t) z += Pt[f * C::PS + t];
-        rec[D * F + f] += z;
+    for (int j = 0; j < ZPT; ++j) {
+        const int f = tid + j * C::NT;
+        if (f < F) {
+            float z = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 32; ++t) z += Pt[f * C::PS + t];
+            rec[D * F + f] = zold[j] + z;
+        }
     }
 }
 
@@ -1705,10 +1716,13 @@ void prefill_mfma_kernel(CommitArgs a)
 // One work-group of D/32 waves per (head, 32 D/32 consecutive tokens of the
 // [R][B] batch). W_h and the tokens' rows go to LDS; each wave then takes 32
 // tokens: u^T = W^T X^T on the matrix cores (lane = token, as in the
-// forward), both softmaxes of each token in fp32 (lanes n and n + 32 hold
-// halves of token n's logits), and phi stored in fp32 straight from the
-// accumulator registers: 16 bytes per lane, lanes n and n + 32 writing 32
-// contiguous bytes of token n's row, every row whole after FW / 8 stores.
+// forward) and both softmaxes of each token in fp32 (lanes n and n + 32 hold
+// halves of token n's logits). phi leaves through the wave's own 32 rows of
+// the X tile, which the logits no longer need: a piece of CW features of
+// every token at a time is written there from the accumulator layout and read
+// back row by row, so each store instruction writes whole CW * 4-byte runs of
+// phi rows (the accumulator layout writes 32-byte pieces of 32 rows per
+// instruction; measured at 256 x 32 tokens x 16 heads, FW = 64: 40.7 us).
 // Roofline: HBM. Algorithmic bytes per (token, head): the row read (2 d) and
 // phi written (4 F); W once per head per launch.
 template <int D, int FW>
@@ -1716,6 +1730,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void feature_map_mfma_kernel(PhiArgs
 {
     using C = Cfg<D, FW>;
     constexpr int NT = C::NT, TOK = 32 * C::NW, CH = D / 8, F = C::F;
+    // features per staged piece (32 rows x CW floats fit the wave's 32 X rows)
+    constexpr int CW = (D == 128 ? 64 : 32) < FW ? (D == 128 ? 64 : 32) : FW;
+    constexpr int CS = CW + 4;              // padded LDS row (floats) of a staged piece
+    static_assert(32 * CS * 4 <= 32 * C::RS * 2, "a staged piece fits the wave's X rows");
     __shared__ alignas(16) uint16_t Ws[FW * C::RS];
     __shared__ alignas(16) uint16_t Xs[TOK * C::RS];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ln = lane & 31, g = lane >> 5;
@@ -1769,23 +1787,33 @@ __global__ __launch_bounds__(64 * (D / 32)) void feature_map_mfma_kernel(PhiArgs
     sp += __shfl_xor(sp, 32, 64);
     sn += __shfl_xor(sn, 32, 64);
     const float ip = 1.0f / sp, in = 1.0f / sn;
-    const int64_t tk = t0 + 32 * wv + ln;
-    if (tk >= ntok) return;
-    float* const out = a.phi + (tk * a.H + h) * F;
+    float* const stage = reinterpret_cast<float*>(Xs + 32 * wv * C::RS);  // this wave's X rows
+    const int64_t tw = t0 + 32 * wv;  // the wave's first token
+    // piece (half hf, features c0 .. c0 + CW - 1 of that half)
 #pragma unroll
-    for (int T = 0; T < FW / 32; ++T)
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            // features 32 T + 8 q4 + 4 g .. + 3 of each half
-            const int f0 = 32 * T + 8 * q4 + 4 * g;
-            f32x4 pv, nv;
+        for (int c0 = 0; c0 < FW; c0 += CW) {
+            __syncthreads();  // the previous piece's reads (or the logits' reads of X) are done
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                pv[e] = u[T][4 * q4 + e] * ip;
-                nv[e] = en[T][4 * q4 + e] * in;
+            for (int T = c0 / 32; T < (c0 + CW) / 32; ++T)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    f32x4 pv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pv[e] = hf ? en[T][4 * q4 + e] * in : u[T][4 * q4 + e] * ip;
+                    *reinterpret_cast<f32x4*>(stage + ln * CS + 32 * T - c0 + 8 * q4 + 4 * g) = pv;
+                }
+            __syncthreads();
+            // rows of CW floats, CW / 4 lanes per row
+#pragma unroll
+            for (int i = 0; i < 32 * CW / 4 / 64; ++i) {
+                const int idx = lane + 64 * i, row = idx / (CW / 4), c4 = idx % (CW / 4);
+                const int64_t tk = tw + row;
+                if (tk < ntok)
+                    *reinterpret_cast<f32x4*>(a.phi + (tk * a.H + h) * F + hf * FW + c0 + 4 * c4) =
+                        *reinterpret_cast<const f32x4*>(stage + row * CS + 4 * c4);
             }
-            *reinterpret_cast<f32x4*>(out + f0) = pv;
-            *reinterpret_cast<f32x4*>(out + FW + f0) = nv;
         }
 }
 
@@ -1805,12 +1833,23 @@ static int compute_units()
 
 // Persistent grid: as many work-groups as can be resident (WPE per CU),
 // rounded down to a multiple of H so that each keeps one head, and no more
-// than there are pairs.
+// than there are pairs. With at least kFwdOneGroupPairs pairs per CU the
+// one-tile forward runs one work-group per CU instead of two: the memory
+// system streams more with half the state slices in flight (measured at
+// d = 128, FW = 64, B = 32, six rotating state pools: 512 requests x 16 heads
+// 151.3 -> 141.2 us, 1,024 requests 295.1 -> 276.9 us), while below that the
+// one work-group's first and last pairs cost more than they save (256
+// requests: 77.8 -> 79.5 us).
+constexpr int kFwdOneGroupPairs = 32;
+
 template <int D, int FW, int KT>
 static hipError_t launch_forward_kt(const ForwardArgs& a, hipStream_t s)
 {
     const int npairs = a.R * a.H;
-    int64_t NG = static_cast<int64_t>(compute_units()) * fwd_wpe<D, FW, KT>();
+    const int cus = compute_units();
+    int wpe = fwd_wpe<D, FW, KT>();
+    if (KT == 1 && wpe == 2 && npairs >= static_cast<int64_t>(kFwdOneGroupPairs) * cus) wpe = 1;
+    int64_t NG = static_cast<int64_t>(cus) * wpe;
     NG = (NG / a.H) * a.H;
     if (NG < a.H) NG = a.H;
     if (NG > npairs) NG = npairs;

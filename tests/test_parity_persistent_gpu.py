@@ -43,9 +43,9 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _states(dev, fw, hk):
+def _states(dev, fw, hk, R=R):
     """Slots, W (hk heads), and states built by one ragged prefill."""
-    case = synth.make_case("decode256", with_prefix=False, with_qkv=False, FW=fw)
+    case = synth.make_case("decode256", R=R, with_prefix=False, with_qkv=False, FW=fw)
     nb = np.random.default_rng(5).integers(0, 5, size=R)
     w, _ = synth.device_layer_params("decode256", 0, dev, FW=fw, H=hk)
     _, gamma = synth.device_layer_params("decode256", 0, dev, FW=fw, H=H)
@@ -61,6 +61,7 @@ def _states(dev, fw, hk):
 
 def _check_all_pairs(y, q, k, v, w, gamma, state, slot_ids, g, fw, tag):
     hk = H // g
+    R = q.shape[0]
     rec = state.cpu().numpy()[slot_ids]  # [R][hk][rec]
     S, Z = record_to_plain(rec, D, 2 * fw)
     rep = lambda a: np.repeat(a, g, axis=1)  # noqa: E731  K/V head -> its query heads
@@ -100,10 +101,13 @@ def test_grouped_forward_every_pair(dev, fw, hk):
     _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, g, fw, f"grouped FW={fw} G={g}")
 
 
-def test_one_tile_forward_every_pair(dev):
-    # the headline kernel (B = 32, FW = 64) at the decode256 grid, every pair
-    case, w, gamma, _, slots_bad, state = _states(dev, 64, H)
-    q, k, v = synth.device_step_qkv("decode256", 0, R, dev)
+@pytest.mark.parametrize("nreq", [256, 512])
+def test_one_tile_forward_every_pair(dev, nreq):
+    # the headline kernel (B = 32, FW = 64) at the decode256 grid (two
+    # work-groups per CU, 8 pairs each), and at 512 requests (8,192 pairs: one
+    # work-group per CU, 32 pairs each), every pair
+    case, w, gamma, _, slots_bad, state = _states(dev, 64, H, R=nreq)
+    q, k, v = synth.device_step_qkv("decode256", 0, nreq, dev)
     y = bha.block_forward(q, k, v, w, gamma, state, slots_bad)
     torch.cuda.synchronize()
-    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, 64, "one-tile FW=64 B=32")
+    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, 64, f"one-tile FW=64 B=32 R={nreq}")
