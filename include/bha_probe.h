@@ -40,6 +40,15 @@ typedef struct {
     int32_t nontemporal;       /* 0: plain loads, 1: non-temporal loads */
     int32_t wgs_per_cu;        /* resident work-groups per compute unit, 1..8 */
     int32_t store_kb_per_wave; /* KiB each wave writes per trip, 0..8 (0: read only) */
+    int32_t store_mode;        /* when a trip's share is written:
+                                  0: plain stores right after the trip's slice is summed
+                                  1: non-temporal stores right after the trip
+                                  2: plain stores of all the work-group's trips after its
+                                     last read (writes gathered at the end of the launch)
+                                  3: plain stores of the last four trips' shares together,
+                                     every fourth trip
+                                  4: the first half of the work-group's trips as in mode 0,
+                                     the second half after its last read */
 } bha_probe_cfg;
 
 /* Bytes one trip reads from src and writes to dst (negative: invalid cfg). */

@@ -36,15 +36,21 @@ __device__ __forceinline__ f32x4 consume(const f32x4 (&b)[NSL], f32x4 acc)
     return acc;
 }
 
+// trip's share of dst: wkb KiB per wave
+template <bool NTS>
 __device__ __forceinline__ void write_share(f32x4* dst, int64_t trip, int wkb, int wv, int lane, f32x4 acc)
 {
     f32x4* p = dst + (trip * kWaves + wv) * (static_cast<int64_t>(wkb) * 64) + lane;
-    for (int i = 0; i < wkb; ++i) p[i * 64] = acc;
+    for (int i = 0; i < wkb; ++i) {
+        if constexpr (NTS) __builtin_nontemporal_store(acc, p + i * 64);
+        else p[i * 64] = acc;
+    }
 }
 
 // Work-group b takes trips b, b + G, ...; each wave keeps NBUF trips' slices
-// in flight and issues the next one as soon as a slice has been summed.
-template <int NSL, int NBUF, bool NT>
+// in flight and issues the next one as soon as a slice has been summed. SM:
+// the store mode of include/bha_probe.h.
+template <int NSL, int NBUF, bool NT, int SM>
 __global__ __launch_bounds__(kThreads) void stream_probe_kernel(const f32x4* src, int64_t trips, f32x4* dst, int wkb,
                                                                 float* sink)
 {
@@ -56,18 +62,31 @@ __global__ __launch_bounds__(kThreads) void stream_probe_kernel(const f32x4* src
     for (int j = 0; j < NBUF; ++j) load_slice<NSL, NT>(src, t + j * G, trips, wv, lane, buf[j]);
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     bool more = t < trips;
+    int done = 0;  // trips of this work-group summed so far
+    const int64_t per_wg = (trips - blockIdx.x + G - 1) / G;
     while (more) {
 #pragma unroll
         for (int j = 0; j < NBUF; ++j) {
             if (more) {
                 acc = consume<NSL>(buf[j], acc);
                 load_slice<NSL, NT>(src, t + NBUF * G, trips, wv, lane, buf[j]);
-                if (wkb > 0) write_share(dst, t, wkb, wv, lane, acc);
+                ++done;
+                if (wkb > 0 && (SM <= 1 || (SM == 4 && 2 * done <= per_wg)))
+                    write_share<SM == 1>(dst, t, wkb, wv, lane, acc);
                 t += G;
                 more = t < trips;
+                if (wkb > 0 && SM == 3 && (done % 4 == 0 || !more)) {
+                    // the shares of the last (up to) four trips
+                    const int n = done % 4 == 0 ? 4 : done % 4;
+                    for (int i = 1; i <= n; ++i) write_share<false>(dst, t - i * G, wkb, wv, lane, acc);
+                }
             }
         }
     }
+    if (wkb > 0 && SM == 2)
+        for (int64_t u = blockIdx.x; u < trips; u += G) write_share<false>(dst, u, wkb, wv, lane, acc);
+    if (wkb > 0 && SM == 4)
+        for (int64_t j = per_wg / 2; j < per_wg; ++j) write_share<false>(dst, blockIdx.x + j * G, wkb, wv, lane, acc);
     const float s = acc[0] + acc[1] + acc[2] + acc[3];
     if (s == kSentinel) sink[static_cast<int64_t>(blockIdx.x) * kThreads + tid] = s;
 }
@@ -76,7 +95,8 @@ bool valid(const bha_probe_cfg* c)
 {
     return c && (c->loads_per_lane == 8 || c->loads_per_lane == 16 || c->loads_per_lane == 32) &&
            (c->buffers == 1 || c->buffers == 2) && (c->nontemporal == 0 || c->nontemporal == 1) &&
-           c->wgs_per_cu >= 1 && c->wgs_per_cu <= 8 && c->store_kb_per_wave >= 0 && c->store_kb_per_wave <= 8;
+           c->wgs_per_cu >= 1 && c->wgs_per_cu <= 8 && c->store_kb_per_wave >= 0 && c->store_kb_per_wave <= 8 &&
+           c->store_mode >= 0 && c->store_mode <= 4;
 }
 
 int compute_units()
@@ -87,24 +107,37 @@ int compute_units()
     return n;
 }
 
-template <int NSL, int NBUF, bool NT>
+template <int NSL, int NBUF, bool NT, int SM>
 hipError_t launch(dim3 grid, hipStream_t s, const f32x4* src, int64_t trips, f32x4* dst, int wkb, float* sink)
 {
     void* argv[] = {&src, &trips, &dst, &wkb, &sink};
-    return hipLaunchKernel(reinterpret_cast<const void*>(stream_probe_kernel<NSL, NBUF, NT>), grid, dim3(kThreads),
-                           argv, 0, s);
+    return hipLaunchKernel(reinterpret_cast<const void*>(stream_probe_kernel<NSL, NBUF, NT, SM>), grid,
+                           dim3(kThreads), argv, 0, s);
+}
+
+template <int NSL, int NBUF, bool NT>
+hipError_t launch_sm(const bha_probe_cfg* c, dim3 grid, hipStream_t s, const f32x4* src, int64_t trips, f32x4* dst,
+                     float* sink)
+{
+    const int w = c->store_kb_per_wave;
+    switch (c->store_mode) {
+        case 0: return launch<NSL, NBUF, NT, 0>(grid, s, src, trips, dst, w, sink);
+        case 1: return launch<NSL, NBUF, NT, 1>(grid, s, src, trips, dst, w, sink);
+        case 2: return launch<NSL, NBUF, NT, 2>(grid, s, src, trips, dst, w, sink);
+        case 3: return launch<NSL, NBUF, NT, 3>(grid, s, src, trips, dst, w, sink);
+        default: return launch<NSL, NBUF, NT, 4>(grid, s, src, trips, dst, w, sink);
+    }
 }
 
 template <int NSL>
 hipError_t launch_nsl(const bha_probe_cfg* c, dim3 grid, hipStream_t s, const f32x4* src, int64_t trips, f32x4* dst,
                       float* sink)
 {
-    const int w = c->store_kb_per_wave;
     if (c->buffers == 1)
-        return c->nontemporal ? launch<NSL, 1, true>(grid, s, src, trips, dst, w, sink)
-                              : launch<NSL, 1, false>(grid, s, src, trips, dst, w, sink);
-    return c->nontemporal ? launch<NSL, 2, true>(grid, s, src, trips, dst, w, sink)
-                          : launch<NSL, 2, false>(grid, s, src, trips, dst, w, sink);
+        return c->nontemporal ? launch_sm<NSL, 1, true>(c, grid, s, src, trips, dst, sink)
+                              : launch_sm<NSL, 1, false>(c, grid, s, src, trips, dst, sink);
+    return c->nontemporal ? launch_sm<NSL, 2, true>(c, grid, s, src, trips, dst, sink)
+                          : launch_sm<NSL, 2, false>(c, grid, s, src, trips, dst, sink);
 }
 
 }  // namespace

@@ -17,7 +17,7 @@ _lib = None
 
 class bha_probe_cfg(ctypes.Structure):
     _fields_ = [("loads_per_lane", ctypes.c_int32), ("buffers", ctypes.c_int32), ("nontemporal", ctypes.c_int32),
-                ("wgs_per_cu", ctypes.c_int32), ("store_kb_per_wave", ctypes.c_int32)]
+                ("wgs_per_cu", ctypes.c_int32), ("store_kb_per_wave", ctypes.c_int32), ("store_mode", ctypes.c_int32)]
 
 
 def load_library():
@@ -37,8 +37,8 @@ def load_library():
     return _lib
 
 
-def cfg(loads_per_lane=16, buffers=1, nontemporal=1, wgs_per_cu=2, store_kb_per_wave=0):
-    return bha_probe_cfg(loads_per_lane, buffers, nontemporal, wgs_per_cu, store_kb_per_wave)
+def cfg(loads_per_lane=16, buffers=1, nontemporal=1, wgs_per_cu=2, store_kb_per_wave=0, store_mode=0):
+    return bha_probe_cfg(loads_per_lane, buffers, nontemporal, wgs_per_cu, store_kb_per_wave, store_mode)
 
 
 def stream_gbps(c: bha_probe_cfg, read_bytes: int, launches: int = 10, regions: int = 5, device=None):

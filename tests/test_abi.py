@@ -343,7 +343,8 @@ def test_probe_rejects_bad_arguments_on_the_host():
     assert plib.bha_probe_trip_write_bytes(ctypes.byref(good)) == 4 * 2 * 1024
     P = ctypes.c_void_p
     for bad in (probe.cfg(12, 1, 1, 2, 0), probe.cfg(16, 3, 1, 2, 0), probe.cfg(16, 1, 2, 2, 0),
-                probe.cfg(16, 1, 1, 0, 0), probe.cfg(16, 1, 1, 9, 0), probe.cfg(16, 1, 1, 2, 9)):
+                probe.cfg(16, 1, 1, 0, 0), probe.cfg(16, 1, 1, 9, 0), probe.cfg(16, 1, 1, 2, 9),
+                probe.cfg(16, 1, 1, 2, 1, 5), probe.cfg(16, 1, 1, 2, 1, -1)):
         assert plib.bha_probe_trip_read_bytes(ctypes.byref(bad)) == -1
         assert plib.bha_probe_stream(ctypes.byref(bad), P(FAKE), 1, P(FAKE), P(FAKE), None) == -1
     assert plib.bha_probe_stream(None, P(FAKE), 1, P(FAKE), P(FAKE), None) == -1
