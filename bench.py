@@ -445,6 +445,36 @@ def shape_sweep(log) -> dict:
                      f"(R={R}, H={H}, d={d}, bf16, cold)", "rows": rows}
 
 
+def probe_sweep(read_bytes, log) -> dict:
+    """The HBM streaming probe (libbha_probe.so) over its configurations at
+    read_bytes per launch: read-only streams (slice size, slices in flight,
+    non-temporal loads, work-groups per CU), then streams with writes mixed in
+    at 2:1 to 16:1 under each store mode of include/bha_probe.h. Medians of 10
+    launches on rotating source regions."""
+    from linear_attention_block_amd import probe
+
+    rows = []
+
+    def run(**c):
+        moved, t, gbps = probe.stream_gbps(probe.cfg(**c), read_bytes)
+        row = dict(c, us=t * 1e6, bytes=moved, GBps=gbps, frac=gbps / PEAK_HBM_GBS)
+        rows.append(row)
+        log(f"probe {c}: {moved / 1e6:.0f} MB in {t * 1e6:.1f} us = {gbps:.0f} GB/s ({gbps / PEAK_HBM_GBS:.1%})")
+
+    for nsl in (8, 16, 32):
+        for nbuf in (1, 2):
+            for nt in (0, 1):
+                for wpe in (1, 2, 4, 8):
+                    if nsl * nbuf * 4 * wpe <= 512:  # register file: slices of every resident wave
+                        run(loads_per_lane=nsl, buffers=nbuf, nontemporal=nt, wgs_per_cu=wpe, store_kb_per_wave=0)
+    for nsl, wkb in ((16, 1), (8, 1), (32, 3), (16, 2), (16, 8), (8, 8)):
+        for sm in (0, 1, 2, 3, 4):
+            for wpe in (1, 2):
+                run(loads_per_lane=nsl, buffers=1, nontemporal=1, wgs_per_cu=wpe, store_kb_per_wave=wkb,
+                    store_mode=sm)
+    return {"probe_sweep": f"streaming probe at {read_bytes / 1e6:.0f} MB read per launch", "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -478,6 +508,9 @@ def main() -> int:
     ap.add_argument("--shape-sweep", action="store_true",
                     help="instead of the block cycle: forward and commit latency over block sizes 8..64 and "
                          "feature widths FW 32..128 (prints its own JSON line)")
+    ap.add_argument("--probe-sweep", action="store_true",
+                    help="instead of the block cycle: the HBM streaming probe over its configurations at the "
+                         "forward's read bytes (prints its own JSON line)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter scaling)")
     args = ap.parse_args()
@@ -508,6 +541,11 @@ def main() -> int:
         return 0
     if args.shape_sweep:
         print(json.dumps(shape_sweep(log)), flush=True)
+        return 0
+    if args.probe_sweep:
+        c = synth.make_case(args.config, R=args.requests or None, with_prefix=False, with_qkv=False)
+        fb = forward_bytes(c.R, c.H, c.d, c.FW, c.B)
+        print(json.dumps(probe_sweep(fb - c.R * c.B * c.H * c.d * 2, log)), flush=True)
         return 0
     if args.kv_heads:
         print(json.dumps(gqa_cycle(args, log)), flush=True)

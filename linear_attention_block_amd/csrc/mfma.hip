@@ -1220,11 +1220,13 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
     f32x4* dst = reinterpret_cast<f32x4*>(rec + wv * F * 32) + lane;
 #pragma unroll
     for (int t = 0; t < C::NSL; ++t) __builtin_nontemporal_store(sv[t], dst + t * 64);
+    // Z as loaded for the forward (its LDS copy), plus the block's phi sums:
+    // the work-group ends with stores only
     for (int f = tid; f < F; f += C::NT) {
         float z = 0.0f;
 #pragma unroll
         for (int t = 0; t < 32; ++t) z += sm.Pt[f * C::PS + t];
-        rec[D * F + f] += z;
+        rec[D * F + f] = sm.f.Zs[f] + z;
     }
 }
 
