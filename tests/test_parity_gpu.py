@@ -688,7 +688,8 @@ def test_state_is_consistent_across_block_sizes(dev, io):
 
 GQA = [("bf16", 128, 64, 32, 2), ("bf16", 128, 64, 17, 4), ("bf16", 64, 32, 32, 4), ("bf16", 128, 32, 9, 2),
        ("bf16", 128, 128, 32, 2), ("bf16", 128, 128, 32, 4), ("bf16", 128, 64, 48, 2), ("f32", 128, 64, 8, 2),
-       ("bf16", 128, 64, 32, 8), ("bf16", 64, 32, 17, 8), ("bf16", 128, 128, 32, 8)]
+       ("bf16", 128, 64, 32, 8), ("bf16", 64, 32, 17, 8), ("bf16", 128, 128, 32, 8), ("bf16", 64, 64, 32, 8),
+       ("bf16", 128, 32, 5, 8)]
 
 
 @pytest.mark.parametrize("io,d,fw,b,g", GQA)

@@ -43,15 +43,15 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _states(dev, fw, hk, R=R):
+def _states(dev, fw, hk, R=R, d=D):
     """Slots, W (hk heads), and states built by one ragged prefill."""
-    case = synth.make_case("decode256", R=R, with_prefix=False, with_qkv=False, FW=fw)
+    case = synth.make_case("decode256", R=R, with_prefix=False, with_qkv=False, FW=fw, d=d)
     nb = np.random.default_rng(5).integers(0, 5, size=R)
-    w, _ = synth.device_layer_params("decode256", 0, dev, FW=fw, H=hk)
-    _, gamma = synth.device_layer_params("decode256", 0, dev, FW=fw, H=H)
+    w, _ = synth.device_layer_params("decode256", 0, dev, FW=fw, H=hk, d=d)
+    _, gamma = synth.device_layer_params("decode256", 0, dev, FW=fw, H=H, d=d)
     slots = torch.from_numpy(case.slot_ids).to(dev)
-    state = bha.new_state(case.num_slots, hk, D, fw, dev)
-    pk, pv, offs = synth.device_packed_prefix("decode256", nb, dev, FW=fw, H=hk)
+    state = bha.new_state(case.num_slots, hk, d, fw, dev)
+    pk, pv, offs = synth.device_packed_prefix("decode256", nb, dev, FW=fw, H=hk, d=d)
     bha.state_prefill(pk, pv, offs, w, state, slots)
     torch.cuda.synchronize()
     bad = case.slot_ids.copy()
@@ -61,9 +61,9 @@ def _states(dev, fw, hk, R=R):
 
 def _check_all_pairs(y, q, k, v, w, gamma, state, slot_ids, g, fw, tag):
     hk = H // g
-    R = q.shape[0]
+    R, d = q.shape[0], q.shape[3]
     rec = state.cpu().numpy()[slot_ids]  # [R][hk][rec]
-    S, Z = record_to_plain(rec, D, 2 * fw)
+    S, Z = record_to_plain(rec, d, 2 * fw)
     rep = lambda a: np.repeat(a, g, axis=1)  # noqa: E731  K/V head -> its query heads
     kq = rep(pairs(to_host(k)))
     vq = rep(pairs(to_host(v)))
@@ -84,30 +84,31 @@ def _check_all_pairs(y, q, k, v, w, gamma, state, slot_ids, g, fw, tag):
 @pytest.mark.parametrize("fw,b", [(32, 48), (32, 64), (64, 48), (64, 64), (128, 48), (128, 64)])
 def test_two_tile_forward_every_pair(dev, fw, b):
     case, w, gamma, _, slots_bad, state = _states(dev, fw, H)
-    q, k, v = synth.device_step_qkv("decode256", 0, R, dev, FW=fw, B=b)
+    q, k, v = synth.device_step_qkv("decode256", 0, R, dev, FW=fw, B=b)  # d = 128
     y = bha.block_forward(q, k, v, w, gamma, state, slots_bad)
     torch.cuda.synchronize()
     _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, fw, f"two-tile FW={fw} B={b}")
 
 
-@pytest.mark.parametrize("fw,hk", [(64, 8), (64, 4), (64, 2), (32, 4), (32, 2), (128, 8), (128, 4)])
-def test_grouped_forward_every_pair(dev, fw, hk):
+@pytest.mark.parametrize("d,fw,hk", [(128, 64, 8), (128, 64, 4), (128, 64, 2), (128, 32, 4), (128, 32, 2),
+                                     (128, 128, 8), (128, 128, 4), (64, 64, 2), (64, 32, 2), (64, 64, 4)])
+def test_grouped_forward_every_pair(dev, d, fw, hk):
     g = H // hk
-    case, w, gamma, _, slots_bad, state = _states(dev, fw, hk)
-    q = synth.device_step_qkv("decode256", 0, R, dev, FW=fw)[0]
-    _, k, v = synth.device_step_qkv("decode256", 0, R, dev, FW=fw, H=hk)
+    case, w, gamma, _, slots_bad, state = _states(dev, fw, hk, d=d)
+    q = synth.device_step_qkv("decode256", 0, R, dev, FW=fw, d=d)[0]
+    _, k, v = synth.device_step_qkv("decode256", 0, R, dev, FW=fw, H=hk, d=d)
     y = bha.block_forward_gqa(q, k, v, w, gamma, state, slots_bad)
     torch.cuda.synchronize()
-    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, g, fw, f"grouped FW={fw} G={g}")
+    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, g, fw, f"grouped d={d} FW={fw} G={g}")
 
 
-@pytest.mark.parametrize("nreq", [256, 512])
-def test_one_tile_forward_every_pair(dev, nreq):
+@pytest.mark.parametrize("d,nreq", [(128, 256), (128, 512), (64, 512)])
+def test_one_tile_forward_every_pair(dev, d, nreq):
     # the headline kernel (B = 32, FW = 64) at the decode256 grid (two
     # work-groups per CU, 8 pairs each), and at 512 requests (8,192 pairs: one
     # work-group per CU, 32 pairs each), every pair
-    case, w, gamma, _, slots_bad, state = _states(dev, 64, H, R=nreq)
-    q, k, v = synth.device_step_qkv("decode256", 0, nreq, dev)
+    case, w, gamma, _, slots_bad, state = _states(dev, 64, H, R=nreq, d=d)
+    q, k, v = synth.device_step_qkv("decode256", 0, nreq, dev, d=d)
     y = bha.block_forward(q, k, v, w, gamma, state, slots_bad)
     torch.cuda.synchronize()
-    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, 64, f"one-tile FW=64 B=32 R={nreq}")
+    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, 64, f"one-tile d={d} FW=64 B=32 R={nreq}")
