@@ -47,9 +47,9 @@ PROBE_CONFIGS = (
     ("read_only_deep", dict(loads_per_lane=32, buffers=1, nontemporal=0, wgs_per_cu=3, store_kb_per_wave=0)),
     ("read_write_11_to_1", dict(loads_per_lane=32, buffers=1, nontemporal=1, wgs_per_cu=2, store_kb_per_wave=3)),
 )
-KERNEL_SOURCES = ("linear_attention_block_amd/csrc/mfma.hip", "linear_attention_block_amd/csrc/bha_device.hpp",
-                  "linear_attention_block_amd/csrc/bha_internal.hpp",
-                  "linear_attention_block_amd/csrc/bha_mfma.hpp")
+KERNEL_SOURCES = tuple(f"linear_attention_block_amd/csrc/{f}" for f in (
+    "mfma_common.hpp", "mfma_forward.hip", "mfma_gqa.hip", "mfma_gqa8.hip", "mfma_commit.hip", "mfma_fused.hip",
+    "mfma_prefill.hip", "mfma_feature_map.hip", "bha_device.hpp", "bha_internal.hpp", "bha_mfma.hpp"))
 
 
 def forward_bytes(R, H, d, FW, B, es=2):

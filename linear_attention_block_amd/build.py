@@ -22,7 +22,10 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libbha.so")
 PROBE_OUT = os.path.join(HERE, "libbha_probe.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["bha_api.cpp", "bha_validate.cpp", "generic.hip", "mfma.hip", "softmax_attn.hip"]
+SOURCES = ["bha_api.cpp", "bha_validate.cpp", "generic.hip", "softmax_attn.hip",
+           # one translation unit per matrix-core kernel family (mfma_common.hpp)
+           "mfma_forward.hip", "mfma_gqa.hip", "mfma_gqa8.hip", "mfma_commit.hip", "mfma_fused.hip",
+           "mfma_prefill.hip", "mfma_feature_map.hip"]
 PROBE_SOURCES = ["stream_probe.hip"]
 
 
