@@ -1,4 +1,4 @@
-"""GPU parity of the persistent forward kernels at production grid sizes.
+"""GPU parity of the persistent forward kernels, and of the commit, at production grid sizes.
 
 The matrix-core forwards run a persistent grid of (resident work-groups per
 CU) x CUs work-groups, each taking pairs b, b + G, b + 2G, ... with the next
@@ -12,7 +12,9 @@ of the batch: its rows must come out NaN while the pairs around it, whose
 look-ahead loads run through it, stay exact.
 
 Covered: blocks of 48 and 64 tokens (two 32-token query tiles) at FW = 32, 64
-and 128; grouped K/V heads with 2, 4 and 8 query heads per K/V head.
+and 128; grouped K/V heads with 2, 4 and 8 query heads per K/V head; the
+one-tile forward at 256 and 512 requests; the commit at 256 and 512 requests
+with skipped requests scattered through the batch.
 States: one ragged prefill over 0..4 blocks of 32 tokens per request (zero
 records included). Bar: normwise 2e-2 (bf16 I/O, fp32 accumulation).
 """
@@ -112,3 +114,36 @@ def test_one_tile_forward_every_pair(dev, d, nreq):
     y = bha.block_forward(q, k, v, w, gamma, state, slots_bad)
     torch.cuda.synchronize()
     _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, 64, f"one-tile d={d} FW=64 B=32 R={nreq}")
+
+
+@pytest.mark.parametrize("d,fw,nreq", [(128, 64, 256), (128, 32, 256), (128, 64, 512), (64, 64, 512), (64, 32, 256)])
+def test_commit_every_pair_with_skipped_requests(dev, d, fw, nreq):
+    # bha_state_commit at production size with requests whose slots are out
+    # of range (negative or past the pool) scattered through the batch:
+    # nothing of theirs is written, every record outside the committed
+    # requests stays unchanged bit for bit, and every committed pair matches
+    # the oracle's commit from the same pre-commit bytes.
+    case, w, _, _, _, state = _states(dev, fw, H, R=nreq, d=d)
+    bads = np.array([3, 77, 78, 130, nreq - 1])
+    slot_np = case.slot_ids.copy()
+    slot_np[bads] = [-1, case.num_slots, case.num_slots + 5, -7, 2**31 - 1]
+    _, k, v = synth.device_step_qkv("decode256", 0, nreq, dev, FW=fw, d=d)
+    pre = state.cpu().numpy()
+    bha.state_commit(k, v, w, state, torch.from_numpy(slot_np).to(dev))
+    torch.cuda.synchronize()
+    post = state.cpu().numpy()
+    good = np.setdiff1d(np.arange(nreq), bads)
+    touched = case.slot_ids[good]
+    untouched = np.setdiff1d(np.arange(case.num_slots), touched)
+    assert np.array_equal(post[untouched].view(np.uint32), pre[untouched].view(np.uint32)), \
+        "records outside the committed requests changed"
+    F = 2 * fw
+    S, Z = record_to_plain(pre[touched], d, F)
+    S, Z = np.ascontiguousarray(S), np.ascontiguousarray(Z)
+    oracle.state_commit_batch(S, Z, np.ascontiguousarray(pairs(to_host(k))[good]),
+                              np.ascontiguousarray(pairs(to_host(v))[good]), to_host(w), nthreads=NTHREADS)
+    S2, Z2 = record_to_plain(post[touched], d, F)
+    err = max(normwise_err(S2, S, (2, 3)), normwise_err(Z2, Z, (2,)))
+    print(f"[commit d={d} FW={fw} R={nreq}] {len(good) * H} pairs committed, "
+          f"{len(bads)} requests skipped: err {err:.2e}", flush=True)
+    assert err <= TOL
