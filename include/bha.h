@@ -286,6 +286,14 @@ const char* bha_status_string(int status);
 /* Library version as major * 10000 + minor * 100 + patch. */
 int bha_version(void);
 
+/* Identity of the build: the first 16 hex digits of a SHA-256 over the source
+ * files the library was built from (its csrc sources and headers and this
+ * header), fixed when it is compiled; "unknown" for a build that did not set
+ * it. Static string, never NULL. The Python binding refuses an in-tree
+ * library whose hash differs from that of the sources beside it, so a stale
+ * build fails loudly instead of running other code. */
+const char* bha_source_hash(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,6 +34,7 @@ __all__ = [
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbha.so")
+_BUILT_LIB_PATH = _LIB_PATH
 _lib = None
 
 BHA_F32 = 0
@@ -44,7 +45,7 @@ EXPORTED_SYMBOLS = (
     "bha_feature_map", "bha_block_forward", "bha_block_forward_gqa", "bha_block_forward_commit", "bha_state_commit", "bha_state_prefill",
     "bha_prefix_attention", "bha_prefix_attention_workspace", "bha_prefix_attention_noalloc",
     "bha_prefix_attention_noalloc_scratch_bytes",
-    "bha_state_record_floats", "bha_status_string", "bha_version",
+    "bha_state_record_floats", "bha_status_string", "bha_version", "bha_source_hash",
 )
 
 
@@ -112,12 +113,27 @@ def load_library():
     lib.bha_version.argtypes = []
     for f in (lib.bha_feature_map, lib.bha_block_forward, lib.bha_state_commit, lib.bha_version):
         f.restype = ctypes.c_int
+    lib.bha_source_hash.argtypes = []
+    lib.bha_source_hash.restype = ctypes.c_char_p
+    if _LIB_PATH == _BUILT_LIB_PATH:
+        # the in-tree library must have been built from the sources beside it
+        from .build import source_hash
+        built, here = lib.bha_source_hash().decode(), source_hash()
+        if built != here:
+            raise RuntimeError(
+                f"{_LIB_PATH} was built from other sources (library {built}, sources on disk {here}): "
+                "rebuild it with `python -m linear_attention_block_amd.build`")
     _lib = lib
     return lib
 
 
 def version() -> int:
     return int(load_library().bha_version())
+
+
+def source_hash() -> str:
+    """The hash of the sources the loaded library was built from."""
+    return load_library().bha_source_hash().decode()
 
 
 def status_string(status: int) -> str:

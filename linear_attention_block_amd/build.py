@@ -12,6 +12,7 @@ it does not know that feature, which is harmless.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -27,6 +28,26 @@ SOURCES = ["bha_api.cpp", "bha_validate.cpp", "generic.hip", "softmax_attn.hip",
            "mfma_forward.hip", "mfma_gqa.hip", "mfma_gqa8.hip", "mfma_commit.hip", "mfma_fused.hip",
            "mfma_prefill.hip", "mfma_feature_map.hip"]
 PROBE_SOURCES = ["stream_probe.hip"]
+HEADER = os.path.join(HERE, "..", "include", "bha.h")
+
+
+def library_sources() -> list[str]:
+    """Every file libbha.so is built from: its sources, the csrc headers and
+    include/bha.h."""
+    headers = sorted(f for f in os.listdir(CSRC) if f.endswith(".hpp"))
+    return [os.path.join(CSRC, f) for f in SOURCES + headers] + [HEADER]
+
+
+def source_hash() -> str:
+    """First 16 hex digits of a SHA-256 over the library's source files (name
+    and contents, in library_sources() order). Compiled into libbha.so
+    (bha_source_hash), so a library can be matched with the sources on disk."""
+    h = hashlib.sha256()
+    for path in library_sources():
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def hipcc() -> str:
@@ -48,12 +69,15 @@ def common_flags() -> list[str]:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
+    src_hash = source_hash()
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         cmd = [cc, *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
+        if src == "bha_api.cpp":
+            cmd.append(f'-DBHA_SOURCE_HASH="{src_hash}"')
         res = subprocess.run(cmd, capture_output=True, text=True)
         msgs = [ln for ln in (res.stdout + res.stderr).splitlines()
                 if "packed-fp32-ops" not in ln]

@@ -334,3 +334,10 @@ extern "C" const char* bha_status_string(int status)
 }
 
 extern "C" int bha_version(void) { return BHA_VERSION_NUMBER; }
+
+// Set by the build to a hash of the library's source files.
+#ifndef BHA_SOURCE_HASH
+#define BHA_SOURCE_HASH "unknown"
+#endif
+
+extern "C" const char* bha_source_hash(void) { return BHA_SOURCE_HASH; }

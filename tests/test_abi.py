@@ -46,6 +46,15 @@ def test_library_exports_every_header_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_library_built_from_these_sources(lib):
+    # the build compiles a hash of its sources into the library; the binding
+    # refuses an in-tree library built from other sources (load_library raises)
+    from linear_attention_block_amd import build
+    got = bha.source_hash()
+    assert len(got) == 16 and all(c in "0123456789abcdef" for c in got)
+    assert got == build.source_hash()
+
+
 def test_version_and_status_strings(lib):
     assert bha.version() == 10000
     for st in (OK, NULL, DIMS, UNSUP, ALIGN, STRIDE, DTYPE, HIP):
