@@ -233,7 +233,7 @@ struct alignas(16) FwdLds {
     uint16_t Ws[FW * C::RS];
     uint16_t Vs[32 * KT * C::RS];  // V rows, read transposed by ds_read_b64_tr_b16
     float Zs[C::F];
-    uint16_t Os[KT == 1 && G == 1 ? 32 * D : 8];  // the pair's output rows (one-head, one-tile kernel)
+    uint16_t Os[KT == 1 && G == 1 ? 32 * (D + 8) : 8];  // the pair's output rows, padded (one-head, one-tile kernel)
 };
 
 // The per-pair operands a thread stages through LDS, held in registers from
@@ -527,7 +527,10 @@ __device__ __forceinline__ void merge_store(const ForwardArgs& a, const f32x16& 
 }
 
 // Merge for token ln of this wave's 32 columns into the output tile Os
-// ([32][D] bf16); after a barrier the work-group stores whole 2D-byte rows
+// ([32][D + 8] bf16: a lane writes row qi, and the 16-byte pad moves each row
+// by four banks, so the 32 rows a write instruction touches spread over the
+// banks instead of all landing on the same two: 32-way bank conflicts on the
+// unpadded 2D-byte rows); after a barrier the work-group stores whole 2D-byte rows
 // with non-temporal stores, so every line reaches memory complete (a wave's
 // own columns are half lines). Measured at decode256 size, interleaved: 74.7
 // -> 73.9 us per forward (plain stores of the same rows 74.0 us); the
@@ -555,7 +558,7 @@ __device__ __forceinline__ void merge_to_lds(const ForwardArgs& a, const f32x16&
             pk[e] = static_cast<uint32_t>(bf16_bits(y0)) | (static_cast<uint32_t>(bf16_bits(y1)) << 16);
         }
         // columns 32 wv + 8 q4 + 4 g .. + 3 of row qi
-        *reinterpret_cast<uint2*>(Os + qi * D + 32 * wv + 8 * q4 + 4 * g) = make_uint2(pk[0], pk[1]);
+        *reinterpret_cast<uint2*>(Os + qi * (D + 8) + 32 * wv + 8 * q4 + 4 * g) = make_uint2(pk[0], pk[1]);
     }
 }
 
@@ -571,7 +574,7 @@ __device__ __forceinline__ void store_out_rows(const ForwardArgs& a, const uint1
         if (row < a.B) {
             uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
                              static_cast<int64_t>(h) * a.os.head + (row * static_cast<int>(a.os.tok) + 8 * ch);
-            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Os + row * D + 8 * ch),
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Os + row * (D + 8) + 8 * ch),
                                         reinterpret_cast<u32x4*>(orow));
         }
     }
