@@ -169,7 +169,10 @@ __device__ __forceinline__ void prefill_load_k(const PrefillPair<D, FW>& pp, int
 // First half of chunk c: V rows to LDS, the loads PD chunks ahead issued,
 // phi(K) of this wave's 16 tokens to LDS and into the Z partials. Safe for
 // c == nchunks (one past the end): no loads, zero phi, buffers unused.
-template <int D, int FW>
+// BUF: the LDS buffer of chunk c when the caller knows it at compile time
+// (c % 2 with two buffers), so that the buffer's base folds into the LDS
+// instructions' offsets; -1: chosen at run time.
+template <int D, int FW, int BUF = -1>
 __device__ __forceinline__ void prefill_phi(const PrefillPair<D, FW>& pp, int c, int tid, uint16_t* Vs,
                                             uint16_t* Ps, const uint16_t* Ws, u32x4 (&vr)[PCfg<D, FW>::VQ],
                                             bf16x8 (&kf)[D / 32], float (&zl)[FW / 2])
@@ -180,8 +183,9 @@ __device__ __forceinline__ void prefill_phi(const PrefillPair<D, FW>& pp, int c,
     const int lane = tid & 63, wv = tid >> 6;
     const int n16 = lane & 15, q = lane >> 4;
     const int nc = prefill_chunk_rows(pp, c);
-    uint16_t* const Vb = Vs + (P::NBUF == 2 ? (c & 1) : 0) * (CT * D);
-    uint16_t* const Pb = Ps + (P::NBUF == 2 ? (c & 1) : 0) * (CT * F);
+    const int buf = P::NBUF == 2 ? (BUF >= 0 ? BUF : (c & 1)) : 0;
+    uint16_t* const Vb = Vs + buf * (CT * D);
+    uint16_t* const Pb = Ps + buf * (CT * F);
     prefill_store_v<D, FW>(Vb, tid, vr);
     if (c + PD < pp.nchunks) prefill_load_v(pp, c + PD, tid, vr);
 
@@ -242,8 +246,10 @@ __device__ __forceinline__ void prefill_phi(const PrefillPair<D, FW>& pp, int c,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float pp_ = u[T][e] * ip, pn = en[T][e] * in;
-            zl[4 * T + e] += pp_;
-            zl[FW / 4 + 4 * T + e] += pn;
+            // Z takes the unrounded products (one rounding, whatever the
+            // compiler would contract)
+            zl[4 * T + e] = __builtin_fmaf(u[T][e], ip, zl[4 * T + e]);
+            zl[FW / 4 + 4 * T + e] = __builtin_fmaf(en[T][e], in, zl[FW / 4 + 4 * T + e]);
             hp[e] = bf16_bits(pp_);
             hn[e] = bf16_bits(pn);
         }
@@ -278,7 +284,7 @@ __device__ __forceinline__ bf16x8 vt_frag_at(const uint16_t* Xs, int lo_off, int
 
 // Second half of chunk c: dS = phi(K)^T V over the chunk, this wave's state
 // rows and value columns, accumulated into its state tiles.
-template <int D, int FW>
+template <int D, int FW, int BUF = -1>
 __device__ __forceinline__ void prefill_ds(int c, int tid, const uint16_t* Vs, const uint16_t* Ps,
                                            f32x16 (&st)[PCfg<D, FW>::RW / 32])
 {
@@ -286,8 +292,9 @@ __device__ __forceinline__ void prefill_ds(int c, int tid, const uint16_t* Vs, c
     constexpr int F = P::F, NC = P::NC, CT = P::CT, RW = P::RW;
     const int lane = tid & 63, wv = tid >> 6;
     const int cs = wv % NC, r0 = (wv / NC) * RW;
-    const uint16_t* const Vb = Vs + (P::NBUF == 2 ? (c & 1) : 0) * (CT * D);
-    const uint16_t* const Pb = Ps + (P::NBUF == 2 ? (c & 1) : 0) * (CT * F);
+    const int buf = P::NBUF == 2 ? (BUF >= 0 ? BUF : (c & 1)) : 0;
+    const uint16_t* const Vb = Vs + buf * (CT * D);
+    const uint16_t* const Pb = Ps + buf * (CT * F);
     if constexpr (P::NBUF == 2) {
 #pragma unroll
         for (int kb = 0; kb < CT / 16; ++kb) {
@@ -430,13 +437,23 @@ void prefill_mfma_kernel(CommitArgs a)
     prefill_load_v(pp, 0, tid, vr);
     prefill_load_k(pp, 0, wv, n16, q, kf);
     if constexpr (P::NBUF == 2) {
-        // chunk c lives in LDS buffer c % 2
+        // chunk c lives in LDS buffer c % 2; two chunks per trip, so every
+        // buffer index is a constant and folds into the LDS offsets
         __syncthreads();  // W rows visible to every wave
-        prefill_phi(pp, 0, tid, Vs, Ps, Ws, vr, kf, zl);
+        prefill_phi<D, FW, 0>(pp, 0, tid, Vs, Ps, Ws, vr, kf, zl);
         __syncthreads();
-        for (int c = 0; c < pp.nchunks; ++c) {
-            prefill_phi(pp, c + 1, tid, Vs, Ps, Ws, vr, kf, zl);
-            prefill_ds<D, FW>(c, tid, Vs, Ps, st);
+        int c = 0;
+        for (; c + 1 < pp.nchunks; c += 2) {
+            prefill_phi<D, FW, 1>(pp, c + 1, tid, Vs, Ps, Ws, vr, kf, zl);
+            prefill_ds<D, FW, 0>(c, tid, Vs, Ps, st);
+            __syncthreads();
+            prefill_phi<D, FW, 0>(pp, c + 2, tid, Vs, Ps, Ws, vr, kf, zl);
+            prefill_ds<D, FW, 1>(c + 1, tid, Vs, Ps, st);
+            __syncthreads();
+        }
+        if (c < pp.nchunks) {
+            prefill_phi<D, FW, 1>(pp, c + 1, tid, Vs, Ps, Ws, vr, kf, zl);
+            prefill_ds<D, FW, 0>(c, tid, Vs, Ps, st);
             __syncthreads();
         }
     } else {
