@@ -97,7 +97,7 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
         for (int ps = 0; ps < G / GP; ++ps) {
             if (ps > 0) {
-                load_q(p, ps);
+                // this pass's Q was loaded during the previous pass's phase two
                 __syncthreads();  // the previous pass's shared operands are read
                 qc.template store_rows<C::RS>(Qs, tid);
                 __syncthreads();
@@ -132,6 +132,9 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(2
                 }
             }
             __syncthreads();
+            // the next pass's Q streams in while this pass's heads are merged
+            // (phase two holds fewer registers than phase one)
+            if (ps + 1 < G / GP) load_q(p, ps + 1);
 #pragma unroll
             for (int j = 0; j < GP; ++j) {
                 bf16x8 pb[F / 16], pp[2];
