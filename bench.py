@@ -305,6 +305,7 @@ def gqa_cycle(args, log) -> dict:
                      "kernel": ("bha_block_forward_gqa: " +
                                 (f"forward_mfma_kernel<{d},{FW},{(B + 31) // 32}>" if G == 1 and B <= 64 else
                                  f"forward_gqa_mfma_kernel<{d},{FW},{G}>" if G in (2, 4) and B <= 32 else
+                                 f"forward_gqa8_kernel<{d},{FW}>" if G == 8 and FW <= 64 and B <= 32 else
                                  "forward_generic_kernel")),
                      "bytes_per_launch": fb, "avg_launch_us": fwd_avg * 1e6},
         "commit": {"kernel": "bha_state_commit over the K/V heads", "avg_launch_us": com_avg * 1e6,
