@@ -13,7 +13,10 @@ namespace {
 // slice, P V and merge). K stays in LDS across both passes, so the work-group
 // needs 79 KiB of LDS at FW = 64 instead of the 114 KiB of staging all eight
 // heads at once, and two work-groups share a CU. Each unit loads its
-// operands at its start; only the state slice runs a unit ahead.
+// operands at its start; only the state slice runs a unit ahead. When every
+// work-group has exactly one unit (ONE), nothing runs ahead: W, K, V, Z and
+// the first pass's Q are issued before the state slice, so phase one runs
+// while the slice arrives (it is first read by phase two's linear reads).
 template <int D, int FW>
 struct alignas(16) Gqa8Lds {
     using C = Cfg<D, FW>;
@@ -31,7 +34,7 @@ struct alignas(16) Gqa8Lds {
     float Zs[F];
 };
 
-template <int D, int FW>
+template <int D, int FW, bool ONE>
 __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(2, 2))) void forward_gqa8_kernel(
     ForwardArgs a, int npairs)
 {
@@ -50,17 +53,15 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(2
     bf16x8* const PB = reinterpret_cast<bf16x8*>(sm.u);
     bf16x8* const PP = reinterpret_cast<bf16x8*>(sm.u + L::PB_BYTES);
     float* const SC = reinterpret_cast<float*>(sm.u + L::PB_BYTES + L::PP_BYTES);
-    {
-        WChunks<D, FW, NT> wc;
-        wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(hk) * a.wh, tid);
-        wc.template store_rows<C::RS>(sm.Ws, tid);
-    }
+    WChunks<D, FW, NT> wc;
+    wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(hk) * a.wh, tid);
+    if constexpr (!ONE) wc.template store_rows<C::RS>(sm.Ws, tid);
     auto slot_of = [&](int pp) { return a.slot_ids[(pp < npairs ? pp : npairs - 1) / HK]; };
     auto rec_of = [&](int u, int sl) {
         const bool ok = sl >= 0 && sl < a.num_slots;
         return a.state + (static_cast<int64_t>(ok ? sl : 0) * HK + u % HK) * static_cast<int64_t>(D + 1) * F;
     };
-    const int count = (npairs - p + NG - 1) / NG;
+    const int count = ONE ? 1 : (npairs - p + NG - 1) / NG;
     const int qtok = static_cast<int>(a.qs.tok), ktok = static_cast<int>(a.ks.tok);
     RowChunks<D, NT> kc, vc;
     RowChunks<D, NT, 32 * GP> qc;
@@ -70,14 +71,14 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(2
         qc.template load_heads<32>(static_cast<const uint16_t*>(a.q) + qbase, qtok, a.qs.head, a.B, tid);
     };
     f32x4 sv[C::NSL];
-    load_state_slice(rec_of(p, slot_of(p)) + wv * F * 32, lane, sv);
+    if constexpr (!ONE) load_state_slice(rec_of(p, slot_of(p)) + wv * F * 32, lane, sv);
     int slot_cur = slot_of(p);
-    int slot_next = slot_of(p + NG);
+    int slot_next = ONE ? 0 : slot_of(p + NG);
     for (int k = 0; k < count; ++k) {
         const int live = k + 1 < count ? 1 : 0;
         const int pn = live ? p + NG : p;
         const int r = p / HK;
-        int slot_after = slot_of(pn + NG);
+        int slot_after = ONE ? 0 : slot_of(pn + NG);
         __syncthreads();  // every wave is done with the previous unit's LDS operands
         {
             const int sl = __builtin_amdgcn_readfirstlane(slot_cur);
@@ -87,6 +88,10 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(2
             vc.load(static_cast<const uint16_t*>(a.v) + kbase, ktok, a.B, tid);
             const f32x4 z = reinterpret_cast<const f32x4*>(rec + D * F)[tid % (F / 4)];
             load_q(p, 0);
+            if constexpr (ONE) {
+                load_state_slice(rec + wv * F * 32, lane, sv);
+                wc.template store_rows<C::RS>(sm.Ws, tid);
+            }
             kc.template store_rows<C::RS>(sm.Ks, tid);
             vc.template store_rows<C::RS>(sm.Vs, tid);
             if (tid < F / 4) reinterpret_cast<f32x4*>(sm.Zs)[tid] = z;
@@ -146,7 +151,7 @@ __global__ __launch_bounds__(64 * (D / 32)) __attribute__((amdgpu_waves_per_eu(2
                 const float den = SC[(j * 5 + 2) * 32 + tln], m = SC[(j * 5 + 3) * 32 + tln];
                 const float l = SC[(j * 5 + 4) * 32 + tln];
                 const f32x16 lacc = linear_read<D, FW>(sv, pb, sp, sn);
-                if (ps == G / GP - 1 && j == GP - 1) {
+                if (!ONE && ps == G / GP - 1 && j == GP - 1) {
                     // the last head's linear read is done: the slice registers
                     // take the next unit's slice
                     __builtin_amdgcn_sched_barrier(0);
@@ -178,9 +183,11 @@ hipError_t launch_forward_gqa8(const ForwardArgs& a, hipStream_t s)
     int64_t NG = static_cast<int64_t>(compute_units()) * 2;
     NG = (NG / hk) * hk;
     if (NG < hk) NG = hk;
-    if (NG > npairs) NG = npairs;
-    return launch_kernel(forward_gqa8_kernel<D, FW>, dim3(static_cast<uint32_t>(NG)), dim3(64 * (D / 32)), s, a,
-                         npairs);
+    if (NG >= npairs)
+        return launch_kernel(forward_gqa8_kernel<D, FW, true>, dim3(static_cast<uint32_t>(npairs)),
+                             dim3(64 * (D / 32)), s, a, npairs);
+    return launch_kernel(forward_gqa8_kernel<D, FW, false>, dim3(static_cast<uint32_t>(NG)), dim3(64 * (D / 32)), s,
+                         a, npairs);
 }
 
 template <int D>

@@ -36,12 +36,13 @@ MIN_OCCUPANCY = {
     ("prefill_mfma_kernel", (128, 64)): 2,
     ("forward_gqa_mfma_kernel", (128, 64, 2)): 2,
     ("forward_gqa_mfma_kernel", (128, 64, 4)): 2,
-    ("forward_gqa8_kernel", (128, 64)): 2,
+    ("forward_gqa8_kernel", (128, 64, 0)): 2,
+    ("forward_gqa8_kernel", (128, 64, 1)): 2,
     ("feature_map_mfma_kernel", (128, 64)): 2,
     ("forward_split_kernel", (128,)): 2,
 }
 
-_SYM = re.compile(r"^_ZN3bha12_GLOBAL__N_1(\d+)(\w+?)I((?:Li\d+E)+)E\S*:")
+_SYM = re.compile(r"^_ZN3bha12_GLOBAL__N_1(\d+)(\w+?)I((?:L[ib]\d+E)+)E\S*:")
 
 
 def _kernel_key(sym_line):
@@ -52,7 +53,7 @@ def _kernel_key(sym_line):
     name = (m.group(2) + m.group(3))[:n]
     if "kernel" not in name:
         return None
-    return name, tuple(int(x) for x in re.findall(r"Li(\d+)E", m.group(3)))
+    return name, tuple(int(x) for x in re.findall(r"L[ib](\d+)E", m.group(3)))
 
 
 def _parse(path):

@@ -5,7 +5,8 @@ CU) x CUs work-groups, each taking pairs b, b + G, b + 2G, ... with the next
 pair's slot id, operands and state slice issued ahead of the current pair's
 arithmetic. A small batch gives every work-group one pair and never reaches
 that loop; these tests run 256 requests x 16 heads (4,096 pairs, or 512 to
-2,048 (request, K/V head) units), so every work-group takes several, and
+2,048 (request, K/V head) units), so every work-group takes several (eight
+query heads per K/V head: 512 requests for that), and
 compare EVERY pair with the fp64 oracle computed from the same fp32 state
 bytes the kernel read. One request carries an out-of-range slot in the middle
 of the batch: its rows must come out NaN while the pairs around it, whose
@@ -102,6 +103,21 @@ def test_grouped_forward_every_pair(dev, d, fw, hk):
     y = bha.block_forward_gqa(q, k, v, w, gamma, state, slots_bad)
     torch.cuda.synchronize()
     _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, g, fw, f"grouped d={d} FW={fw} G={g}")
+
+
+@pytest.mark.parametrize("d,fw", [(128, 64), (64, 32)])
+def test_eight_head_groups_several_units_per_work_group(dev, d, fw):
+    # eight query heads per K/V head: at 256 requests every work-group of the
+    # two-per-CU grid has one unit (the variant that issues the slice after
+    # the operands); at 512 requests each takes two, through the loop that
+    # loads the next unit's slice during the current unit's last head
+    g, hk, nreq = 8, H // 8, 512
+    case, w, gamma, _, slots_bad, state = _states(dev, fw, hk, R=nreq, d=d)
+    q = synth.device_step_qkv("decode256", 0, nreq, dev, FW=fw, d=d)[0]
+    _, k, v = synth.device_step_qkv("decode256", 0, nreq, dev, FW=fw, H=hk, d=d)
+    y = bha.block_forward_gqa(q, k, v, w, gamma, state, slots_bad)
+    torch.cuda.synchronize()
+    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, g, fw, f"grouped d={d} FW={fw} G={g} R={nreq}")
 
 
 @pytest.mark.parametrize("d,nreq", [(128, 256), (128, 512), (64, 512)])
