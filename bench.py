@@ -43,9 +43,9 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 # 16-byte loads per lane per trip, trips in flight per wave, non-temporal
 # loads, work-groups per CU, KiB written per wave per trip
 PROBE_CONFIGS = (
-    ("read_only_forward_shape", dict(loads_per_lane=16, buffers=1, nontemporal=1, wgs_per_cu=2, store_kb_per_wave=0)),
+    ("read_only_forward_shape", dict(loads_per_lane=16, buffers=1, nontemporal=1, wgs_per_cu=1, store_kb_per_wave=0)),
     ("read_only_deep", dict(loads_per_lane=32, buffers=1, nontemporal=0, wgs_per_cu=3, store_kb_per_wave=0)),
-    ("read_write_11_to_1", dict(loads_per_lane=32, buffers=1, nontemporal=1, wgs_per_cu=2, store_kb_per_wave=3)),
+    ("read_write_11_to_1", dict(loads_per_lane=32, buffers=1, nontemporal=1, wgs_per_cu=1, store_kb_per_wave=3)),
 )
 KERNEL_SOURCES = tuple(f"linear_attention_block_amd/csrc/{f}" for f in (
     "mfma_common.hpp", "mfma_forward.hip", "mfma_gqa.hip", "mfma_gqa8.hip", "mfma_commit.hip", "mfma_fused.hip",

@@ -225,25 +225,32 @@ __global__ __launch_bounds__(2 * 64 * (D / 32)) __attribute__((amdgpu_waves_per_
     }
 }
 
-// Persistent grid: as many work-groups as can be resident (WPE per CU),
-// rounded down to a multiple of H so that each keeps one head, and no more
-// than there are pairs. With at least kFwdOneGroupPairs pairs per CU the
-// one-tile forward runs one work-group per CU instead of two: the memory
-// system streams more with half the state slices in flight (measured at
-// d = 128, FW = 64, B = 32, six rotating state pools: 512 requests x 16 heads
-// 151.3 -> 141.2 us, 1,024 requests 295.1 -> 276.9 us), while below that the
-// one work-group's first and last pairs cost more than they save (256
-// requests: 77.8 -> 79.5 us).
-constexpr int kFwdOneGroupPairs = 32;
+// Persistent grid, sized in waves per SIMD: fwd_wpe resident waves per SIMD
+// (what the kernel's registers allow), that is fwd_wpe * 4 / (D / 32)
+// work-groups of D / 32 waves per CU, rounded down to a multiple of H so that
+// each work-group keeps one head, and no more than there are pairs. With at
+// least kFwdOneWavePairs pairs per CU the one-tile forward runs one wave per
+// SIMD instead of two: each pair's chain of loads, products and stores then
+// has its SIMD to itself and the memory system streams more with half the
+// state slices in flight. Measured at FW = 64, B = 32, six rotating state
+// pools, d = 128 (one work-group per CU against two): 128 requests x 16
+// heads 38.6 -> 37.9 us, 192: 54.4 -> 51.3 us, 256: 72.7-72.9 -> 67.1-70.0
+// us, 384: 110.2 -> 100.3 us, 512: 149.3 -> 133.3 us; FW = 32, 256 requests
+// 50.3 -> 46.8 us; below 8 pairs per CU no difference. At d = 64 (two-wave
+// work-groups) one wave per SIMD means two work-groups per CU: 512 requests
+// 88.2 -> 79.9 us (FW = 64) and 65.9 -> 52.4 us (FW = 32) against one. The
+// two-tile forward, the commit, the fused step, the grouped forwards and the
+// prefill are each slower at one wave per SIMD (at 256 requests, d = 128).
+constexpr int kFwdOneWavePairs = 8;
 
 template <int D, int FW, int KT>
 hipError_t launch_forward_kt(const ForwardArgs& a, hipStream_t s)
 {
     const int npairs = a.R * a.H;
     const int cus = compute_units();
-    int wpe = fwd_wpe<D, FW, KT>();
-    if (KT == 1 && wpe == 2 && npairs >= static_cast<int64_t>(kFwdOneGroupPairs) * cus) wpe = 1;
-    int64_t NG = static_cast<int64_t>(cus) * wpe;
+    int wps = fwd_wpe<D, FW, KT>();  // resident waves per SIMD
+    if (KT == 1 && npairs >= static_cast<int64_t>(kFwdOneWavePairs) * cus) wps = 1;
+    int64_t NG = static_cast<int64_t>(cus) * wps * 4 / (D / 32);
     NG = (NG / a.H) * a.H;
     if (NG < a.H) NG = a.H;
     if (NG > npairs) NG = npairs;

@@ -13,9 +13,10 @@ of the batch: its rows must come out NaN while the pairs around it, whose
 look-ahead loads run through it, stay exact.
 
 Covered: blocks of 48 and 64 tokens (two 32-token query tiles) at FW = 32, 64
-and 128; grouped K/V heads with 2, 4 and 8 query heads per K/V head; the
-one-tile forward at 256 and 512 requests; the commit at 256 and 512 requests
-with skipped requests scattered through the batch.
+and 128 (d = 128, and d = 64 at FW = 64 and 128); grouped K/V heads with 2, 4
+and 8 query heads per K/V head; the one-tile forward at 64, 256 and 512
+requests (d = 128) and d = 64 at FW = 32, 64 and 128; the commit at 256 and
+512 requests with skipped requests scattered through the batch.
 States: one ragged prefill over 0..4 blocks of 32 tokens per request (zero
 records included). Bar: normwise 2e-2 (bf16 I/O, fp32 accumulation).
 """
@@ -35,7 +36,7 @@ pytestmark = pytest.mark.gpu
 NTHREADS = min(16, os.cpu_count() or 1)
 TOL = 2e-2
 R, H, D = 256, 16, 128
-BAD = 77  # request given an out-of-range slot
+BAD = 77  # request given an out-of-range slot (77 mod R in smaller batches)
 
 
 @pytest.fixture(scope="module")
@@ -58,7 +59,7 @@ def _states(dev, fw, hk, R=R, d=D):
     bha.state_prefill(pk, pv, offs, w, state, slots)
     torch.cuda.synchronize()
     bad = case.slot_ids.copy()
-    bad[BAD] = case.num_slots
+    bad[BAD % R] = case.num_slots
     return case, w, gamma, slots, torch.from_numpy(bad).to(dev), state
 
 
@@ -73,9 +74,9 @@ def _check_all_pairs(y, q, k, v, w, gamma, state, slot_ids, g, fw, tag):
     ref = oracle.block_forward_batch(pairs(to_host(q)), kq, vq, np.repeat(to_host(w), g, axis=0),
                                      gamma.cpu().numpy().astype(np.float64), rep(S), rep(Z), nthreads=NTHREADS)
     yh = pairs(to_host(y))  # [R][H][B][d]
-    assert np.all(np.isnan(yh[BAD])), f"[{tag}] request with an out-of-range slot must be NaN"
+    assert np.all(np.isnan(yh[BAD % R])), f"[{tag}] request with an out-of-range slot must be NaN"
     good = np.ones(R, dtype=bool)
-    good[BAD] = False
+    good[BAD % R] = False
     assert np.all(np.isfinite(yh[good])), f"[{tag}] non-finite outputs outside the bad request"
     err = normwise_err(yh[good], ref[good], (2, 3))
     cus = torch.cuda.get_device_properties(y.device).multi_processor_count
@@ -84,13 +85,14 @@ def _check_all_pairs(y, q, k, v, w, gamma, state, slot_ids, g, fw, tag):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("fw,b", [(32, 48), (32, 64), (64, 48), (64, 64), (128, 48), (128, 64)])
-def test_two_tile_forward_every_pair(dev, fw, b):
-    case, w, gamma, _, slots_bad, state = _states(dev, fw, H)
-    q, k, v = synth.device_step_qkv("decode256", 0, R, dev, FW=fw, B=b)  # d = 128
+@pytest.mark.parametrize("d,fw,b", [(128, 32, 48), (128, 32, 64), (128, 64, 48), (128, 64, 64), (128, 128, 48),
+                                    (128, 128, 64), (64, 64, 64), (64, 128, 48)])
+def test_two_tile_forward_every_pair(dev, d, fw, b):
+    case, w, gamma, _, slots_bad, state = _states(dev, fw, H, d=d)
+    q, k, v = synth.device_step_qkv("decode256", 0, R, dev, FW=fw, B=b, d=d)
     y = bha.block_forward(q, k, v, w, gamma, state, slots_bad)
     torch.cuda.synchronize()
-    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, fw, f"two-tile FW={fw} B={b}")
+    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, fw, f"two-tile d={d} FW={fw} B={b}")
 
 
 @pytest.mark.parametrize("d,fw,hk", [(128, 64, 8), (128, 64, 4), (128, 64, 2), (128, 32, 4), (128, 32, 2),
@@ -120,16 +122,19 @@ def test_eight_head_groups_several_units_per_work_group(dev, d, fw):
     _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, g, fw, f"grouped d={d} FW={fw} G={g} R={nreq}")
 
 
-@pytest.mark.parametrize("d,nreq", [(128, 256), (128, 512), (64, 512)])
-def test_one_tile_forward_every_pair(dev, d, nreq):
-    # the headline kernel (B = 32, FW = 64) at the decode256 grid (two
-    # work-groups per CU, 8 pairs each), and at 512 requests (8,192 pairs: one
-    # work-group per CU, 32 pairs each), every pair
-    case, w, gamma, _, slots_bad, state = _states(dev, 64, H, R=nreq, d=d)
-    q, k, v = synth.device_step_qkv("decode256", 0, nreq, dev, d=d)
+@pytest.mark.parametrize("d,fw,nreq", [(128, 64, 256), (128, 64, 512), (128, 64, 64), (64, 64, 512),
+                                       (64, 128, 256), (64, 32, 64)])
+def test_one_tile_forward_every_pair(dev, d, fw, nreq):
+    # the headline kernel (B = 32, FW = 64) at the decode256 grid (one
+    # four-wave work-group per CU, 16 pairs each), at 512 requests (32 pairs
+    # each) and at 64 requests (two work-groups per CU, 2 pairs each); d = 64
+    # (two-wave work-groups, two or four per CU) at FW = 32, 64 and 128; every
+    # pair
+    case, w, gamma, _, slots_bad, state = _states(dev, fw, H, R=nreq, d=d)
+    q, k, v = synth.device_step_qkv("decode256", 0, nreq, dev, d=d, FW=fw)
     y = bha.block_forward(q, k, v, w, gamma, state, slots_bad)
     torch.cuda.synchronize()
-    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, 64, f"one-tile d={d} FW=64 B=32 R={nreq}")
+    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, fw, f"one-tile d={d} FW={fw} B=32 R={nreq}")
 
 
 @pytest.mark.parametrize("d,fw,nreq", [(128, 64, 256), (128, 32, 256), (128, 64, 512), (64, 64, 512), (64, 32, 256)])
