@@ -17,11 +17,12 @@ namespace {
 // and the merge and stores follow. The next pair's Q, K, V, Z loads are issued
 // right after the current ones reach LDS. The vector memory counter retires in
 // issue order, so every wait only covers loads issued before the ones still
-// streaming.
-template <int D, int FW, int KT>
+// streaming. ONE: compiled for one resident wave per SIMD (the register
+// budget of a whole SIMD) instead of fwd_wpe.
+template <int D, int FW, int KT, bool ONE>
 __global__ __launch_bounds__(64 * (D / 32))
-__attribute__((amdgpu_waves_per_eu(fwd_wpe<D, FW, KT>(), fwd_wpe<D, FW, KT>()))) void forward_mfma_kernel(
-    ForwardArgs a, int npairs)
+__attribute__((amdgpu_waves_per_eu(ONE ? 1 : fwd_wpe<D, FW, KT>(), ONE ? 1 : fwd_wpe<D, FW, KT>()))) void
+forward_mfma_kernel(ForwardArgs a, int npairs)
 {
     using C = Cfg<D, FW>;
     constexpr int F = C::F;
@@ -241,6 +242,10 @@ __global__ __launch_bounds__(2 * 64 * (D / 32)) __attribute__((amdgpu_waves_per_
 // 88.2 -> 79.9 us (FW = 64) and 65.9 -> 52.4 us (FW = 32) against one. The
 // two-tile forward, the commit, the fused step, the grouped forwards and the
 // prefill are each slower at one wave per SIMD (at 256 requests, d = 128).
+// At one wave per SIMD the d = 64 kernel is also compiled for that register
+// budget (256 VGPRs instead of 238): 39.2 -> 37.5 us at FW = 64, 256 requests,
+// and 51.7 -> 48.4 us at FW = 32, 512 requests; the d = 128 kernel so
+// compiled (272 VGPRs) was 1-2 % slower and keeps the two-wave budget.
 constexpr int kFwdOneWavePairs = 8;
 
 template <int D, int FW, int KT>
@@ -254,8 +259,10 @@ hipError_t launch_forward_kt(const ForwardArgs& a, hipStream_t s)
     NG = (NG / a.H) * a.H;
     if (NG < a.H) NG = a.H;
     if (NG > npairs) NG = npairs;
-    return launch_kernel(forward_mfma_kernel<D, FW, KT>, dim3(static_cast<uint32_t>(NG)), dim3(64 * (D / 32)), s, a,
-                         npairs);
+    const dim3 grid(static_cast<uint32_t>(NG)), block(64 * (D / 32));
+    if constexpr (D == 64 && KT == 1 && Cfg<D, FW>::WPE == 2)
+        if (wps == 1) return launch_kernel(forward_mfma_kernel<D, FW, KT, true>, grid, block, s, a, npairs);
+    return launch_kernel(forward_mfma_kernel<D, FW, KT, false>, grid, block, s, a, npairs);
 }
 
 // The split-slice F = 256 forward: one work-group of 2 NW waves per CU.

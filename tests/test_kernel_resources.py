@@ -28,9 +28,13 @@ SCRATCH_ALLOWED = {("forward_gqa_mfma_kernel", (64, 128, 4)): 80}
 
 # resident waves per SIMD the decode-size kernels are built for
 MIN_OCCUPANCY = {
-    ("forward_mfma_kernel", (128, 64, 1)): 2,
-    ("forward_mfma_kernel", (128, 32, 1)): 2,
-    ("forward_mfma_kernel", (128, 64, 2)): 2,
+    ("forward_mfma_kernel", (128, 64, 1, 0)): 2,
+    ("forward_mfma_kernel", (128, 32, 1, 0)): 2,
+    ("forward_mfma_kernel", (128, 64, 2, 0)): 2,
+    ("forward_mfma_kernel", (64, 64, 1, 0)): 2,
+    # d = 64 at one wave per SIMD, compiled for that budget
+    ("forward_mfma_kernel", (64, 64, 1, 1)): 1,
+    ("forward_mfma_kernel", (64, 32, 1, 1)): 1,
     ("forward_commit_mfma_kernel", (128, 64)): 2,
     ("commit_mfma_kernel", (128, 64)): 2,
     ("prefill_mfma_kernel", (128, 64)): 2,

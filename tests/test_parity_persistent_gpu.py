@@ -123,7 +123,7 @@ def test_eight_head_groups_several_units_per_work_group(dev, d, fw):
 
 
 @pytest.mark.parametrize("d,fw,nreq", [(128, 64, 256), (128, 64, 512), (128, 64, 64), (64, 64, 512),
-                                       (64, 128, 256), (64, 32, 64)])
+                                       (64, 32, 256), (64, 128, 256), (64, 32, 64)])
 def test_one_tile_forward_every_pair(dev, d, fw, nreq):
     # the headline kernel (B = 32, FW = 64) at the decode256 grid (one
     # four-wave work-group per CU, 16 pairs each), at 512 requests (32 pairs
