@@ -52,14 +52,16 @@ struct Cfg {
     static constexpr int PS = 32 + 4;       // padded LDS row (fp32) of phi(K)^T
     static constexpr int NSL = F / 8;       // 128-bit state loads per lane
     static constexpr int NKB = D / 16;      // k-steps over d
-    // resident work-groups per CU the persistent forward is built for: its
+    // resident waves per SIMD the persistent forward is compiled for (at
+    // d = 128, with four-wave work-groups, also work-groups per CU): its
     // register budget (state slice + one pair's working set) allows two,
     // except with F = 256 whose state slice alone takes 128 registers
     static constexpr int WPE = FW >= 128 ? 1 : 2;
 };
 
-// Resident work-groups per CU of the forward with KT key (and query) tiles.
-// At two work-groups the query tiles are kept apart by a scheduling barrier,
+// Resident waves per SIMD the forward with KT key (and query) tiles is
+// compiled for (work-groups per CU at d = 128; the launcher sizes the grid
+// from it). At two the query tiles are kept apart by a scheduling barrier,
 // so a tile's working set does not overlap the next one's; the second key
 // tile's scores and operands do not fit two work-groups' registers at
 // FW >= 64 (measured: one work-group per CU, no spills, is as fast as two

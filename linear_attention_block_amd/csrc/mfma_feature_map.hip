@@ -35,11 +35,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void feature_map_mfma_kernel(PhiArgs
     const int h = blockIdx.x / tiles;
     const int64_t ntok = static_cast<int64_t>(a.R) * a.B;
     const int64_t t0 = static_cast<int64_t>(blockIdx.x % tiles) * TOK;
-    {
-        WChunks<D, FW, NT> wc;
-        wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
-        wc.template store_rows<C::RS>(Ws, tid);
-    }
+    // W's loads and the tile rows' loads go out together; W reaches LDS once
+    // all have been issued, so the two round trips overlap
+    WChunks<D, FW, NT> wc;
+    wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
     // the tile's rows, 16 bytes per thread per step (rows past the batch read
     // its last row and are not stored)
     u32x4 xv[TOK * CH / NT];
@@ -52,6 +51,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void feature_map_mfma_kernel(PhiArgs
                               static_cast<int64_t>(h) * a.xs.head + 8 * ch;
         xv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
     }
+    wc.template store_rows<C::RS>(Ws, tid);
 #pragma unroll
     for (int i = 0; i < TOK * CH / NT; ++i) {
         const int idx = tid + i * NT, row = idx / CH, ch = idx % CH;

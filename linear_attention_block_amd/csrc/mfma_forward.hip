@@ -88,8 +88,8 @@ forward_mfma_kernel(ForwardArgs a, int npairs)
                 lacc = linear_read<D, FW>(sv, pb, sp, sn);
             }
             merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, 32 * qt + ln, g, valid);
-            // at two work-groups per CU the tiles must not overlap (registers);
-            // at one, letting them overlap is faster
+            // compiled for two waves per SIMD the tiles must not overlap
+            // (registers); for one, letting them overlap is faster
             if constexpr (fwd_wpe<D, FW, KT>() > 1) __builtin_amdgcn_sched_barrier(0);
         }
         constexpr int QL = KT - 1;
