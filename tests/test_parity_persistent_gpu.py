@@ -47,12 +47,12 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _states(dev, fw, hk, R=R, d=D):
-    """Slots, W (hk heads), and states built by one ragged prefill."""
+def _states(dev, fw, hk, R=R, d=D, nq=H):
+    """Slots, W (hk heads), gates (nq query heads), and states built by one ragged prefill."""
     case = synth.make_case("decode256", R=R, with_prefix=False, with_qkv=False, FW=fw, d=d)
     nb = np.random.default_rng(5).integers(0, 5, size=R)
     w, _ = synth.device_layer_params("decode256", 0, dev, FW=fw, H=hk, d=d)
-    _, gamma = synth.device_layer_params("decode256", 0, dev, FW=fw, H=H, d=d)
+    _, gamma = synth.device_layer_params("decode256", 0, dev, FW=fw, H=nq, d=d)
     slots = torch.from_numpy(case.slot_ids).to(dev)
     state = bha.new_state(case.num_slots, hk, d, fw, dev)
     pk, pv, offs = synth.device_packed_prefix("decode256", nb, dev, FW=fw, H=hk, d=d)
@@ -64,8 +64,8 @@ def _states(dev, fw, hk, R=R, d=D):
 
 
 def _check_all_pairs(y, q, k, v, w, gamma, state, slot_ids, g, fw, tag):
-    hk = H // g
-    R, d = q.shape[0], q.shape[3]
+    R, nq, d = q.shape[0], q.shape[2], q.shape[3]
+    hk = nq // g
     rec = state.cpu().numpy()[slot_ids]  # [R][hk][rec]
     S, Z = record_to_plain(rec, d, 2 * fw)
     rep = lambda a: np.repeat(a, g, axis=1)  # noqa: E731  K/V head -> its query heads
@@ -81,7 +81,7 @@ def _check_all_pairs(y, q, k, v, w, gamma, state, slot_ids, g, fw, tag):
     err = normwise_err(yh[good], ref[good], (2, 3))
     cus = torch.cuda.get_device_properties(y.device).multi_processor_count
     print(f"[{tag}] {R * hk} units on a persistent grid over {cus} CUs: err {err:.2e} over all "
-          f"{int(good.sum()) * H} (request, query head) pairs", flush=True)
+          f"{int(good.sum()) * nq} (request, query head) pairs", flush=True)
     assert err <= TOL
 
 
@@ -120,6 +120,19 @@ def test_eight_head_groups_several_units_per_work_group(dev, d, fw):
     y = bha.block_forward_gqa(q, k, v, w, gamma, state, slots_bad)
     torch.cuda.synchronize()
     _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, g, fw, f"grouped d={d} FW={fw} G={g} R={nreq}")
+
+
+@pytest.mark.parametrize("nheads,nreq", [(20, 128), (12, 192)])
+def test_one_tile_forward_every_pair_other_head_counts(dev, nheads, nreq):
+    # the persistent grid is rounded down to a multiple of H so that a
+    # work-group keeps one head: at one wave per SIMD (d = 128, 256 CUs)
+    # 20 heads give 240 work-groups (10 or 11 pairs each) and 12 give 252
+    # (9 or 10), so work-groups end after different numbers of pairs
+    case, w, gamma, _, slots_bad, state = _states(dev, 64, nheads, R=nreq, nq=nheads)
+    q, k, v = synth.device_step_qkv("decode256", 0, nreq, dev, H=nheads)
+    y = bha.block_forward(q, k, v, w, gamma, state, slots_bad)
+    torch.cuda.synchronize()
+    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, 64, f"one-tile H={nheads} R={nreq}")
 
 
 @pytest.mark.parametrize("d,fw,nreq", [(128, 64, 256), (128, 64, 512), (128, 64, 64), (64, 64, 512),
