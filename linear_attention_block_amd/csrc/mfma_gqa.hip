@@ -100,10 +100,12 @@ __attribute__((amdgpu_waves_per_eu(gqa_wpe<D, FW, G>(), gqa_wpe<D, FW, G>()))) v
         return a.state + (static_cast<int64_t>(ok ? sl : 0) * HK + u % HK) * static_cast<int64_t>(D + 1) * F;
     };
     constexpr bool SYNC = gqa_sync_operands<D, FW, G>();
-    if constexpr (!SYNC) op.load(a, p, slot_of(p), tid);
-    __builtin_amdgcn_sched_barrier(0);
-    load_state_slice((SYNC ? rec_of(p, slot_of(p)) : op.rec) + wv * F * 32, lane, sv);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!SYNC) {
+        op.load(a, p, slot_of(p), tid);
+        __builtin_amdgcn_sched_barrier(0);
+        load_state_slice(op.rec + wv * F * 32, lane, sv);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     int slot_cur = slot_of(p);
     int slot_next = slot_of(p + NG);
     for (int k = 0; k < count; ++k) {
@@ -115,6 +117,10 @@ __attribute__((amdgpu_waves_per_eu(gqa_wpe<D, FW, G>(), gqa_wpe<D, FW, G>()))) v
         if constexpr (SYNC) op.load(a, p, __builtin_amdgcn_readfirstlane(slot_cur), tid);
         const bool valid = op.valid;
         op.store_to(Qs, Ks, sm.Vs, sm.Zs, tid);
+        // SYNC: the first unit's slice goes out once its operands are in, so
+        // that phase one runs while it arrives (later units' slices are
+        // issued a unit ahead)
+        if (SYNC && k == 0) load_state_slice(rec_of(p, __builtin_amdgcn_readfirstlane(slot_cur)) + wv * F * 32, lane, sv);
         __syncthreads();
         if constexpr (!SYNC) op.load(a, pn, __builtin_amdgcn_readfirstlane(slot_next), tid, live);
 
