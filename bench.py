@@ -52,6 +52,21 @@ KERNEL_SOURCES = tuple(f"linear_attention_block_amd/csrc/{f}" for f in (
     "mfma_prefill.hip", "mfma_feature_map.hip", "bha_device.hpp", "bha_internal.hpp", "bha_mfma.hpp"))
 
 
+def forward_kernel_name(d, FW, B, npairs, dev):
+    """The matrix-core kernel bha_block_forward runs for B <= 32 (one query
+    head per K/V head), as the launcher chooses it: the split-slice kernel at
+    d = 128, FW = 128; otherwise the persistent one-tile kernel, compiled for
+    one wave per SIMD at d = 64, FW <= 64 when it runs that grid (from 8 pairs
+    per CU)."""
+    import torch
+
+    if d == 128 and FW == 128:
+        return "forward_split_kernel<128>"
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    one = d == 64 and FW <= 64 and npairs >= 8 * cus
+    return f"forward_mfma_kernel<{d},{FW},1,{'true' if one else 'false'}>"
+
+
 def forward_bytes(R, H, d, FW, B, es=2):
     """Algorithmic HBM bytes of one bha_block_forward launch: per (request, head)
     the fp32 S tiles and Z (read), Q, K, V (read) and O (written); W once per head."""
@@ -816,7 +831,7 @@ def main() -> int:
                         f"bha_block_forward_commit: forward_generic_kernel<float,{d},{FW}> then "
                         f"commit_generic_kernel<float,{d},{FW}> (1/{nd} of requests commit per launch)")
                        if args.staggered else
-                       f"bha_block_forward: forward_mfma_kernel<{d},{FW},1> (persistent, bf16 MFMA)"
+                       f"bha_block_forward: {forward_kernel_name(d, FW, B, R * H, dev)} (persistent, bf16 MFMA)"
                        if args.io == "bf16" else
                        f"bha_block_forward: forward_generic_kernel<float,{d},{FW}> (fp32 MFMA)"),
             "bytes_per_launch": fb,
