@@ -8,10 +8,13 @@ namespace {
 // ---------------------------------------------------------------------------
 // Feature map (bha_feature_map, bf16 tokens)
 // ---------------------------------------------------------------------------
-// One work-group of D/32 waves per (head, 32 D/32 consecutive tokens of the
-// [R][B] batch). W_h and the tokens' rows go to LDS; each wave then takes 32
-// tokens: u^T = W^T X^T on the matrix cores (lane = token, as in the
-// forward) and both softmaxes of each token in fp32 (lanes n and n + 32 hold
+// Persistent: units are (tile of 32 D/32 consecutive tokens of the [R][B]
+// batch, head), unit u = tile u / H of head u % H, and work-group b takes
+// units b, b + NG, ... (NG a multiple of H, so W_h is loaded once). The next
+// unit's rows are loaded into registers while the current one is computed.
+// A unit's rows go to LDS beside W_h; each wave then takes 32 tokens:
+// u^T = W^T X^T on the matrix cores (lane = token, as in the forward) and
+// both softmaxes of each token in fp32 (lanes n and n + 32 hold
 // halves of token n's logits). phi leaves through the wave's own 32 rows of
 // the X tile, which the logits no longer need: a piece of CW features of
 // every token at a time is written there from the accumulator layout and read
@@ -21,7 +24,7 @@ namespace {
 // Roofline: HBM. Algorithmic bytes per (token, head): the row read (2 d) and
 // phi written (4 F); W once per head per launch.
 template <int D, int FW>
-__global__ __launch_bounds__(64 * (D / 32)) void feature_map_mfma_kernel(PhiArgs a, int tiles)
+__global__ __launch_bounds__(64 * (D / 32)) void feature_map_mfma_kernel(PhiArgs a, int nunits)
 {
     using C = Cfg<D, FW>;
     constexpr int NT = C::NT, TOK = 32 * C::NW, CH = D / 8, F = C::F;
@@ -32,84 +35,95 @@ __global__ __launch_bounds__(64 * (D / 32)) void feature_map_mfma_kernel(PhiArgs
     __shared__ alignas(16) uint16_t Ws[FW * C::RS];
     __shared__ alignas(16) uint16_t Xs[TOK * C::RS];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, ln = lane & 31, g = lane >> 5;
-    const int h = blockIdx.x / tiles;
+    const int NG = gridDim.x;  // a multiple of H: every unit of a work-group has its head
+    int unit = blockIdx.x;    // tile unit / H of head unit % H
+    if (unit >= nunits) return;
+    const int h = unit % a.H;
     const int64_t ntok = static_cast<int64_t>(a.R) * a.B;
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x % tiles) * TOK;
-    // W's loads and the tile rows' loads go out together; W reaches LDS once
-    // all have been issued, so the two round trips overlap
     WChunks<D, FW, NT> wc;
     wc.load(static_cast<const uint16_t*>(a.w) + static_cast<int64_t>(h) * a.wh, tid);
-    // the tile's rows, 16 bytes per thread per step (rows past the batch read
+    // a tile's rows, 16 bytes per thread per step (rows past the batch read
     // its last row and are not stored)
     u32x4 xv[TOK * CH / NT];
+    auto load_x = [&](int uu) {
+        const int64_t tt0 = static_cast<int64_t>(uu / a.H) * TOK;
 #pragma unroll
-    for (int i = 0; i < TOK * CH / NT; ++i) {
-        const int idx = tid + i * NT, row = idx / CH, ch = idx % CH;
-        const int64_t tk = t0 + row < ntok ? t0 + row : ntok - 1;
-        const int64_t r = tk / a.B, t = tk % a.B;
-        const uint16_t* src = static_cast<const uint16_t*>(a.x) + r * a.xs.req + t * a.xs.tok +
-                              static_cast<int64_t>(h) * a.xs.head + 8 * ch;
-        xv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-    }
+        for (int i = 0; i < TOK * CH / NT; ++i) {
+            const int idx = tid + i * NT, row = idx / CH, ch = idx % CH;
+            const int64_t tk = tt0 + row < ntok ? tt0 + row : ntok - 1;
+            const int64_t r = tk / a.B, t = tk % a.B;
+            const uint16_t* src = static_cast<const uint16_t*>(a.x) + r * a.xs.req + t * a.xs.tok +
+                                  static_cast<int64_t>(h) * a.xs.head + 8 * ch;
+            xv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+        }
+    };
+    // W_h's loads and the first unit's rows go out together; W_h reaches LDS
+    // once all have been issued
+    load_x(unit);
     wc.template store_rows<C::RS>(Ws, tid);
+    for (; unit < nunits; unit += NG) {
+        const int64_t t0 = static_cast<int64_t>(unit / a.H) * TOK;
+        __syncthreads();  // the previous unit's staged pieces are read
 #pragma unroll
-    for (int i = 0; i < TOK * CH / NT; ++i) {
-        const int idx = tid + i * NT, row = idx / CH, ch = idx % CH;
-        *reinterpret_cast<u32x4*>(Xs + row * C::RS + 8 * ch) = xv[i];
-    }
-    __syncthreads();
-    f32x16 u[FW / 32];
-    feature_logits<D, FW, C::RS>(Ws, Xs + 32 * wv * C::RS, ln, g, u);
-    constexpr float kLog2e = 1.4426950408889634f;
-#pragma unroll
-    for (int T = 0; T < FW / 32; ++T)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) u[T][v] *= kLog2e;  // base-2 logits
-    float mx, mn;
-    logit_range<FW>(u, mx, mn);
-    float sp = 0.0f, sn = 0.0f;
-    f32x16 en[FW / 32];
-#pragma unroll
-    for (int T = 0; T < FW / 32; ++T)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float x = u[T][v];
-            u[T][v] = __builtin_amdgcn_exp2f(x - mx);
-            en[T][v] = __builtin_amdgcn_exp2f(mn - x);
-            sp += u[T][v];
-            sn += en[T][v];
+        for (int i = 0; i < TOK * CH / NT; ++i) {
+            const int idx = tid + i * NT, row = idx / CH, ch = idx % CH;
+            *reinterpret_cast<u32x4*>(Xs + row * C::RS + 8 * ch) = xv[i];
         }
-    sp += __shfl_xor(sp, 32, 64);
-    sn += __shfl_xor(sn, 32, 64);
-    const float ip = 1.0f / sp, in = 1.0f / sn;
-    float* const stage = reinterpret_cast<float*>(Xs + 32 * wv * C::RS);  // this wave's X rows
-    const int64_t tw = t0 + 32 * wv;  // the wave's first token
-    // piece (half hf, features c0 .. c0 + CW - 1 of that half)
+        __syncthreads();
+        if (unit + NG < nunits) load_x(unit + NG);  // the next unit's rows stream in during this one
+        f32x16 u[FW / 32];
+        feature_logits<D, FW, C::RS>(Ws, Xs + 32 * wv * C::RS, ln, g, u);
+        constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+        for (int T = 0; T < FW / 32; ++T)
 #pragma unroll
-        for (int c0 = 0; c0 < FW; c0 += CW) {
-            __syncthreads();  // the previous piece's reads (or the logits' reads of X) are done
+            for (int v = 0; v < 16; ++v) u[T][v] *= kLog2e;  // base-2 logits
+        float mx, mn;
+        logit_range<FW>(u, mx, mn);
+        float sp = 0.0f, sn = 0.0f;
+        f32x16 en[FW / 32];
 #pragma unroll
-            for (int T = c0 / 32; T < (c0 + CW) / 32; ++T)
+        for (int T = 0; T < FW / 32; ++T)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    f32x4 pv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) pv[e] = hf ? en[T][4 * q4 + e] * in : u[T][4 * q4 + e] * ip;
-                    *reinterpret_cast<f32x4*>(stage + ln * CS + 32 * T - c0 + 8 * q4 + 4 * g) = pv;
-                }
-            __syncthreads();
-            // rows of CW floats, CW / 4 lanes per row
-#pragma unroll
-            for (int i = 0; i < 32 * CW / 4 / 64; ++i) {
-                const int idx = lane + 64 * i, row = idx / (CW / 4), c4 = idx % (CW / 4);
-                const int64_t tk = tw + row;
-                if (tk < ntok)
-                    *reinterpret_cast<f32x4*>(a.phi + (tk * a.H + h) * F + hf * FW + c0 + 4 * c4) =
-                        *reinterpret_cast<const f32x4*>(stage + row * CS + 4 * c4);
+            for (int v = 0; v < 16; ++v) {
+                const float x = u[T][v];
+                u[T][v] = __builtin_amdgcn_exp2f(x - mx);
+                en[T][v] = __builtin_amdgcn_exp2f(mn - x);
+                sp += u[T][v];
+                sn += en[T][v];
             }
-        }
+        sp += __shfl_xor(sp, 32, 64);
+        sn += __shfl_xor(sn, 32, 64);
+        const float ip = 1.0f / sp, in = 1.0f / sn;
+        float* const stage = reinterpret_cast<float*>(Xs + 32 * wv * C::RS);  // this wave's X rows
+        const int64_t tw = t0 + 32 * wv;  // the wave's first token
+        // piece (half hf, features c0 .. c0 + CW - 1 of that half)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int c0 = 0; c0 < FW; c0 += CW) {
+                __syncthreads();  // the previous piece's reads (or the logits' reads of X) are done
+#pragma unroll
+                for (int T = c0 / 32; T < (c0 + CW) / 32; ++T)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        f32x4 pv;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) pv[e] = hf ? en[T][4 * q4 + e] * in : u[T][4 * q4 + e] * ip;
+                        *reinterpret_cast<f32x4*>(stage + ln * CS + 32 * T - c0 + 8 * q4 + 4 * g) = pv;
+                    }
+                __syncthreads();
+                // rows of CW floats, CW / 4 lanes per row
+#pragma unroll
+                for (int i = 0; i < 32 * CW / 4 / 64; ++i) {
+                    const int idx = lane + 64 * i, row = idx / (CW / 4), c4 = idx % (CW / 4);
+                    const int64_t tk = tw + row;
+                    if (tk < ntok)
+                        *reinterpret_cast<f32x4*>(a.phi + (tk * a.H + h) * F + hf * FW + c0 + 4 * c4) =
+                            *reinterpret_cast<const f32x4*>(stage + row * CS + 4 * c4);
+                }
+            }
+    }
 }
 
 template <int D>
@@ -117,8 +131,14 @@ hipError_t feature_map_by_fw(const PhiArgs& a, hipStream_t s)
 {
     constexpr int TOK = 32 * (D / 32);
     const int64_t tiles = (static_cast<int64_t>(a.R) * a.B + TOK - 1) / TOK;
-    const dim3 grid(static_cast<uint32_t>(tiles * a.H)), block(64 * (D / 32));
-    const int nt = static_cast<int>(tiles);
+    const int nunits = static_cast<int>(tiles * a.H);
+    // two waves per SIMD (two four-wave work-groups per CU at d = 128)
+    int64_t NG = static_cast<int64_t>(compute_units()) * 2 * 4 / (D / 32);
+    NG = (NG / a.H) * a.H;
+    if (NG < a.H) NG = a.H;
+    if (NG > nunits) NG = nunits;
+    const dim3 grid(static_cast<uint32_t>(NG)), block(64 * (D / 32));
+    const int nt = nunits;
     switch (a.FW) {
         case 32: return launch_kernel(feature_map_mfma_kernel<D, 32>, grid, block, s, a, nt);
         case 64: return launch_kernel(feature_map_mfma_kernel<D, 64>, grid, block, s, a, nt);

@@ -12,7 +12,8 @@ bytes the kernel read. One request carries an out-of-range slot in the middle
 of the batch: its rows must come out NaN while the pairs around it, whose
 look-ahead loads run through it, stay exact.
 
-Covered: blocks of 48 and 64 tokens (two 32-token query tiles) at FW = 32, 64
+Also the feature map at 256 x 32 tokens x 16 heads (several tiles per
+work-group) and with a ragged last tile. Covered: blocks of 48 and 64 tokens (two 32-token query tiles) at FW = 32, 64
 and 128 (d = 128, and d = 64 at FW = 64 and 128); grouped K/V heads with 2, 4
 and 8 query heads per K/V head; the one-tile forward at 64, 256 and 512
 requests (d = 128) and d = 64 at FW = 32, 64 and 128; the commit at 256 and
@@ -133,6 +134,25 @@ def test_one_tile_forward_every_pair_other_head_counts(dev, nheads, nreq):
     y = bha.block_forward(q, k, v, w, gamma, state, slots_bad)
     torch.cuda.synchronize()
     _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, 64, f"one-tile H={nheads} R={nreq}")
+
+
+@pytest.mark.parametrize("d,fw,nreq,b", [(128, 64, 256, 32), (128, 64, 255, 31), (64, 32, 256, 32)])
+def test_feature_map_every_token(dev, d, fw, nreq, b):
+    # the persistent feature map at production size: 128-token (64 at
+    # d = 64) tiles x 16 heads on two waves per SIMD, two units per
+    # work-group (some one, with a ragged last tile, at 255 x 31 tokens);
+    # every token and head against the oracle's phi
+    case = synth.make_case("decode256", R=nreq, with_prefix=False, with_qkv=False, FW=fw, d=d, B=b)
+    w, _ = synth.device_layer_params("decode256", 0, dev, FW=fw, d=d)
+    x = synth.device_step_qkv("decode256", 0, nreq, dev, FW=fw, d=d, B=b)[0]
+    phi = to_host(bha.feature_map(x, w))  # [R][B][H][2 FW]
+    xh, wh = to_host(x), to_host(w)
+    ref = np.empty_like(phi)
+    for h in range(H):
+        ref[:, :, h] = oracle.phi(xh[:, :, h].reshape(-1, d), wh[h]).reshape(nreq, b, 2 * fw)
+    err = normwise_err(phi, ref, (3,))
+    print(f"[feature map d={d} FW={fw} {nreq} x {b} tokens x {H} heads] err {err:.2e}", flush=True)
+    assert err <= 1e-5
 
 
 @pytest.mark.parametrize("d,fw,nreq", [(128, 64, 256), (128, 64, 512), (128, 64, 64), (64, 64, 512),
