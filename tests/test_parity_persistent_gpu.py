@@ -136,6 +136,36 @@ def test_one_tile_forward_every_pair_other_head_counts(dev, nheads, nreq):
     _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, 1, 64, f"one-tile H={nheads} R={nreq}")
 
 
+def _draw_grid_case(seed):
+    rng = np.random.default_rng(9100 + seed)
+    d = int(rng.choice([64, 128]))
+    fw = int(rng.choice([32, 64]))
+    g = int(rng.choice([1, 1, 2, 4, 8]))
+    b = int(rng.integers(1, 65 if g == 1 else 33))
+    hk = int(rng.integers(8, 25)) if g == 1 else int(rng.integers(1, 32 // g + 1))
+    nreq = int(rng.integers(64, 401))
+    return dict(d=d, fw=fw, g=g, b=b, hk=hk, nq=hk * g, nreq=nreq)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes_on_production_grids(dev, seed):
+    # seeded shapes whose pair counts fall on both sides of the
+    # one-wave-per-SIMD threshold (8 pairs per CU), with head counts that do
+    # not divide the grid evenly: the one-tile, two-tile and grouped forwards
+    # (1, 2, 4 or 8 query heads per K/V head), every pair against the oracle
+    c = _draw_grid_case(seed)
+    d, fw, g, b, hk, nq, nreq = c["d"], c["fw"], c["g"], c["b"], c["hk"], c["nq"], c["nreq"]
+    case, w, gamma, _, slots_bad, state = _states(dev, fw, hk, R=nreq, d=d, nq=nq)
+    q = synth.device_step_qkv("decode256", 0, nreq, dev, FW=fw, d=d, B=b, H=nq)[0]
+    _, k, v = synth.device_step_qkv("decode256", 0, nreq, dev, FW=fw, d=d, B=b, H=hk)
+    if g == 1:
+        y = bha.block_forward(q, k, v, w, gamma, state, slots_bad)
+    else:
+        y = bha.block_forward_gqa(q, k, v, w, gamma, state, slots_bad)
+    torch.cuda.synchronize()
+    _check_all_pairs(y, q, k, v, w, gamma, state, case.slot_ids, g, fw, f"random grid case {seed}: {c}")
+
+
 @pytest.mark.parametrize("d,fw,nreq,b", [(128, 64, 256, 32), (128, 64, 255, 31), (64, 32, 256, 32)])
 def test_feature_map_every_token(dev, d, fw, nreq, b):
     # the persistent feature map at production size: 128-token (64 at
