@@ -57,13 +57,13 @@ def forward_kernel_name(d, FW, B, npairs, dev):
     head per K/V head), as the launcher chooses it: the split-slice kernel at
     d = 128, FW = 128; otherwise the persistent one-tile kernel, compiled for
     one wave per SIMD at d = 64, FW <= 64 when it runs that grid (from 8 pairs
-    per CU)."""
+    per CU, blocks of more than 16 tokens)."""
     import torch
 
     if d == 128 and FW == 128:
         return "forward_split_kernel<128>"
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    one = d == 64 and FW <= 64 and npairs >= 8 * cus
+    one = d == 64 and FW <= 64 and B > 16 and npairs >= 8 * cus
     return f"forward_mfma_kernel<{d},{FW},1,{'true' if one else 'false'}>"
 
 

@@ -230,10 +230,10 @@ __global__ __launch_bounds__(2 * 64 * (D / 32)) __attribute__((amdgpu_waves_per_
 // (what the kernel's registers allow), that is fwd_wpe * 4 / (D / 32)
 // work-groups of D / 32 waves per CU, rounded down to a multiple of H so that
 // each work-group keeps one head, and no more than there are pairs. With at
-// least kFwdOneWavePairs pairs per CU the one-tile forward runs one wave per
-// SIMD instead of two: each pair's chain of loads, products and stores then
-// has its SIMD to itself and the memory system streams more with half the
-// state slices in flight. Measured at FW = 64, B = 32, six rotating state
+// least kFwdOneWavePairs pairs per CU and blocks of more than kFwdOneWaveRows
+// tokens the one-tile forward runs one wave per SIMD instead of two: each
+// pair's chain of loads, products and stores then has its SIMD to itself and
+// the memory system streams more with half the state slices in flight. Measured at FW = 64, B = 32, six rotating state
 // pools, d = 128 (one work-group per CU against two): 128 requests x 16
 // heads 38.6 -> 37.9 us, 192: 54.4 -> 51.3 us, 256: 72.7-72.9 -> 67.1-70.0
 // us, 384: 110.2 -> 100.3 us, 512: 149.3 -> 133.3 us; FW = 32, 256 requests
@@ -247,6 +247,11 @@ __global__ __launch_bounds__(2 * 64 * (D / 32)) __attribute__((amdgpu_waves_per_
 // and 51.7 -> 48.4 us at FW = 32, 512 requests; the d = 128 kernel so
 // compiled (272 VGPRs) was 1-2 % slower and keeps the two-wave budget.
 constexpr int kFwdOneWavePairs = 8;
+// Smaller blocks keep two waves per SIMD, where each pair's chain is short
+// and a second wave covers its latency (256 requests, FW = 32: B = 8
+// 41.0 -> 37.7 us and B = 16 43.4 -> 41.1 us at two; FW = 64: B = 8 61.6 ->
+// 59.8 us, B = 16 even, B = 24 even, B = 32 69.7 -> 73.4 us).
+constexpr int kFwdOneWaveRows = 16;
 
 template <int D, int FW, int KT>
 hipError_t launch_forward_kt(const ForwardArgs& a, hipStream_t s)
@@ -254,7 +259,7 @@ hipError_t launch_forward_kt(const ForwardArgs& a, hipStream_t s)
     const int npairs = a.R * a.H;
     const int cus = compute_units();
     int wps = fwd_wpe<D, FW, KT>();  // resident waves per SIMD
-    if (KT == 1 && npairs >= static_cast<int64_t>(kFwdOneWavePairs) * cus) wps = 1;
+    if (KT == 1 && a.B > kFwdOneWaveRows && npairs >= static_cast<int64_t>(kFwdOneWavePairs) * cus) wps = 1;
     int64_t NG = static_cast<int64_t>(cus) * wps * 4 / (D / 32);
     NG = (NG / a.H) * a.H;
     if (NG < a.H) NG = a.H;
