@@ -84,7 +84,10 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
         }
     __syncthreads();
 
-    // dS = phi(K)^T V: rows f, this wave's 32 columns; fold into the loaded slice
+    f32x4* dst = reinterpret_cast<f32x4*>(rec + wv * F * 32) + lane;
+    // dS = phi(K)^T V: rows f, this wave's 32 columns; fold into the loaded
+    // slice. Each 32-row tile is stored as soon as its dS is added, so the
+    // first tiles' stores overlap the later tiles' products
 #pragma unroll
     for (int ft = 0; ft < F / 32; ++ft) {
         f32x16 acc = f32x16{};
@@ -103,10 +106,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) sv[4 * ft + (v >> 2)][v & 3] += acc[v];
-    }
-    f32x4* dst = reinterpret_cast<f32x4*>(rec + wv * F * 32) + lane;
 #pragma unroll
-    for (int t = 0; t < C::NSL; ++t) __builtin_nontemporal_store(sv[t], dst + t * 64);
+        for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(sv[4 * ft + i], dst + (4 * ft + i) * 64);
+    }
 
     // dZ = sum_t phi(k_t), fp32 from the LDS copy
 #pragma unroll

@@ -90,8 +90,11 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
     }
     __syncthreads();
 
+    float* rec = const_cast<float*>(op.rec);
+    f32x4* dst = reinterpret_cast<f32x4*>(rec + wv * F * 32) + lane;
     // dS = phi(K)^T V into the slice: A from phi(K)^T rows with the token
-    // order of vt_frag (16 kb + 4 g + {0..3}, 16 kb + 8 + 4 g + {0..3})
+    // order of vt_frag (16 kb + 4 g + {0..3}, 16 kb + 8 + 4 g + {0..3}); each
+    // 32-row tile is stored as soon as its dS is added
 #pragma unroll
     for (int ft = 0; ft < F / 32; ++ft) {
         f32x16 acc = f32x16{};
@@ -110,11 +113,9 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) sv[4 * ft + (v >> 2)][v & 3] += acc[v];
-    }
-    float* rec = const_cast<float*>(op.rec);
-    f32x4* dst = reinterpret_cast<f32x4*>(rec + wv * F * 32) + lane;
 #pragma unroll
-    for (int t = 0; t < C::NSL; ++t) __builtin_nontemporal_store(sv[t], dst + t * 64);
+        for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(sv[4 * ft + i], dst + (4 * ft + i) * 64);
+    }
     // Z as loaded for the forward (its LDS copy), plus the block's phi sums:
     // the work-group ends with stores only
     for (int f = tid; f < F; f += C::NT) {
