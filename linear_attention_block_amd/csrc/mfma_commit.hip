@@ -84,7 +84,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
         }
     __syncthreads();
 
-    f32x4* dst = reinterpret_cast<f32x4*>(rec + wv * F * 32) + lane;
+    // this wave's slice: load t of lane l at byte 16 (64 t + l)
+    const __amdgpu_buffer_rsrc_t dst = wave_buffer(rec + wv * F * 32, C::NSL * 1024);
     // dS = phi(K)^T V: rows f, this wave's 32 columns; fold into the loaded
     // slice. Each 32-row tile is stored as soon as its dS is added, so the
     // first tiles' stores overlap the later tiles' products
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
 #pragma unroll
         for (int v = 0; v < 16; ++v) sv[4 * ft + (v >> 2)][v & 3] += acc[v];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(sv[4 * ft + i], dst + (4 * ft + i) * 64);
+        for (int i = 0; i < 4; ++i) store_nt_sc1(sv[4 * ft + i], dst, 16 * lane + 1024 * (4 * ft + i));
     }
 
     // dZ = sum_t phi(k_t), fp32 from the LDS copy

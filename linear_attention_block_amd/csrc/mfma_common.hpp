@@ -564,6 +564,40 @@ __device__ __forceinline__ void merge_to_lds(const ForwardArgs& a, const f32x16&
     }
 }
 
+// The state slices that the commit and the fused step write back go out
+// non-temporal at device scope (the NT and SC1 cache-policy bits), which a
+// plain global store cannot carry, so they are buffer stores. Measured
+// against non-temporal global stores at 256 x 16 pairs, d = 128, FW = 64,
+// alternated on two boxes, same bits: commit 111.1 -> 109.7 us, forward +
+// commit 130.4 -> 125.5 us; device scope without NT 116.7-117.1 us, NT with
+// SC0 no different from NT alone. The loads keep NT alone (the forward with
+// its state slices read under the other policies measured the same). The
+// feature map's rows so stored gained only in its fastest launches and the
+// buffer offsets cost registers past occupancy steps at other shapes, so it
+// keeps global stores.
+constexpr int kStoreNtSc1 = 2 | 16;  // cache policy: NT (SLC) | SC1 (SCC)
+
+// A raw buffer resource over `bytes` bytes from `base`, which must be the
+// same in every lane of the wave (its halves are read from the first lane,
+// as unsigned words: sign-extending the low word would corrupt the address).
+// Stores at offsets at or past `bytes` are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_buffer(void* base, uint32_t bytes)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(v))));
+    const uint32_t hi =
+        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(v >> 32))));
+    void* const p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(lo));
+    // word 3: 32-bit data format, no index stride, no thread-id addressing
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// 16-byte non-temporal, device-scope store at byte offset `off` of `r`.
+__device__ __forceinline__ void store_nt_sc1(const f32x4& x, __amdgpu_buffer_rsrc_t r, int off)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, kStoreNtSc1);
+}
+
 // The B output rows of the tile, 16 bytes per thread per step, whole rows
 // per store instruction (non-temporal: full lines).
 template <int D, int NT>

@@ -91,7 +91,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
     __syncthreads();
 
     float* rec = const_cast<float*>(op.rec);
-    f32x4* dst = reinterpret_cast<f32x4*>(rec + wv * F * 32) + lane;
+    const __amdgpu_buffer_rsrc_t dst = wave_buffer(rec + wv * F * 32, C::NSL * 1024);
     // dS = phi(K)^T V into the slice: A from phi(K)^T rows with the token
     // order of vt_frag (16 kb + 4 g + {0..3}, 16 kb + 8 + 4 g + {0..3}); each
     // 32-row tile is stored as soon as its dS is added
@@ -114,7 +114,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
 #pragma unroll
         for (int v = 0; v < 16; ++v) sv[4 * ft + (v >> 2)][v & 3] += acc[v];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(sv[4 * ft + i], dst + (4 * ft + i) * 64);
+        for (int i = 0; i < 4; ++i) store_nt_sc1(sv[4 * ft + i], dst, 16 * lane + 1024 * (4 * ft + i));
     }
     // Z as loaded for the forward (its LDS copy), plus the block's phi sums:
     // the work-group ends with stores only
