@@ -84,6 +84,16 @@ def forward_kernel_name(d, FW, B, npairs, dev):
     return f"forward_mfma_kernel<{d},{FW},1,{'true' if one else 'false'}>"
 
 
+def state_store_scope(FW, npairs, dev) -> str:
+    """The template flag the commit and fused-step launchers choose for the
+    state write-back: device-scope non-temporal stores at F <= 128 from 16
+    pairs per CU, non-temporal alone otherwise."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    return "true" if FW <= 64 and npairs >= 16 * cus else "false"
+
+
 def forward_bytes(R, H, d, FW, B, es=2):
     """Algorithmic HBM bytes of one bha_block_forward launch: per (request, head)
     the fp32 S tiles and Z (read), Q, K, V (read) and O (written); W once per head."""
@@ -843,7 +853,8 @@ def main() -> int:
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": (None if args.staggered or args.io != "bf16" or args.requests
                         else read_traffic(args.config)),
-            "kernel": ((f"bha_block_forward_commit: forward_commit_mfma_kernel<{d},{FW}> (1/{nd} of requests "
+            "kernel": ((f"bha_block_forward_commit: forward_commit_mfma_kernel<{d},{FW},"
+                        f"{state_store_scope(FW, R * H, dev)}> (1/{nd} of requests "
                         f"commit per launch)" if args.io == "bf16" else
                         f"bha_block_forward_commit: forward_generic_kernel<float,{d},{FW}> then "
                         f"commit_generic_kernel<float,{d},{FW}> (1/{nd} of requests commit per launch)")
@@ -871,7 +882,8 @@ def main() -> int:
             "frac": cb / com_avg / 1e9 / PEAK_HBM_GBS,
         },
         "standalone_commit": None if com_ms is None else {
-            "kernel": (f"bha_state_commit: commit_mfma_kernel<{d},{FW}>" if args.io == "bf16" and B <= 32
+            "kernel": (f"bha_state_commit: commit_mfma_kernel<{d},{FW},{state_store_scope(FW, R * H, dev)}>"
+                       if args.io == "bf16" and B <= 32
                        else "bha_state_commit"),
             "avg_launch_us": com_ms * 1e3,
             "bytes_per_launch": scb,

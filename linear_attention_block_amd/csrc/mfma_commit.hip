@@ -8,7 +8,7 @@ namespace {
 // ---------------------------------------------------------------------------
 // Commit
 // ---------------------------------------------------------------------------
-template <int D, int FW>
+template <int D, int FW, bool DEV>
 __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a)
 {
     using C = Cfg<D, FW>;
@@ -84,8 +84,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
         }
     __syncthreads();
 
-    // this wave's slice: load t of lane l at byte 16 (64 t + l)
-    const __amdgpu_buffer_rsrc_t dst = wave_buffer(rec + wv * F * 32, C::NSL * 1024);
+    float* const slice = rec + wv * F * 32;  // this wave's slice
     // dS = phi(K)^T V: rows f, this wave's 32 columns; fold into the loaded
     // slice. Each 32-row tile is stored as soon as its dS is added, so the
     // first tiles' stores overlap the later tiles' products
@@ -108,7 +107,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void commit_mfma_kernel(CommitArgs a
 #pragma unroll
         for (int v = 0; v < 16; ++v) sv[4 * ft + (v >> 2)][v & 3] += acc[v];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) store_nt_sc1(sv[4 * ft + i], dst, 16 * lane + 1024 * (4 * ft + i));
+        for (int i = 0; i < 4; ++i) store_state<DEV, C::NSL>(sv[4 * ft + i], slice, lane, 4 * ft + i);
     }
 
     // dZ = sum_t phi(k_t), fp32 from the LDS copy
@@ -132,10 +131,15 @@ template <int D>
 hipError_t commit_by_fw(const CommitArgs& a, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>(a.R * a.H)), block(64 * (D / 32));
+    const bool dev = static_cast<int64_t>(a.R) * a.H >= static_cast<int64_t>(kDevScopePairsPerCu) * compute_units();
     switch (a.FW) {
-        case 32: return launch_kernel(commit_mfma_kernel<D, 32>, grid, block, s, a);
-        case 64: return launch_kernel(commit_mfma_kernel<D, 64>, grid, block, s, a);
-        default: return launch_kernel(commit_mfma_kernel<D, 128>, grid, block, s, a);
+        case 32:
+            return dev ? launch_kernel(commit_mfma_kernel<D, 32, true>, grid, block, s, a)
+                       : launch_kernel(commit_mfma_kernel<D, 32, false>, grid, block, s, a);
+        case 64:
+            return dev ? launch_kernel(commit_mfma_kernel<D, 64, true>, grid, block, s, a)
+                       : launch_kernel(commit_mfma_kernel<D, 64, false>, grid, block, s, a);
+        default: return launch_kernel(commit_mfma_kernel<D, 128, false>, grid, block, s, a);
     }
 }
 

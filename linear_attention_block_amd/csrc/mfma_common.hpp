@@ -564,18 +564,25 @@ __device__ __forceinline__ void merge_to_lds(const ForwardArgs& a, const f32x16&
     }
 }
 
-// The state slices that the commit and the fused step write back go out
-// non-temporal at device scope (the NT and SC1 cache-policy bits), which a
-// plain global store cannot carry, so they are buffer stores. Measured
-// against non-temporal global stores at 256 x 16 pairs, d = 128, FW = 64,
-// alternated on two boxes, same bits: commit 111.1 -> 109.7 us, forward +
-// commit 130.4 -> 125.5 us; device scope without NT 116.7-117.1 us, NT with
-// SC0 no different from NT alone. The loads keep NT alone (the forward with
-// its state slices read under the other policies measured the same). The
-// feature map's rows so stored gained only in its fastest launches and the
-// buffer offsets cost registers past occupancy steps at other shapes, so it
-// keeps global stores.
-constexpr int kStoreNtSc1 = 2 | 16;  // cache policy: NT (SLC) | SC1 (SCC)
+// The state slices that the commit and the fused step write back are
+// non-temporal stores; on large batches at F <= 128 they also carry device
+// scope (the NT and SC1 cache-policy bits), which a plain global store
+// cannot, so they are buffer stores. Measured against non-temporal global
+// stores, d = 128, same bits, alternated runs on three boxes: commit at
+// FW = 64, 256 requests x 16 heads 111.0 -> 109.5 us, 512: 215.0 -> 211.3
+// us, 1,024: 423.5 -> 413.2 us, 128: even, 64: 31.2 -> 31.9 us (slower);
+// FW = 32, 256: even; FW = 128, 256: 217.4 -> 219.3 us, 2,048: 1,682 ->
+// 1,754 us (slower); forward + commit at FW = 64, 256: 130.4 -> 125.5 us.
+// Device scope without NT was 5 % slower, NT with SC0 no different. So the
+// launchers take device scope when F <= 128 and there are at least
+// kDevScopePairsPerCu pairs per CU (eight rounds of the two resident work-
+// groups). The loads keep NT alone (the forward with its state slices read
+// under the other policies measured the same), and so do the forward's
+// output rows (with SC1: 76 -> 80 us at 256 requests).
+constexpr int kDevScopePairsPerCu = 16;
+template <bool DEV>
+constexpr int kStorePolicy = DEV ? (2 | 16) : 2;  // NT (SLC), | SC1 (SCC)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_buffer(void* base, uint32_t bytes);
 
 // A raw buffer resource over `bytes` bytes from `base`, which must be the
 // same in every lane of the wave (its halves are read from the first lane,
@@ -592,10 +599,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_buffer(void* base, uint32
     return __builtin_amdgcn_make_buffer_rsrc(p, 0, static_cast<int>(bytes), 0x00020000);
 }
 
-// 16-byte non-temporal, device-scope store at byte offset `off` of `r`.
-__device__ __forceinline__ void store_nt_sc1(const f32x4& x, __amdgpu_buffer_rsrc_t r, int off)
+// Store t of lane `lane` of a wave's state slice (NSL 16-byte stores per
+// lane, 1 KiB per store across the wave, as load_state_slice reads it):
+// non-temporal at device scope with DEV (a buffer store), else a
+// non-temporal global store (the buffer form of the same policy measured
+// 1.5 % slower at F = 256).
+template <bool DEV, int NSL>
+__device__ __forceinline__ void store_state(const f32x4& x, float* slice, int lane, int t)
 {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, kStoreNtSc1);
+    if constexpr (DEV) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), wave_buffer(slice, NSL * 1024),
+                                               16 * lane + 1024 * t, 0, kStorePolicy<true>);
+    } else {
+        __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(slice) + lane + 64 * t);
+    }
 }
 
 // The B output rows of the tile, 16 bytes per thread per step, whole rows

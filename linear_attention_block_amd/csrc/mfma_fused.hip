@@ -19,7 +19,7 @@ struct alignas(16) FusedLds {
     float Pt[Cfg<D, FW>::F * Cfg<D, FW>::PS];  // phi(K)^T, fp32 [f][t]
 };
 
-template <int D, int FW>
+template <int D, int FW, bool DEV>
 __global__ __launch_bounds__(64 * (D / 32))
 __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forward_commit_mfma_kernel(ForwardArgs a, CommitArgs c)
 {
@@ -91,7 +91,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
     __syncthreads();
 
     float* rec = const_cast<float*>(op.rec);
-    const __amdgpu_buffer_rsrc_t dst = wave_buffer(rec + wv * F * 32, C::NSL * 1024);
+    float* const slice = rec + wv * F * 32;  // this wave's slice
     // dS = phi(K)^T V into the slice: A from phi(K)^T rows with the token
     // order of vt_frag (16 kb + 4 g + {0..3}, 16 kb + 8 + 4 g + {0..3}); each
     // 32-row tile is stored as soon as its dS is added
@@ -114,7 +114,7 @@ __attribute__((amdgpu_waves_per_eu(Cfg<D, FW>::WPE, Cfg<D, FW>::WPE))) void forw
 #pragma unroll
         for (int v = 0; v < 16; ++v) sv[4 * ft + (v >> 2)][v & 3] += acc[v];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) store_nt_sc1(sv[4 * ft + i], dst, 16 * lane + 1024 * (4 * ft + i));
+        for (int i = 0; i < 4; ++i) store_state<DEV, C::NSL>(sv[4 * ft + i], slice, lane, 4 * ft + i);
     }
     // Z as loaded for the forward (its LDS copy), plus the block's phi sums:
     // the work-group ends with stores only
@@ -130,10 +130,16 @@ template <int D>
 hipError_t forward_commit_by_fw(const ForwardArgs& a, const CommitArgs& c, hipStream_t s)
 {
     const dim3 grid(static_cast<uint32_t>(a.R * a.H)), block(64 * (D / 32));
+    // the state write-back policy of the commit kernel (same rule)
+    const bool dev = static_cast<int64_t>(a.R) * a.H >= static_cast<int64_t>(kDevScopePairsPerCu) * compute_units();
     switch (a.FW) {
-        case 32: return launch_kernel(forward_commit_mfma_kernel<D, 32>, grid, block, s, a, c);
-        case 64: return launch_kernel(forward_commit_mfma_kernel<D, 64>, grid, block, s, a, c);
-        default: return launch_kernel(forward_commit_mfma_kernel<D, 128>, grid, block, s, a, c);
+        case 32:
+            return dev ? launch_kernel(forward_commit_mfma_kernel<D, 32, true>, grid, block, s, a, c)
+                       : launch_kernel(forward_commit_mfma_kernel<D, 32, false>, grid, block, s, a, c);
+        case 64:
+            return dev ? launch_kernel(forward_commit_mfma_kernel<D, 64, true>, grid, block, s, a, c)
+                       : launch_kernel(forward_commit_mfma_kernel<D, 64, false>, grid, block, s, a, c);
+        default: return launch_kernel(forward_commit_mfma_kernel<D, 128, false>, grid, block, s, a, c);
     }
 }
 

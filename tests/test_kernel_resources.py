@@ -35,8 +35,10 @@ MIN_OCCUPANCY = {
     # d = 64 at one wave per SIMD, compiled for that budget
     ("forward_mfma_kernel", (64, 64, 1, 1)): 1,
     ("forward_mfma_kernel", (64, 32, 1, 1)): 1,
-    ("forward_commit_mfma_kernel", (128, 64)): 2,
-    ("commit_mfma_kernel", (128, 64)): 2,
+    ("forward_commit_mfma_kernel", (128, 64, 0)): 2,
+    ("forward_commit_mfma_kernel", (128, 64, 1)): 2,
+    ("commit_mfma_kernel", (128, 64, 0)): 2,
+    ("commit_mfma_kernel", (128, 64, 1)): 2,
     ("prefill_mfma_kernel", (128, 64)): 2,
     ("forward_gqa_mfma_kernel", (128, 64, 2)): 2,
     ("forward_gqa_mfma_kernel", (128, 64, 4)): 2,
