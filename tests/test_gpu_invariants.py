@@ -12,6 +12,11 @@
   "Architecture Design"), so saving the records after block n, restoring them
   into a fresh state pool under other slots, and continuing must give the
   same outputs and states, bit for bit, as the uninterrupted run.
+* Store policy: the commit and the fused last step write the state back
+  with device-scope non-temporal stores from 16 pairs per CU (at F <= 128)
+  and with plain non-temporal stores below that; a batch that takes the
+  first path must give the same states and outputs, bit for bit, as its two
+  halves committed separately (each taking the second).
 Shapes: the decode-like 64 x 16 batch on the matrix-core path (d = 128,
 FW = 64, B = 32), the two-tile path (B = 48) and the fp32 path.
 """
@@ -152,3 +157,27 @@ def test_checkpoint_round_trip(dev, io, b, tmp_path):
     assert torch.equal(run.view(case.num_slots, H, -1)[slots.long()], fresh.view(pool, H, -1)[new_slots.long()])
     print(f"[checkpoint] io={io} B={b}: resumed after block 1 under new slots; outputs and states of blocks 2-3 "
           "bit-identical to the uninterrupted run", flush=True)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_store_policy_keeps_the_bits(dev, fused):
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    H = 16
+    R = 16 * cus // H  # the smallest batch that takes the device-scope stores
+    case, w, gamma, slots, state, q, k, v = _batch(dev, "bf16", 32, R=R, H=H)
+    half = R // 2
+    print(f"[store-policy] fused={fused} R={R} H={H} ({R * H} pairs; halves of {half * H})", flush=True)
+    whole, parts = state.clone(), state.clone()
+    if fused:
+        y_whole = bha.block_forward_commit(q, k, v, w, gamma, whole, slots)
+        y_parts = torch.cat([bha.block_forward_commit(q[i:i + half], k[i:i + half], v[i:i + half], w, gamma, parts,
+                                                      slots[i:i + half].contiguous()) for i in (0, half)])
+    else:
+        bha.state_commit(k, v, w, whole, slots)
+        for i in (0, half):
+            bha.state_commit(k[i:i + half], v[i:i + half], w, parts, slots[i:i + half].contiguous())
+    torch.cuda.synchronize()
+    assert not torch.equal(whole, state), "the commit changed nothing"
+    assert torch.equal(whole.view(torch.int32), parts.view(torch.int32))
+    if fused:
+        assert torch.equal(y_whole.view(torch.int16), y_parts.view(torch.int16))
