@@ -94,6 +94,16 @@ def state_store_scope(FW, npairs, dev) -> str:
     return "true" if FW <= 64 and npairs >= 16 * cus else "false"
 
 
+def fmap_store_scope(d, FW, ntok, H, dev) -> str:
+    """The template flag the feature-map launcher chooses: device-scope
+    stores at d = 128, FW = 64 for up to 4 units (128 tokens x head) per CU."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    units = (ntok + 127) // 128 * H
+    return "true" if d == 128 and FW == 64 and units <= 4 * cus else "false"
+
+
 def forward_bytes(R, H, d, FW, B, es=2):
     """Algorithmic HBM bytes of one bha_block_forward launch: per (request, head)
     the fp32 S tiles and Z (read), Q, K, V (read) and O (written); W once per head."""
@@ -893,7 +903,8 @@ def main() -> int:
             "timing": "on copies of the states, one event pair around 5 rounds over the layers",
         },
         "feature_map": {
-            "kernel": (f"bha_feature_map: feature_map_mfma_kernel<{d},{FW}>" if args.io == "bf16"
+            "kernel": (f"bha_feature_map: feature_map_mfma_kernel<{d},{FW},{fmap_store_scope(d, FW, R * B, H, dev)}>"
+                       if args.io == "bf16"
                        else "bha_feature_map: feature_map_generic_kernel<float>"),
             "avg_launch_us": fm_ms * 1e3,
             "bytes_per_launch": fmb,

@@ -23,7 +23,16 @@ namespace {
 // instruction; measured at 256 x 32 tokens x 16 heads, FW = 64: 40.7 us).
 // Roofline: HBM. Algorithmic bytes per (token, head): the row read (2 d) and
 // phi written (4 F); W once per head per launch.
-template <int D, int FW>
+// DEV: the rows are stored non-temporal at device scope (buffer stores; see
+// kStorePolicy), which the launcher takes at d = 128, FW = 64 (the one shape
+// where the buffer offsets keep the kernel in its occupancy step) for up to
+// kFmapDevScopeUnitsPerCu units per CU. Measured at 16 heads, B = 32, same
+// bits, three alternated runs: 64 requests 8.62-8.69 -> 7.15-7.42 us, 256:
+// 19.17-19.54 -> 18.06-18.72 us, 1,024 (16 units per CU): 67.6-67.7 ->
+// 74.8-75.2 us (slower).
+constexpr int kFmapDevScopeUnitsPerCu = 4;
+
+template <int D, int FW, bool DEV>
 __global__ __launch_bounds__(64 * (D / 32)) void feature_map_mfma_kernel(PhiArgs a, int nunits)
 {
     using C = Cfg<D, FW>;
@@ -97,6 +106,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void feature_map_mfma_kernel(PhiArgs
         const float ip = 1.0f / sp, in = 1.0f / sn;
         float* const stage = reinterpret_cast<float*>(Xs + 32 * wv * C::RS);  // this wave's X rows
         const int64_t tw = t0 + 32 * wv;  // the wave's first token
+        float* const prow0 = a.phi + (tw * a.H + h) * F;  // its row of head h
         // piece (half hf, features c0 .. c0 + CW - 1 of that half)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
@@ -118,9 +128,15 @@ __global__ __launch_bounds__(64 * (D / 32)) void feature_map_mfma_kernel(PhiArgs
                 for (int i = 0; i < 32 * CW / 4 / 64; ++i) {
                     const int idx = lane + 64 * i, row = idx / (CW / 4), c4 = idx % (CW / 4);
                     const int64_t tk = tw + row;
-                    if (tk < ntok)
-                        *reinterpret_cast<f32x4*>(a.phi + (tk * a.H + h) * F + hf * FW + c0 + 4 * c4) =
-                            *reinterpret_cast<const f32x4*>(stage + row * CS + 4 * c4);
+                    if (tk < ntok) {
+                        const f32x4 x = *reinterpret_cast<const f32x4*>(stage + row * CS + 4 * c4);
+                        if constexpr (DEV)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                __builtin_bit_cast(u32x4, x), wave_buffer(prow0, 32u * a.H * F * 4u),
+                                4 * ((row * a.H) * F + hf * FW + c0 + 4 * c4), 0, kStorePolicy<true>);
+                        else
+                            *reinterpret_cast<f32x4*>(a.phi + (tk * a.H + h) * F + hf * FW + c0 + 4 * c4) = x;
+                    }
                 }
             }
     }
@@ -139,10 +155,16 @@ hipError_t feature_map_by_fw(const PhiArgs& a, hipStream_t s)
     if (NG > nunits) NG = nunits;
     const dim3 grid(static_cast<uint32_t>(NG)), block(64 * (D / 32));
     const int nt = nunits;
+    // device-scope stores (a wave's 32 rows span 32 H F floats: byte offsets
+    // within 31 bits)
+    const bool dev = D == 128 && nunits <= static_cast<int64_t>(kFmapDevScopeUnitsPerCu) * compute_units() &&
+                     int64_t(32) * a.H * (2 * a.FW) * 4 <= INT32_MAX;
     switch (a.FW) {
-        case 32: return launch_kernel(feature_map_mfma_kernel<D, 32>, grid, block, s, a, nt);
-        case 64: return launch_kernel(feature_map_mfma_kernel<D, 64>, grid, block, s, a, nt);
-        default: return launch_kernel(feature_map_mfma_kernel<D, 128>, grid, block, s, a, nt);
+        case 32: return launch_kernel(feature_map_mfma_kernel<D, 32, false>, grid, block, s, a, nt);
+        case 64:
+            return dev ? launch_kernel(feature_map_mfma_kernel<D, 64, true>, grid, block, s, a, nt)
+                       : launch_kernel(feature_map_mfma_kernel<D, 64, false>, grid, block, s, a, nt);
+        default: return launch_kernel(feature_map_mfma_kernel<D, 128, false>, grid, block, s, a, nt);
     }
 }
 

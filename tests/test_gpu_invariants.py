@@ -16,7 +16,10 @@
   with device-scope non-temporal stores from 16 pairs per CU (at F <= 128)
   and with plain non-temporal stores below that; a batch that takes the
   first path must give the same states and outputs, bit for bit, as its two
-  halves committed separately (each taking the second).
+  halves committed separately (each taking the second). The feature map
+  stores its rows at device scope up to 4 units (128 tokens x head) per CU
+  at d = 128, FW = 64, and plainly above: a batch above that must give the
+  rows of its halves, bit for bit.
 Shapes: the decode-like 64 x 16 batch on the matrix-core path (d = 128,
 FW = 64, B = 32), the two-tile path (B = 48) and the fp32 path.
 """
@@ -181,3 +184,17 @@ def test_store_policy_keeps_the_bits(dev, fused):
     assert torch.equal(whole.view(torch.int32), parts.view(torch.int32))
     if fused:
         assert torch.equal(y_whole.view(torch.int16), y_parts.view(torch.int16))
+
+
+def test_feature_map_store_policy_keeps_the_bits(dev):
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    H, B = 16, 32
+    R = 2 * (4 * cus * 128 // (H * B))  # twice the largest batch with device-scope stores
+    _, w, _, _, _, q, _, _ = _batch(dev, "bf16", B, R=R, H=H)
+    half = R // 2
+    print(f"[store-policy] feature map R={R} H={H} ({R * B // 128 * H} units; halves of {half * B // 128 * H})",
+          flush=True)
+    whole = bha.feature_map(q, w)
+    parts = torch.cat([bha.feature_map(q[i:i + half], w) for i in (0, half)])
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int32), parts.view(torch.int32))

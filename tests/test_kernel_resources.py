@@ -44,7 +44,8 @@ MIN_OCCUPANCY = {
     ("forward_gqa_mfma_kernel", (128, 64, 4)): 2,
     ("forward_gqa8_kernel", (128, 64, 0)): 2,
     ("forward_gqa8_kernel", (128, 64, 1)): 2,
-    ("feature_map_mfma_kernel", (128, 64)): 2,
+    ("feature_map_mfma_kernel", (128, 64, 0)): 2,
+    ("feature_map_mfma_kernel", (128, 64, 1)): 2,
     ("forward_split_kernel", (128,)): 2,
 }
 
