@@ -31,6 +31,8 @@ struct alignas(16) GqaLds {
     uint16_t Ws[FW * C::RS];
     uint16_t Vs[32 * C::RS];
     float Zs[F];
+    // one query head's output tile (merge_to_lds layout), staged at FW <= 64
+    uint16_t Os[FW <= 64 ? 32 * (D + 8) : 8];
     __device__ uint16_t* qs() { return reinterpret_cast<uint16_t*>(u); }
     __device__ uint16_t* ks() { return reinterpret_cast<uint16_t*>(u) + 32 * G * C::RS; }
     __device__ bf16x8* pb() { return reinterpret_cast<bf16x8*>(u); }
@@ -183,7 +185,19 @@ __attribute__((amdgpu_waves_per_eu(gqa_wpe<D, FW, G>(), gqa_wpe<D, FW, G>()))) v
             f32x16 vacc = f32x16{};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) vacc = mfma32(vt_frag<C::RS>(sm.Vs, 32 * wv, kb, tlane), pp[kb], vacc);
-            merge_store(a, vacc, lacc, gamma[j], m, l, den, sn, r, hk * G + j, wv, tln, tg, valid);
+            // at FW <= 64 the head's output rows go through LDS and out as whole
+            // rows with non-temporal stores, as in the one-head forward
+            // (measured at 16 query heads, same bits: 256 requests over 8 K/V
+            // heads 49.5 -> 47.6 us, over 4: 37.3 -> 37.0 us; 512 over 4: 68.0
+            // -> 67.1 us); at FW = 128 the tile's registers would spill
+            if constexpr (FW <= 64) {
+                merge_to_lds<D>(a, vacc, lacc, gamma[j], m, l, den, sn, wv, tln, tg, valid, sm.Os);
+                __syncthreads();
+                store_out_rows<D, C::NT>(a, sm.Os, r, hk * G + j, tid);
+                __syncthreads();  // the tile is read before the next head's merge writes it
+            } else {
+                merge_store(a, vacc, lacc, gamma[j], m, l, den, sn, r, hk * G + j, wv, tln, tg, valid);
+            }
             __builtin_amdgcn_sched_barrier(0);  // one head's operands in registers at a time
         }
         asm volatile("" : "+v"(slot_after));
