@@ -218,8 +218,14 @@ __global__ __launch_bounds__(2 * 64 * (D / 32)) __attribute__((amdgpu_waves_per_
             __builtin_amdgcn_sched_barrier(0);
             load_state_slice(op.rec + soff, lane, sv, live);
             __builtin_amdgcn_sched_barrier(0);
-            merge_store(a, vacc, lacc, gamma, m, l, dp / sp + dz / s, s, r, h, cs, ln, g, valid);
+            merge_to_lds<D>(a, vacc, lacc, gamma, m, l, dp / sp + dz / s, s, cs, ln, g, valid, sm.Os);
         }
+        // the output rows go out whole from LDS, non-temporal, as in the
+        // one-wave kernel (measured at FW = 128, same bits: 512 x 16 pairs
+        // 253.6-254.9 -> 249.0-250.2 us, 256 x 16: 134.5-135.5 -> 130.5-132.7
+        // us against 32-byte row pieces stored from the merge)
+        __syncthreads();
+        store_out_rows<D, NT>(a, sm.Os, r, h, tid);
         asm volatile("" : "+v"(slot_after));
         slot_next = slot_after;
         p = pn;
