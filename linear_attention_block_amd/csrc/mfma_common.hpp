@@ -235,7 +235,7 @@ struct alignas(16) FwdLds {
     uint16_t Ws[FW * C::RS];
     uint16_t Vs[32 * KT * C::RS];  // V rows, read transposed by ds_read_b64_tr_b16
     float Zs[C::F];
-    uint16_t Os[KT == 1 && G == 1 ? 32 * (D + 8) : 8];  // the pair's output rows, padded (one-head, one-tile kernel)
+    uint16_t Os[G == 1 ? 32 * (D + 8) : 8];  // a 32-row output tile, padded (one-head kernels)  // the pair's output rows, padded (one-head, one-tile kernel)
 };
 
 // The per-pair operands a thread stages through LDS, held in registers from
@@ -615,19 +615,21 @@ __device__ __forceinline__ void store_state(const f32x4& x, float* slice, int la
     }
 }
 
-// The B output rows of the tile, 16 bytes per thread per step, whole rows
-// per store instruction (non-temporal: full lines).
+// Rows row0 .. row0 + 31 of the block's output (those below B) from the
+// staged tile, 16 bytes per thread per step, whole rows per store
+// instruction (non-temporal: full lines).
 template <int D, int NT>
-__device__ __forceinline__ void store_out_rows(const ForwardArgs& a, const uint16_t* Os, int r, int h, int tid)
+__device__ __forceinline__ void store_out_rows(const ForwardArgs& a, const uint16_t* Os, int r, int h, int tid,
+                                               int row0 = 0)
 {
     constexpr int CH = D / 8;
 #pragma unroll
     for (int i = 0; i < 32 * CH / NT; ++i) {
-        const int idx = tid + i * NT, row = idx / CH, ch = idx % CH;
+        const int idx = tid + i * NT, ch = idx % CH, row = row0 + idx / CH;
         if (row < a.B) {
             uint16_t* orow = static_cast<uint16_t*>(a.out) + static_cast<int64_t>(r) * a.os.req +
                              static_cast<int64_t>(h) * a.os.head + (row * static_cast<int>(a.os.tok) + 8 * ch);
-            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Os + row * (D + 8) + 8 * ch),
+            __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Os + (row - row0) * (D + 8) + 8 * ch),
                                         reinterpret_cast<u32x4*>(orow));
         }
     }

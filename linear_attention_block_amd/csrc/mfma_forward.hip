@@ -87,7 +87,14 @@ forward_mfma_kernel(ForwardArgs a, int npairs)
                 vacc = block_softmax_pv<D, FW, KT, 1>(a, sm, 32 * qt, wv, ln, g, m, l);
                 lacc = linear_read<D, FW>(sv, pb, sp, sn);
             }
-            merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, 32 * qt + ln, g, valid);
+            merge_to_lds<D>(a, vacc, lacc, gamma, m, l, den, sn, wv, ln, g, valid, sm.Os);
+            __syncthreads();
+            // each query tile's rows go out whole from LDS (two-tile blocks of
+            // 48 / 64 tokens at FW = 64: 121.8-124.9 -> 120.5-122.1 us and
+            // 130.6-132.1 -> 128.0-129.1 us against 32-byte row pieces stored
+            // from the merge, same bits)
+            store_out_rows<D, C::NT>(a, sm.Os, r, h, tid, 32 * qt);
+            __syncthreads();  // the tile is read before the next tile's merge writes it
             // compiled for two waves per SIMD the tiles must not overlap
             // (registers); for one, letting them overlap is faster
             if constexpr (fwd_wpe<D, FW, KT>() > 1) __builtin_amdgcn_sched_barrier(0);
@@ -109,10 +116,10 @@ forward_mfma_kernel(ForwardArgs a, int npairs)
             load_state_slice(nrec + wv * F * 32, lane, sv, live);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kFwdStagedOut && KT == 1) {
+        if constexpr (kFwdStagedOut) {
             merge_to_lds<D>(a, vacc, lacc, gamma, m, l, den, sn, wv, ln, g, valid, sm.Os);
             __syncthreads();
-            store_out_rows<D, C::NT>(a, sm.Os, r, h, tid);
+            store_out_rows<D, C::NT>(a, sm.Os, r, h, tid, 32 * QL);
         } else {
             merge_store(a, vacc, lacc, gamma, m, l, den, sn, r, h, wv, 32 * QL + ln, g, valid);
         }
